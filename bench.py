@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused top-k + page-table transform on one MI355X.
+
+One step = one call of the whole hot path (key map, radix select, compaction,
+tie fill, page-table gather, -1 padding) over one batch of the bandwidth
+workload: batch 2048, seq_len 65536, k 512, N(0,1) fp32 scores, page_size 64,
+identity table.  The value is its effective HBM throughput (algorithmic bytes:
+scores read + seq_lens read + indices written; the page table is not counted,
+as in SGLang PR #26788's footprint).  The batch-1, 1M-token latency is reported
+beside it.
+
+Inputs are resident in HBM before timing starts.  Each timed call reads a
+different copy of the inputs, with more than 1 GiB of distinct inputs in the
+rotation, so the 256 MiB Infinity Cache cannot serve them (the pages' own
+benchmark rotates every read tensor for the same reason).
+
+The CPU baseline is the oracle (numpy, one core) on a bounded sample of rows of
+the same workload.
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+ROTATE_BYTES = 1.25 * (1 << 30)
+METRIC = "top-k+transform µs/call at b=1,L=1M,k=2048; effective HBM GB/s at b=2048,L=64K"
+
+
+def algorithmic_bytes(w, raw: bool) -> int:
+    import numpy as np
+    L = np.clip(w.seq_lens.astype(np.int64), 0, w.width)
+    per_idx = 4 * w.batch * w.k
+    return int(4 * L.sum() + 4 * w.batch + per_idx + (per_idx if raw else 0))
+
+
+def device_inputs(w, copies: int):
+    import torch
+    dev = torch.device("cuda", 0)
+    s = torch.from_numpy(w.scores).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    pt = torch.from_numpy(w.page_table).to(dev)
+    sets = [(s, sl, pt)]
+    for _ in range(copies - 1):
+        sets.append((s.clone(), sl.clone(), pt.clone()))
+    return sets
+
+
+def time_calls(topk, w, sets, steps: int, warmup: int, raw: bool = False):
+    """Average ms per call over `steps` calls (HIP events on the launch stream)."""
+    import torch
+    dev = sets[0][0].device
+    out = torch.empty((w.batch, w.k), dtype=torch.int32, device=dev)
+    out_raw = torch.empty((w.batch, w.k), dtype=torch.int32, device=dev) if raw else None
+    for i in range(warmup):
+        s, sl, pt = sets[i % len(sets)]
+        topk.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=out_raw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        s, sl, pt = sets[i % len(sets)]
+        topk.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=out_raw)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall * 1e3 / steps
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle as it stands, timed on a bounded sample of the workload's rows."""
+    import numpy as np
+    from oracle import topk_transform as oracle_topk
+    t = time.perf_counter()
+    oracle_topk(w.scores, w.seq_lens, w.page_table, w.k, w.page_size, rows=range(4))
+    per_row = (time.perf_counter() - t) / 4
+    rows = int(max(8, min(w.batch, budget_s / max(per_row, 1e-6))))
+    t = time.perf_counter()
+    oracle_topk(w.scores, w.seq_lens, w.page_table, w.k, w.page_size, rows=range(rows))
+    el = time.perf_counter() - t
+    L = np.clip(w.seq_lens[:rows].astype(np.int64), 0, w.width)
+    nbytes = int(4 * L.sum() + 4 * rows + 4 * rows * w.k)
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {w.batch} rows of {w.name} (numpy sort per row, single thread); "
+                      f"{el:.1f} s, {rows / el:.1f} rows/s, {el / rows * 1e3:.2f} ms/row"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all", action="store_true", help="also time every workload (table on stderr)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the operation is per-row and this build runs on a single "
+              "MI355X (rows would shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_fp32_amd as topk
+    import workloads
+
+    topk.load()
+    props = torch.cuda.get_device_properties(0)
+
+    # ---- headline: bandwidth workload (batch 2048 x 65536, k 512) -----------------
+    w = workloads.c4a()
+    nbytes = algorithmic_bytes(w, raw=False)
+    in_bytes = w.scores.nbytes + w.seq_lens.nbytes + w.page_table.nbytes
+    copies = max(2, math.ceil(ROTATE_BYTES / in_bytes))
+    sets = device_inputs(w, copies)
+    ms, wall_ms = time_calls(topk, w, sets, args.steps, args.warmup)
+    launch = topk.topk_last_launch()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    hot_ms, _ = time_calls(topk, w, sets[:1], args.steps, 2)
+    del sets
+    torch.cuda.empty_cache()
+
+    # ---- batch-1, 1M-token latency (k 2048) ---------------------------------------
+    w3 = workloads.c3(1)
+    b3 = algorithmic_bytes(w3, raw=False)
+    in3 = w3.scores.nbytes + w3.seq_lens.nbytes + w3.page_table.nbytes
+    sets3 = device_inputs(w3, max(2, math.ceil(ROTATE_BYTES / in3)))
+    ms3, _ = time_calls(topk, w3, sets3, max(args.steps, 100), args.warmup)
+    launch3 = topk.topk_last_launch()
+    hot3, _ = time_calls(topk, w3, sets3[:1], max(args.steps, 100), 2)
+    del sets3
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if args.all:
+        for name in ("c1", "c2", "c3_b4", "c3_b8", "c4b", "c5"):
+            wx = workloads.make(name)
+            bx = algorithmic_bytes(wx, raw=wx.want_raw)
+            inx = wx.scores.nbytes + wx.seq_lens.nbytes + wx.page_table.nbytes
+            sx = device_inputs(wx, max(2, math.ceil(ROTATE_BYTES / inx)))
+            msx, _ = time_calls(topk, wx, sx, max(args.steps, 50), args.warmup, raw=wx.want_raw)
+            extra[name] = {"us_per_call": round(msx * 1e3, 2), "GBps": round(bx / (msx * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(bx / (msx * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "rows_per_s": round(wx.batch / (msx * 1e-3), 1), "launch": topk.topk_last_launch()}
+            print(f"{name:8s} {extra[name]}", file=sys.stderr, flush=True)
+            del sx
+            torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu else cpu_baseline(w)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(gbps / 3600.0, 3),
+        "vs_baseline_ref": "B200 ~3.0-3.6 TB/s at batch>=2048, seq>=64K, k=512 (SGLang PR #26788); top of range",
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.width, "k": w.k, "page_size": w.page_size,
+                   "page_table": "identity", "out_raw": False, "launch": launch,
+                   "cold_inputs": f"{copies} rotated input copies"},
+        "rows_per_s": round(w.batch / (ms * 1e-3), 1),
+        "hot_cache_GBps": round(nbytes / (hot_ms * 1e-3) / 1e9, 1),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "latency_b1_L1M_k2048_us": round(ms3 * 1e3, 2),
+        "latency_b1_L1M_hot_us": round(hot3 * 1e3, 2),
+        "latency_b1_roofline": {"bound": "hbm", "bytes": b3, "roofline_us": round(b3 / HBM_PEAK_GBPS / 1e3, 3),
+                                "frac": round(b3 / HBM_PEAK_GBPS / 1e3 / (ms3 * 1e3), 4), "launch": launch3},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+    }
+    if extra:
+        result["other_workloads"] = extra
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

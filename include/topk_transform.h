@@ -1,0 +1,142 @@
+/*
+ * topk_transform.h -- C ABI of the MI355X (gfx950) fused top-k + page-table transform.
+ *
+ * The operation is the sparse-attention indexer's per-row selection step: for
+ * each row of fp32 index scores, pick the k positions with the greatest scores
+ * among the row's first seq_len entries, and map each selected position through
+ * that row's KV page table.  It is the operation of SGLang PR #26788
+ * "DeepSeek-V4 DSA indexer: faster top-k + page-table transform (runtime
+ * k <= 2048)" (Motivation and Feature sections: runtime k up to 2048, ragged
+ * per-row sequence lengths, arbitrary power-of-two page size, optional raw
+ * pre-transform index output), implemented from scratch for CDNA4.
+ *
+ * Every function is a plain C call: pointers, sizes and a HIP stream.  No
+ * exception crosses this boundary; every failure is a status code.
+ */
+#ifndef TOPK_TRANSFORM_H_
+#define TOPK_TRANSFORM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest k accepted (PR #26788 title and Feature section: runtime k <= 2048). */
+#define TOPK_MAX_K 2048
+
+typedef enum topk_status_t {
+  TOPK_SUCCESS = 0,
+  /* A required pointer is NULL (seq_lens and out_idx always; scores when
+   * width > 0; page_table when pages_per_row > 0), k is outside
+   * [1, TOPK_MAX_K], page_size is not a power of two, batch / width /
+   * pages_per_row is negative, or width exceeds INT32_MAX. */
+  TOPK_ERROR_INVALID_VALUE = 1,
+  /* The current device is not gfx950, or the shape needs more cooperating
+   * workgroups than the device can hold resident at once. */
+  TOPK_ERROR_UNSUPPORTED = 2,
+  /* The internal workspace could not be allocated. */
+  TOPK_ERROR_OUT_OF_MEMORY = 3,
+  /* A HIP call failed; topk_last_error() holds the HIP error text. */
+  TOPK_ERROR_LAUNCH = 4
+} topk_status_t;
+
+/*
+ * topk_transform -- exact per-row top-k fused with the page-table transform.
+ *
+ * Defined by SGLang PR #26788 (Feature section; the raw-index commit note:
+ * raw_out[i, j] is the pre-transform position chosen for slot j, or -1 for
+ * padding, and out[j] equals the page transform of raw[j]) and LiteTopk PR
+ * #32094 (Notes: an exact top-k *set* whose order within the row is
+ * unspecified; sglang deviations: -1 pads invalid slots).
+ *
+ * Arguments (all pointers are device pointers on the current HIP device, read
+ * or written only by kernels queued on `stream`):
+ *   scores      (batch, width) fp32, row-major, contiguous.  Read only.
+ *   seq_lens    (batch,) int32.  Row b uses positions [0, L_b) with
+ *               L_b = clamp(seq_lens[b], 0, width).  Negative lengths are
+ *               empty rows; lengths above width are read as width.
+ *   page_table  (batch, pages_per_row) int32, row-major.  Only the entries of
+ *               pages that hold a selected position are read.
+ *   k           1 <= k <= TOPK_MAX_K; a runtime value.
+ *   page_size   a power of two >= 1.
+ *   out_idx     (batch, k) int32, written.  For slot j < n_b = min(k, L_b):
+ *               page_table[b, p / page_size] * page_size + p % page_size for a
+ *               selected position p; slots j >= n_b hold -1.
+ *   out_raw     (batch, k) int32 or NULL.  When non-NULL, slot j holds the
+ *               selected position p itself (same slot order as out_idx), and
+ *               -1 in the same padding slots.  NULL costs nothing.
+ *   stream      HIP stream the work is queued on (0 = the null stream).
+ *   batch       number of rows, >= 0 (0 is a no-op).
+ *   width       row stride of scores in elements, >= 0.
+ *   pages_per_row  row stride of page_table in entries, >= 0.
+ *
+ * Result: slots [0, n_b) of each row hold n_b distinct positions in [0, L_b)
+ * that are a top-n_b set of the row: every position whose score is strictly
+ * greater than the smallest selected score is selected, and the remaining slots
+ * take distinct positions whose score equals it.  Scores are ordered as IEEE
+ * fp32 values with -0.0 below +0.0; -inf is an ordinary (selectable) value; NaN
+ * is outside the contract.  Which of several equal scores fill the last slots,
+ * and the order of the slots, are unspecified.
+ *
+ * Caller preconditions (not checked on the device, because checking would need
+ * a host synchronisation): pages_per_row * page_size >= L_b for every row, and
+ * every transformed index fits in int32.  A slot whose page lies beyond
+ * pages_per_row gets -1 in out_idx (its raw position is still written).
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer past
+ * the call.  Rows long enough to be split across workgroups use an internal
+ * per-(device, stream) workspace that the library allocates on first need,
+ * keeps zeroed between calls, and frees in topk_release_workspaces().  The
+ * first call that needs a larger workspace synchronises `stream` (so do not
+ * make that first call under stream capture).
+ *
+ * Completion is asynchronous: outputs are valid once `stream` reaches the call.
+ * Returns TOPK_SUCCESS, or an error status; on error nothing was queued.
+ */
+topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const int32_t* page_table,
+                             int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
+                             hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row);
+
+/* Static text for a status code (never NULL). */
+const char* topk_status_string(topk_status_t status);
+
+/* Detail text of the most recent failing call on this host thread ("" if none). */
+const char* topk_last_error(void);
+
+/* Text naming the launch configuration of the most recent successful call on
+ * this host thread (kernel variant, workgroups per row, elements per thread,
+ * grid size).  For logs and benchmarks. */
+const char* topk_last_launch(void);
+
+/* Frees every internal workspace (after synchronising the device).  Safe to
+ * call at any time no call is in flight. */
+topk_status_t topk_release_workspaces(void);
+
+/*
+ * Testing and tuning override of the dispatcher, process-wide:
+ *   elems_per_thread  0 = automatic, else one of 4, 8, 16, 32, 64: scores held
+ *                     in registers per thread (a workgroup holds 1024 times
+ *                     this many positions of a row);
+ *   wgs_per_row       0 = automatic, else the number of workgroups that share
+ *                     one row (raised to what the row width needs).  1 selects
+ *                     the single-workgroup kernel.
+ * Returns TOPK_ERROR_INVALID_VALUE for other values.
+ */
+topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_per_row);
+
+/* Reads (and clears) the device-side fault word of `stream`'s workspace after
+ * synchronising the stream: 0 when no cross-workgroup wait ever timed out. */
+topk_status_t topk_debug_fault_word(hipStream_t stream, uint32_t* word);
+
+/* ABI version of this header (bumped on any signature change). */
+int32_t topk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPK_TRANSFORM_H_ */

@@ -1,0 +1,149 @@
+"""Python binding of libtopk_transform.so (the gfx950 fused top-k + page-table transform).
+
+Argument marshalling only: every step of the operation runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is not built, or the call fails, this raises.
+
+The C entry points have the same names; see include/topk_transform.h for the
+argument meaning, layouts, ownership and error behaviour.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+from .build import LIB_PATH
+
+TOPK_MAX_K = 2048
+STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUPPORTED",
+          3: "TOPK_ERROR_OUT_OF_MEMORY", 4: "TOPK_ERROR_LAUNCH"}
+
+EXPORTED = ("topk_transform", "topk_status_string", "topk_last_error", "topk_last_launch",
+            "topk_release_workspaces", "topk_set_dispatch_override", "topk_debug_fault_word",
+            "topk_abi_version")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class TopkError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    try:  # make torch's HIP runtime the one the library binds to, when torch is present
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    c_i32, c_i64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.topk_transform.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64]
+    lib.topk_transform.restype = ctypes.c_int
+    lib.topk_status_string.argtypes = [ctypes.c_int]
+    lib.topk_status_string.restype = ctypes.c_char_p
+    lib.topk_last_error.argtypes = []
+    lib.topk_last_error.restype = ctypes.c_char_p
+    lib.topk_last_launch.argtypes = []
+    lib.topk_last_launch.restype = ctypes.c_char_p
+    lib.topk_release_workspaces.argtypes = []
+    lib.topk_release_workspaces.restype = ctypes.c_int
+    lib.topk_set_dispatch_override.argtypes = [c_i32, c_i32]
+    lib.topk_set_dispatch_override.restype = ctypes.c_int
+    lib.topk_debug_fault_word.argtypes = [c_vp, ctypes.POINTER(ctypes.c_uint32)]
+    lib.topk_debug_fault_word.restype = ctypes.c_int
+    lib.topk_abi_version.argtypes = []
+    lib.topk_abi_version.restype = c_i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        text = load().topk_last_error().decode(errors="replace")
+        if status == 1:
+            raise ValueError(f"{STATUS[1]}: {text}")
+        raise TopkError(status, text)
+
+
+def topk_transform(scores, seq_lens, page_table, k: int, page_size: int, out=None, out_raw=None,
+                   want_raw: bool = False, stream=None) -> Tuple[object, Optional[object]]:
+    """Exact per-row top-k of `scores` fused with the page-table transform.
+
+    scores (B, W) float32, seq_lens (B,) int32, page_table (B, P) int32, all
+    contiguous on one GPU.  Returns (out (B, k) int32, out_raw (B, k) int32 or
+    None).  `out` / `out_raw` may be passed preallocated; `want_raw` allocates
+    out_raw when it is not passed.  The call is asynchronous on `stream`
+    (default: torch's current stream of the tensors' device).
+    """
+    import torch
+    lib = load()
+    if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous 2-D float32 tensor")
+    B, W = scores.shape
+    dev = scores.device
+    if dev.type != "cuda":
+        raise ValueError("scores must be on a GPU")
+    if seq_lens.shape != (B,) or seq_lens.dtype != torch.int32 or seq_lens.device != dev:
+        raise ValueError("seq_lens must be an int32 tensor of shape (B,) on the scores' device")
+    if (page_table.dim() != 2 or page_table.shape[0] != B or page_table.dtype != torch.int32
+            or not page_table.is_contiguous() or page_table.device != dev):
+        raise ValueError("page_table must be a contiguous int32 tensor of shape (B, P) on the scores' device")
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    elif (out.shape != (B, k) or out.dtype != torch.int32 or not out.is_contiguous() or out.device != dev):
+        raise ValueError("out must be a contiguous int32 tensor of shape (B, k)")
+    if out_raw is None and want_raw:
+        out_raw = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if out_raw is not None and (out_raw.shape != (B, k) or out_raw.dtype != torch.int32
+                                or not out_raw.is_contiguous() or out_raw.device != dev):
+        raise ValueError("out_raw must be a contiguous int32 tensor of shape (B, k)")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = lib.topk_transform(scores.data_ptr(), seq_lens.data_ptr(), page_table.data_ptr(), int(k),
+                                int(page_size), out.data_ptr(),
+                                out_raw.data_ptr() if out_raw is not None else None,
+                                ctypes.c_void_p(stream.cuda_stream), int(B), int(W), int(page_table.shape[1]))
+    _check(st)
+    return out, out_raw
+
+
+def topk_status_string(status: int) -> str:
+    return load().topk_status_string(int(status)).decode()
+
+
+def topk_last_error() -> str:
+    return load().topk_last_error().decode(errors="replace")
+
+
+def topk_last_launch() -> str:
+    return load().topk_last_launch().decode(errors="replace")
+
+
+def topk_release_workspaces() -> None:
+    _check(load().topk_release_workspaces())
+
+
+def topk_set_dispatch_override(elems_per_thread: int = 0, wgs_per_row: int = 0) -> None:
+    _check(load().topk_set_dispatch_override(int(elems_per_thread), int(wgs_per_row)))
+
+
+def topk_debug_fault_word(stream=None) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    w = ctypes.c_uint32(0)
+    _check(load().topk_debug_fault_word(ctypes.c_void_p(stream.cuda_stream), ctypes.byref(w)))
+    return int(w.value)
+
+
+def topk_abi_version() -> int:
+    return int(load().topk_abi_version())

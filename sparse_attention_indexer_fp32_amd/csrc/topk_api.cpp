@@ -1,0 +1,328 @@
+// C-ABI layer of the fused top-k + page-table transform: argument checks,
+// device checks, the dispatcher that picks a kernel shape from the host-known
+// (batch, width, k) and the device's resident-workgroup capacity, and the
+// per-(device, stream) workspace the split-row kernel synchronises through.
+//
+// Dispatch follows the pages' lesson that the path must depend on batch and
+// length (SGLang PR #26788 commit notes: one block per row at large batch,
+// several cooperating blocks per row for long rows at small batch), with the
+// thresholds set for MI355X: 256 CUs, 1024-thread workgroups, rows held in
+// VGPRs at 4..64 elements per thread.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "topk_internal.h"
+#include "topk_transform.h"
+
+namespace {
+
+thread_local std::string t_last_error;
+thread_local std::string t_last_launch;
+
+struct DeviceInfo {
+  bool supported = false;
+  int cus = 0;
+  bool coop = false;
+  int occ[2][topk::kNumEpt] = {};   // [coop][ept] resident workgroups per CU
+  std::string arch;
+};
+
+struct Workspace {
+  uint32_t* ptr = nullptr;
+  int64_t slots = 0;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_devices;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+int g_override_ept = 0;
+int g_override_wgs = 0;
+
+topk_status_t fail(topk_status_t st, const std::string& msg) {
+  t_last_error = msg;
+  return st;
+}
+
+topk_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(TOPK_ERROR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Caller holds g_mu.
+topk_status_t device_info(int dev, DeviceInfo** out) {
+  auto it = g_devices.find(dev);
+  if (it != g_devices.end()) {
+    *out = &it->second;
+    return TOPK_SUCCESS;
+  }
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  DeviceInfo info;
+  info.arch = prop.gcnArchName;
+  info.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  info.cus = prop.multiProcessorCount;
+  int coop = 0;
+  e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  info.coop = coop != 0;
+  if (info.supported) {
+    for (int c = 0; c < 2; ++c)
+      for (int i = 0; i < topk::kNumEpt; ++i) {
+        e = topk::rows_occupancy(i, c == 1, &info.occ[c][i]);
+        if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+      }
+  }
+  *out = &g_devices.emplace(dev, info).first->second;
+  return TOPK_SUCCESS;
+}
+
+// Caller holds g_mu.
+topk_status_t get_workspace(int dev, hipStream_t stream, int64_t slots, uint32_t** ptr, int64_t* capacity) {
+  Workspace& w = g_ws[std::make_pair(dev, stream)];
+  if (w.ptr && w.slots >= slots) {
+    *ptr = w.ptr;
+    *capacity = w.slots;
+    return TOPK_SUCCESS;
+  }
+  if (w.ptr) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    (void)hipFree(w.ptr);
+    w.ptr = nullptr;
+    w.slots = 0;
+  }
+  const size_t bytes = topk::workspace_words(slots) * sizeof(uint32_t);
+  void* p = nullptr;
+  if (std::getenv("TOPK_TEST_FAIL_ALLOC") == nullptr) {
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
+    }
+  } else {
+    return fail(TOPK_ERROR_OUT_OF_MEMORY, "workspace allocation failure forced by TOPK_TEST_FAIL_ALLOC");
+  }
+  hipError_t e = hipMemsetAsync(p, 0, bytes, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(e, "workspace hipMemset");
+  }
+  w.ptr = static_cast<uint32_t*>(p);
+  w.slots = slots;
+  *ptr = w.ptr;
+  *capacity = w.slots;
+  return TOPK_SUCCESS;
+}
+
+int ept_index(int ept) {
+  for (int i = 0; i < topk::kNumEpt; ++i)
+    if (topk::kEptValues[i] == ept) return i;
+  return -1;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int ept_idx = 0;
+  bool coop = false;
+  int64_t G = 1;
+  int64_t slots = 1;
+};
+
+// Kernel shape for (batch, width) on this device.
+topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, Plan* plan) {
+  const int64_t B = batch;
+  const int64_t Wc = width > 0 ? width : 1;
+  const int64_t row_cap = (int64_t)topk::kThreads * topk::kEptValues[topk::kNumEpt - 1];
+
+  if (g_override_ept || g_override_wgs) {
+    int idx = 0;
+    if (g_override_ept) {
+      idx = ept_index(g_override_ept);
+    } else {
+      while (idx < topk::kNumEpt - 1 && (int64_t)topk::kThreads * topk::kEptValues[idx] * g_override_wgs < Wc) ++idx;
+    }
+    const int64_t C = (int64_t)topk::kThreads * topk::kEptValues[idx];
+    int64_t G = ceil_div(Wc, C);
+    if (g_override_wgs > G) G = g_override_wgs;
+    plan->ept_idx = idx;
+    plan->G = G;
+    plan->coop = G > 1;
+  } else {
+    const int64_t cap_single = (int64_t)dev.cus;   // one resident row per CU is already a full wave
+    if (Wc <= row_cap && (B >= 2 * cap_single || Wc <= 8192)) {
+      int idx = 0;
+      while ((int64_t)topk::kThreads * topk::kEptValues[idx] < Wc) ++idx;
+      plan->ept_idx = idx;
+      plan->G = 1;
+      plan->coop = false;
+    } else {
+      // Split rows: the most workgroups per row whose grid still fits resident.
+      int chosen = -1;
+      for (int i = 0; i < topk::kNumEpt; ++i) {
+        const int64_t G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[i]);
+        const int64_t cap = (int64_t)dev.occ[1][i] * dev.cus;
+        if (G >= 1 && B * G <= cap) {
+          chosen = i;
+          break;
+        }
+      }
+      if (chosen < 0) chosen = topk::kNumEpt - 1;
+      plan->ept_idx = chosen;
+      plan->G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[chosen]);
+      plan->coop = plan->G > 1;
+      if (!plan->coop) plan->ept_idx = chosen;
+    }
+  }
+  if (plan->coop) {
+    if (!dev.coop) return fail(TOPK_ERROR_UNSUPPORTED, "device does not support cooperative launch");
+    const int64_t cap = (int64_t)dev.occ[1][plan->ept_idx] * dev.cus;
+    if (plan->G > cap)
+      return fail(TOPK_ERROR_UNSUPPORTED, "row width needs more cooperating workgroups than fit resident");
+    int64_t slots = cap / plan->G;
+    if (slots > B) slots = B;
+    plan->slots = slots;
+  } else {
+    plan->slots = B;
+  }
+  return TOPK_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
+                             int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream,
+                             int32_t batch, int64_t width, int64_t pages_per_row) {
+  t_last_error.clear();
+  if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERROR_INVALID_VALUE, "k must be in [1, 2048]");
+  if (page_size < 1 || (page_size & (page_size - 1)) != 0)
+    return fail(TOPK_ERROR_INVALID_VALUE, "page_size must be a power of two >= 1");
+  if (batch < 0 || width < 0 || pages_per_row < 0)
+    return fail(TOPK_ERROR_INVALID_VALUE, "batch, width and pages_per_row must be >= 0");
+  if (width > (int64_t)INT32_MAX) return fail(TOPK_ERROR_INVALID_VALUE, "width must fit in int32");
+  if (batch == 0) {
+    t_last_launch = "noop batch=0";
+    return TOPK_SUCCESS;
+  }
+  if (!seq_lens || !out_idx) return fail(TOPK_ERROR_INVALID_VALUE, "seq_lens and out_idx must be non-null");
+  if (!scores && width > 0) return fail(TOPK_ERROR_INVALID_VALUE, "scores must be non-null when width > 0");
+  if (!page_table && pages_per_row > 0)
+    return fail(TOPK_ERROR_INVALID_VALUE, "page_table must be non-null when pages_per_row > 0");
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo* info = nullptr;
+  topk_status_t st = device_info(dev, &info);
+  if (st != TOPK_SUCCESS) return st;
+  if (!info->supported) return fail(TOPK_ERROR_UNSUPPORTED, "device " + info->arch + " is not gfx950");
+
+  Plan plan;
+  st = plan_launch(*info, batch, width, &plan);
+  if (st != TOPK_SUCCESS) return st;
+
+  topk::KernelArgs a;
+  a.scores = scores;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.out = out_idx;
+  a.out_raw = out_raw;
+  a.ws = nullptr;
+  a.ws_slots = 0;
+  a.width = width;
+  a.pages_per_row = pages_per_row;
+  a.batch = batch;
+  a.k = k;
+  int lg = 0;
+  while ((1 << lg) < page_size) ++lg;
+  a.log2_page = lg;
+  a.wgs_per_row = (int32_t)plan.G;
+  a.slots = (int32_t)plan.slots;
+  a.vec = (width % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
+  if (plan.coop) {
+    int64_t capacity = 0;
+    st = get_workspace(dev, stream, plan.slots, &a.ws, &capacity);
+    if (st != TOPK_SUCCESS) return st;
+    a.ws_slots = (int32_t)capacity;
+  }
+  e = topk::launch_rows(plan.ept_idx, plan.coop, a, stream);
+  if (e != hipSuccess) return hip_fail(e, plan.coop ? "hipLaunchCooperativeKernel" : "kernel launch");
+  char buf[160];
+  std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d",
+                plan.coop ? "split-row" : "row-per-wg", topk::kEptValues[plan.ept_idx], (long long)plan.G,
+                (long long)plan.slots, (long long)(plan.slots * plan.G), topk::kThreads, a.vec);
+  t_last_launch = buf;
+  return TOPK_SUCCESS;
+}
+
+const char* topk_status_string(topk_status_t status) {
+  switch (status) {
+    case TOPK_SUCCESS: return "TOPK_SUCCESS";
+    case TOPK_ERROR_INVALID_VALUE: return "TOPK_ERROR_INVALID_VALUE";
+    case TOPK_ERROR_UNSUPPORTED: return "TOPK_ERROR_UNSUPPORTED";
+    case TOPK_ERROR_OUT_OF_MEMORY: return "TOPK_ERROR_OUT_OF_MEMORY";
+    case TOPK_ERROR_LAUNCH: return "TOPK_ERROR_LAUNCH";
+  }
+  return "TOPK_UNKNOWN_STATUS";
+}
+
+const char* topk_last_error(void) { return t_last_error.c_str(); }
+
+const char* topk_last_launch(void) { return t_last_launch.c_str(); }
+
+topk_status_t topk_release_workspaces(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_ws.empty()) return TOPK_SUCCESS;
+  hipError_t e = hipDeviceSynchronize();
+  for (auto& kv : g_ws)
+    if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+  g_ws.clear();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  return TOPK_SUCCESS;
+}
+
+topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_per_row) {
+  if (elems_per_thread != 0 && ept_index(elems_per_thread) < 0)
+    return fail(TOPK_ERROR_INVALID_VALUE, "elems_per_thread must be 0, 4, 8, 16, 32 or 64");
+  if (wgs_per_row < 0 || wgs_per_row > 65536) return fail(TOPK_ERROR_INVALID_VALUE, "wgs_per_row out of range");
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_override_ept = elems_per_thread;
+  g_override_wgs = wgs_per_row;
+  return TOPK_SUCCESS;
+}
+
+topk_status_t topk_debug_fault_word(hipStream_t stream, uint32_t* word) {
+  if (!word) return fail(TOPK_ERROR_INVALID_VALUE, "word must be non-null");
+  *word = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_ws.find(std::make_pair(dev, stream));
+  if (it == g_ws.end() || !it->second.ptr) return TOPK_SUCCESS;
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  e = hipMemcpy(word, it->second.ptr, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  const uint32_t zero = 0;
+  e = hipMemcpy(it->second.ptr, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  return TOPK_SUCCESS;
+}
+
+int32_t topk_abi_version(void) { return 1; }
+
+}  // extern "C"

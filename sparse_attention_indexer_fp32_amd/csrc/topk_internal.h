@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI layer (topk_api.cpp) and the gfx950
+// kernels (topk_kernels.hip): launch parameters, workspace layout, launchers.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace topk {
+
+constexpr int kThreads = 1024;          // threads per workgroup (16 wave64s)
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxK = 2048;
+constexpr int kBinsWide = 4096;         // radix pass 0 digit: key bits 31..20
+constexpr int kBinsNarrow = 1024;       // passes 1 and 2: key bits 19..10, 9..0
+constexpr int kCandCap = 4096;          // threshold-bin candidates one workgroup finishes in LDS
+
+// Elements per thread the kernels are instantiated for (register-resident keys).
+constexpr int kNumEpt = 5;
+constexpr int kEptValues[kNumEpt] = {4, 8, 16, 32, 64};
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup workspace, in 32-bit words.  One region per (row slot,
+// parity); rows handled by one slot alternate parity, so a region is never
+// cleared while the slot's other workgroups already accumulate the next row.
+// Every region is left zeroed by the workgroup that finishes its row.
+// ---------------------------------------------------------------------------
+constexpr size_t kHdrWords = 64;        // [0] = fault word (a bounded wait timed out)
+constexpr size_t kBarWords = 32;        // per slot: [0] arrivals, [1] generation (own 128 B line)
+constexpr size_t kRegHist0 = 0;
+constexpr size_t kRegHist1 = kRegHist0 + kBinsWide;
+constexpr size_t kRegHist2 = kRegHist1 + kBinsNarrow;
+constexpr size_t kRegCtr = kRegHist2 + kBinsNarrow;   // 64 words of counters
+constexpr size_t kCtrGreater = 0;       // slots taken by strictly-greater elements
+constexpr size_t kCtrEqual = 16;        // tie slots / candidates appended
+constexpr size_t kCtrExit = 32;         // workgroups done with the row
+constexpr size_t kRegCandKey = kRegCtr + 64;
+constexpr size_t kRegCandPos = kRegCandKey + kCandCap;
+constexpr size_t kRegRaw = kRegCandPos + kCandCap;
+constexpr size_t kRegionWords = kRegRaw + kMaxK;
+
+inline size_t workspace_words(int64_t slots) {
+  return kHdrWords + (size_t)slots * kBarWords + (size_t)slots * 2 * kRegionWords;
+}
+
+struct KernelArgs {
+  const float* scores;        // (batch, width)
+  const int32_t* seq_lens;    // (batch,)
+  const int32_t* page_table;  // (batch, pages_per_row)
+  int32_t* out;               // (batch, k)
+  int32_t* out_raw;           // (batch, k) or nullptr
+  uint32_t* ws;               // workspace (wgs_per_row > 1 only)
+  int64_t width;
+  int64_t pages_per_row;
+  int32_t batch;
+  int32_t k;
+  int32_t log2_page;
+  int32_t wgs_per_row;        // G: workgroups sharing one row
+  int32_t slots;              // S: rows in flight; grid = S * G
+  int32_t ws_slots;           // slots the workspace was laid out for (>= slots)
+  int32_t vec;                // rows are 16-byte aligned: use dwordx4 loads
+};
+
+// ept_index selects kEptValues[ept_index]; coop selects the cross-workgroup
+// kernel (cooperative launch, grid = slots * wgs_per_row).
+hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStream_t stream);
+hipError_t rows_occupancy(int ept_index, bool coop, int* blocks_per_cu);
+
+}  // namespace topk

@@ -1,0 +1,78 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol, and
+rejects bad arguments before touching a device (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_fp32_amd as topk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topk_transform.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(topk_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(topk.LIB_PATH):
+        pytest.fail("libtopk_transform.so is not built (run __graft_entry__.build())")
+    return topk.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "topk_transform" in names and len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(topk.EXPORTED)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert topk.topk_abi_version() == 1
+    for code, name in topk.STATUS.items():
+        assert topk.topk_status_string(code) == name
+    assert topk.topk_status_string(99) == "TOPK_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("k,ps,batch,width,pages,expect", [
+    (0, 64, 1, 16, 1, 1),          # k below range
+    (2049, 64, 1, 16, 1, 1),       # k above range
+    (16, 3, 1, 16, 1, 1),          # page size not a power of two
+    (16, 0, 1, 16, 1, 1),
+    (16, -64, 1, 16, 1, 1),
+    (16, 64, -1, 16, 1, 1),        # negative batch
+    (16, 64, 1, -5, 1, 1),         # negative width
+    (16, 64, 1, 16, -1, 1),        # negative pages_per_row
+    (16, 64, 1, 2**31, 1, 1),      # width beyond int32
+    (16, 64, 0, 16, 1, 0),         # batch 0: no-op success
+    (2048, 1, 0, 0, 0, 0),
+    (16, 64, 3, 16, 1, 1),         # null pointers with batch > 0
+])
+def test_argument_validation_without_device(lib, k, ps, batch, width, pages, expect):
+    st = lib.topk_transform(None, None, None, k, ps, None, None, None, batch, width, pages)
+    assert st == expect, topk.topk_last_error()
+    if expect:
+        assert topk.topk_last_error()
+
+
+def test_dispatch_override_validation(lib):
+    assert lib.topk_set_dispatch_override(5, 0) == 1
+    assert lib.topk_set_dispatch_override(4, -1) == 1
+    assert lib.topk_set_dispatch_override(64, 3) == 0
+    assert lib.topk_set_dispatch_override(0, 0) == 0
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    s = torch.zeros((2, 8), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        topk.topk_transform(s, torch.zeros(2, dtype=torch.int32), torch.zeros((2, 1), dtype=torch.int32), 4, 8)
+    with pytest.raises(ValueError):
+        topk.topk_transform(s.double(), torch.zeros(2, dtype=torch.int32), torch.zeros((2, 1), dtype=torch.int32),
+                            4, 8)

@@ -1,0 +1,166 @@
+"""GPU parity: the HIP path (through the C-ABI binding) against the CPU oracle.
+
+Integer results, so the bar is bit-exact: the set of strictly-greater positions
+is unique and compared exactly; tied slots must hold distinct positions with
+exactly the threshold key; the transform is compared slot by slot.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import check, check_properties_all_rows, note, run, upload
+
+pytestmark = pytest.mark.gpu
+
+
+# ---- the five benchmark workloads at full size ------------------------------
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c3_b4", "c3_b8", "c4b", "c5"])
+def test_config_full(lib, name):
+    note(f"config {name}")
+    w = workloads.make(name)
+    lib.topk_set_dispatch_override(0, 0)
+    t = upload(w)
+    out, raw = run(lib, w, raw=True, tensors=t)
+    note(f"config {name}: {lib.topk_last_launch()}")
+    check(w, out, raw)
+    out2, _ = run(lib, w, raw=False, tensors=t)
+    check(w, out2, None)
+
+
+def test_config_c4a_sampled(lib):
+    """batch 2048 x 65536: every row checked by properties, 256 sampled rows by the oracle."""
+    note("config c4a")
+    w = workloads.c4a()
+    lib.topk_set_dispatch_override(0, 0)
+    out, raw = run(lib, w, raw=True)
+    note(f"config c4a: {lib.topk_last_launch()}")
+    check_properties_all_rows(w, out, raw)
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows = sorted(rng.choice(w.batch, size=256, replace=False).tolist())
+    check(w, out, raw, rows=rows)
+
+
+# ---- every kernel shape, forced, on shapes spanning several tiles + a ragged tail
+
+SHAPES = [
+    # (elems_per_thread, wgs_per_row)
+    (4, 0), (4, 3), (8, 0), (8, 2), (16, 0), (16, 5), (32, 0), (32, 2), (64, 0), (64, 2), (64, 1),
+]
+
+
+@pytest.mark.parametrize("ept,wgs", SHAPES)
+@pytest.mark.parametrize("kind", ["normal", "ties", "int"])
+def test_forced_shapes(lib, ept, wgs, kind):
+    W = 3 * 4096 + 123          # not a multiple of 4: scalar-load path, ragged tail
+    seq = [0, 1, 511, 512, 513, W, W - 1, 2 * 4096 + 7, -3, W + 50]
+    for k in (1, 512, 2048):
+        w = workloads.custom(100 + ept + wgs, len(seq), W, k, 16, seq_lens=seq, kind=kind)
+        note(f"forced ept={ept} wgs={wgs} kind={kind} k={k} W={W}")
+        lib.topk_set_dispatch_override(ept, wgs)
+        try:
+            out, raw = run(lib, w, raw=True)
+        finally:
+            lib.topk_set_dispatch_override(0, 0)
+        check(w, out, raw)
+
+
+@pytest.mark.parametrize("ept,wgs", [(4, 0), (16, 3), (64, 1), (32, 2)])
+def test_forced_shapes_aligned(lib, ept, wgs):
+    W = 40960                    # multiple of 4: dwordx4 path, partial last workgroup
+    seq = [W, W - 3, 4096, 4097, 0, 2047, 2048, 2049, 30000]
+    w = workloads.custom(7, len(seq), W, 2048, 64, seq_lens=seq, kind="normal", table="perm")
+    note(f"forced aligned ept={ept} wgs={wgs}")
+    lib.topk_set_dispatch_override(ept, wgs)
+    try:
+        out, raw = run(lib, w, raw=True)
+    finally:
+        lib.topk_set_dispatch_override(0, 0)
+    check(w, out, raw)
+
+
+# ---- edge cases -------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["const", "neginf", "zeros", "asc", "desc", "wide", "ties", "int"])
+@pytest.mark.parametrize("W", [5000, 70000])
+def test_adversarial_rows(lib, kind, W):
+    seq = [W, W // 2, 3, 1025, W - 1]
+    w = workloads.custom(11, len(seq), W, 1024, 16, seq_lens=seq, kind=kind)
+    note(f"adversarial kind={kind} W={W}")
+    lib.topk_set_dispatch_override(0, 0)
+    out, raw = run(lib, w, raw=True)
+    check(w, out, raw)
+
+
+@pytest.mark.parametrize("k", [1, 7, 512, 1024, 2047, 2048])
+@pytest.mark.parametrize("ps", [1, 16, 64, 256])
+def test_k_and_page_size(lib, k, ps):
+    W = 20000
+    seq = [0, 1, k - 1, k, k + 1, W]
+    seq = [max(s, 0) for s in seq]
+    w = workloads.custom(5 + k + ps, len(seq), W, k, ps, seq_lens=seq, kind="normal", table="perm")
+    note(f"k={k} ps={ps}")
+    out, raw = run(lib, w, raw=True)
+    check(w, out, raw)
+    out2, _ = run(lib, w, raw=False)
+    assert np.array_equal(out2 == -1, out == -1)
+    check(w, out2, None)
+
+
+def test_batch_zero_and_width_zero(lib):
+    import torch
+    dev = torch.device("cuda", 0)
+    s = torch.zeros((0, 16), dtype=torch.float32, device=dev)
+    out, _ = lib.topk_transform(s, torch.zeros(0, dtype=torch.int32, device=dev),
+                                torch.zeros((0, 1), dtype=torch.int32, device=dev), 8, 4)
+    assert out.shape == (0, 8)
+    s = torch.zeros((3, 0), dtype=torch.float32, device=dev)
+    out, raw = lib.topk_transform(s, torch.tensor([0, 5, -1], dtype=torch.int32, device=dev),
+                                  torch.zeros((3, 1), dtype=torch.int32, device=dev), 8, 4, want_raw=True)
+    torch.cuda.synchronize()
+    assert (out.cpu() == -1).all() and (raw.cpu() == -1).all()
+
+
+def test_repeated_split_rows_stress(lib):
+    """The cross-workgroup path, many times with fresh seeds (race check)."""
+    for rep in range(40):
+        B = 1 + rep % 6
+        W = 65536 + 4 * rep
+        seq = [W - rep * 37 % 5000 for _ in range(B)]
+        kind = ("normal", "ties", "int")[rep % 3]
+        w = workloads.custom(1000 + rep, B, W, 512 + rep * 37, 64, seq_lens=seq, kind=kind)
+        note(f"stress rep={rep} B={B} kind={kind}")
+        out, raw = run(lib, w, raw=rep % 2 == 0)
+        check(w, out, raw)
+    assert lib.topk_debug_fault_word() == 0
+
+
+def test_graph_replay(lib):
+    """Calls captured in a HIP graph and replayed give the eager result every time."""
+    import torch
+    w = workloads.custom(3, 4, 131072, 2048, 64, kind="normal")
+    s, sl, pt = upload(w)
+    out = torch.empty((w.batch, w.k), dtype=torch.int32, device=s.device)
+    lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)   # warm-up: workspace allocated outside capture
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy().copy()
+    check(w, eager, None)
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)  # warm the side stream's workspace
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)
+    for rep in range(5):
+        out.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        check(w, got, None)
+        s.add_(0.0)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_fault_word_clear(lib):
+    assert lib.topk_debug_fault_word() == 0
