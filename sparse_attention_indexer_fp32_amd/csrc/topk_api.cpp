@@ -184,7 +184,6 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, P
     }
   }
   if (plan->coop) {
-    if (!dev.coop) return fail(TOPK_ERROR_UNSUPPORTED, "device does not support cooperative launch");
     const int64_t cap = (int64_t)dev.occ[1][plan->ept_idx] * dev.cus;
     if (plan->G > cap)
       return fail(TOPK_ERROR_UNSUPPORTED, "row width needs more cooperating workgroups than fit resident");
@@ -259,7 +258,7 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
     a.ws_slots = (int32_t)capacity;
   }
   e = topk::launch_rows(plan.ept_idx, plan.coop, a, stream);
-  if (e != hipSuccess) return hip_fail(e, plan.coop ? "hipLaunchCooperativeKernel" : "kernel launch");
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
   char buf[160];
   std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d",
                 plan.coop ? "split-row" : "row-per-wg", topk::kEptValues[plan.ept_idx], (long long)plan.G,

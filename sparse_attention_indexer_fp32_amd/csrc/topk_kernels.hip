@@ -18,7 +18,8 @@
 //     bin where the count from the top crosses the remaining k.
 //   * Long rows are split over G workgroups (there is no distributed shared
 //     memory on CDNA4): partial histograms are merged with agent-scope global
-//     atomics and a per-row barrier in global memory.  When the threshold bin
+//     atomics and a per-row barrier in global memory (the grid is sized to
+//     what the GPU holds resident, so every workgroup of a row is running).  When the threshold bin
 //     is small enough, each workgroup appends its threshold-bin elements to a
 //     global candidate list and the last workgroup to leave the row finishes
 //     the remaining digits on the candidates in LDS -- one barrier per row
@@ -151,36 +152,42 @@ __device__ __forceinline__ void find_threshold(const uint32_t* h, int nb, uint32
   __syncthreads();
 }
 
-// Per-row barrier among the G workgroups of one slot (all co-resident: the
-// cross-workgroup kernel is launched cooperatively).  Sense is a generation
-// counter, so the barrier resets itself and works across calls and graph
-// replays.  The wait is bounded: on timeout the fault word is set and every
-// later wait returns at once, so the kernel always drains.
+// Waits until this wave's outstanding memory operations have completed.  All
+// cross-workgroup data moves through agent-scope atomics and agent-scope
+// (sc1, coherent) loads and stores, so once a wave's operations are complete
+// they are visible to every XCD; no L2 write-back or invalidate is needed.
+__device__ __forceinline__ void wave_mem_drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Per-row barrier among the G workgroups of one slot.  The grid never exceeds
+// the device's resident-workgroup capacity, so all G are running.  Sense is a
+// generation counter: the last arriver resets the arrival count (drained
+// before it bumps the generation), so the barrier resets itself across calls
+// and graph replays.  The wait is bounded: on timeout the fault word is set
+// and every later wait returns at once, so the kernel always drains.
 __device__ __forceinline__ void row_barrier(uint32_t* bar, int G, uint32_t* fault, int tid) {
-  // Every wave releases its own global writes (histogram atomics, staging
-  // stores) at agent scope before the workgroup meets: a plain workgroup
-  // barrier does not wait for outstanding global memory operations.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wave_mem_drain();
   __syncthreads();
   if (tid == 0) {
     const uint32_t gen = g_load(bar + 1);
-    const uint32_t old = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    wave_mem_drain();   // the generation is read before this workgroup's arrival
+    const uint32_t old = g_add_ret(bar, 1u);
     if (old == (uint32_t)G - 1) {
       g_store(bar, 0u);
-      __hip_atomic_fetch_add(bar + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      wave_mem_drain();
+      g_add(bar + 1, 1u);
     } else if (g_load(fault) == 0u) {
       uint32_t spins = 0;
-      while (__hip_atomic_load(bar + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(2);
+      while (g_load(bar + 1) == gen) {
+        __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) {
           g_store(fault, 1u);
           break;
         }
       }
     }
+    wave_mem_drain();
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // Gather + transform pass: slot j < n holds raw position r (trivial rows: r = j);
@@ -211,6 +218,38 @@ __device__ __forceinline__ void write_row_output(const KernelArgs& a, int64_t ro
 
 // Histogram of one radix digit over the register-resident keys that match the
 // prefix of the previous digits.
+// Register slots per thread that form the pass-0 sample (see hist_pass0).
+template <int E>
+struct SampleSlots {
+  static constexpr int value = E >= 16 ? 8 : E;
+};
+
+// Pass-0 histogram of the register-resident keys.  Slots [0, S) of every
+// thread are a sample: its full histogram gives the highest bin t_s such that
+// at least `need` sampled keys lie at or above it.  The row then has at least
+// `need` keys at or above t_s, so the threshold bin is >= t_s and only bins
+// >= t_s need exact counts: the other slots add to the histogram only when
+// their bin is >= t_s.  Exact for every bin the threshold search can reach,
+// with several times fewer LDS atomics on the usual (non-adversarial) rows.
+// For a split row each workgroup gates on its own sample, which is as valid:
+// the row's threshold bin is >= every workgroup's t_s.
+template <int E>
+__device__ __forceinline__ void hist_pass0(const uint32_t (&key)[E], uint32_t need, uint32_t* h,
+                                           uint32_t* sh_scan, uint32_t* sh_var, int tid) {
+  constexpr int S = SampleSlots<E>::value;
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+    if (key[j]) atomicAdd(&h[key[j] >> 20], 1u);
+  if (S == E) return;
+  __syncthreads();
+  find_threshold(h, kBinsWide, need, sh_scan, sh_var, tid);
+  // Bin >= 1 also excludes key 0 (no element).
+  const uint32_t gate = uniform(sh_var[0]) > 1u ? uniform(sh_var[0]) : 1u;
+#pragma unroll
+  for (int j = S; j < E; ++j)
+    if ((key[j] >> 20) >= gate) atomicAdd(&h[key[j] >> 20], 1u);
+}
+
 template <int E>
 __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass, uint32_t prefix,
                                               uint32_t* h) {
@@ -278,7 +317,7 @@ __device__ __forceinline__ void finish_candidates(int ncand, int pass_done, uint
 template <int E, bool COOP>
 __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
   __shared__ uint32_t sh_hist[kBinsWide];
-  __shared__ int32_t sh_raw[kMaxK];
+  __shared__ int32_t sh_raw[kMaxK + 64];   // + one trash word per lane
   __shared__ uint32_t sh_scan[kWaves + 1];
   __shared__ uint32_t sh_var[16];
   __shared__ uint32_t sh_ckey[COOP ? kCandCap : 1];
@@ -305,7 +344,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
       if (g == 0) write_row_output(a, row, L, n, true, sh_raw, tid);
       continue;
     }
-    const bool split = COOP && G > 1;
+    constexpr bool split = COOP;   // the host launches the split kernel only with G > 1
     // Consecutive split rows of a slot alternate regions.  A region is reused
     // two split rows later, after every workgroup of the slot has passed the
     // in-between row's first barrier -- which the finisher that clears it
@@ -375,7 +414,8 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
       for (int b = tid; b < nb; b += kThreads) sh_hist[b] = 0;
       __syncthreads();
       launder(key);
-      hist_resident<E>(key, pass, prefix, sh_hist);
+      if (pass == 0) hist_pass0<E>(key, need, sh_hist, sh_scan, sh_var, tid);
+      else hist_resident<E>(key, pass, prefix, sh_hist);
       __syncthreads();
       if (split) {
         uint32_t* gh = region + (pass == 0 ? kRegHist0 : pass == 1 ? kRegHist1 : kRegHist2);
@@ -415,10 +455,9 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const uint32_t x = key[j];
-      if (!x) continue;
       const uint32_t xp = x >> shift;
-      cg += xp > prefix;
-      ce += xp == prefix;
+      cg += xp > prefix ? 1u : 0u;
+      ce += (xp == prefix && x != 0u) ? 1u : 0u;
     }
     uint32_t tot;
     const uint32_t off = block_exclusive_scan((cg << 17) | ce, sh_scan, tot, tid);
@@ -433,28 +472,33 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
       off_g += uniform(sh_var[4]);
       off_e += uniform(sh_var[5]);
     }
+    // Selected keys are rare: a wave skips a register slot unless one of its
+    // lanes holds a key at or above the threshold prefix.  Inside, lanes that
+    // have nothing to store write a private trash word instead of branching.
+    const uint32_t trash = (uint32_t)kMaxK + (uint32_t)(tid & 63);
+    launder(key);   // recompute the compares here instead of keeping 2E masks from the counting loop
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const uint32_t x = key[j];
-      if (!x) continue;
       const uint32_t xp = x >> shift;
-      if (xp > prefix) {
-        const uint32_t s = off_g++;
-        if (s < n_gt) {
-          if (split) g_store(region + kRegRaw + s, (uint32_t)pos_of(j));
-          else sh_raw[s] = pos_of(j);
+      const bool isg = xp > prefix;
+      const bool ise = (xp == prefix) && (x != 0u);
+      if (__ballot(isg || ise) == 0ull) continue;
+      const uint32_t sg = off_g, se = off_e;
+      off_g += isg ? 1u : 0u;
+      off_e += ise ? 1u : 0u;
+      if (!split) {
+        const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : trash);
+        sh_raw[slot] = pos_of(j);
+      } else if (mode == kModeCands) {
+        if (isg && sg < n_gt) g_store(region + kRegRaw + sg, (uint32_t)pos_of(j));
+        if (ise && se < (uint32_t)kCandCap) {
+          g_store(region + kRegCandKey + se, x);
+          g_store(region + kRegCandPos + se, (uint32_t)pos_of(j));
         }
-      } else if (xp == prefix) {
-        const uint32_t e = off_e++;
-        if (mode == kModeCands) {
-          if (e < (uint32_t)kCandCap) {
-            g_store(region + kRegCandKey + e, x);
-            g_store(region + kRegCandPos + e, (uint32_t)pos_of(j));
-          }
-        } else if (e < need) {
-          if (split) g_store(region + kRegRaw + n_gt + e, (uint32_t)pos_of(j));
-          else sh_raw[n_gt + e] = pos_of(j);
-        }
+      } else {
+        const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : 0xFFFFFFFFu);
+        if (slot != 0xFFFFFFFFu) g_store(region + kRegRaw + slot, (uint32_t)pos_of(j));
       }
     }
 
@@ -465,16 +509,15 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     }
 
     // ---- the last workgroup to leave the row finishes it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    wave_mem_drain();
     __syncthreads();
     if (tid == 0) {
-      const uint32_t old =
-          __hip_atomic_fetch_add(region + kRegCtr + kCtrExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t old = g_add_ret(region + kRegCtr + kCtrExit, 1u);
+      wave_mem_drain();
       sh_var[6] = (old == (uint32_t)G - 1) ? 1u : 0u;
     }
     __syncthreads();
     if (!uniform(sh_var[6])) continue;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     const uint32_t filled = mode == kModeCands ? n_gt : (uint32_t)n;
     for (uint32_t j = tid; j < filled; j += kThreads) sh_raw[j] = (int32_t)g_load(region + kRegRaw + j);
@@ -503,16 +546,17 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 
 template <int E>
 hipError_t launch_e(bool coop, const KernelArgs& args, hipStream_t stream) {
+  // Split rows need every workgroup of a row resident at once; the host sizes
+  // the grid to at most the device's resident capacity for this kernel, so a
+  // regular launch suffices (a cooperative launch would add ~18 us per call).
   const dim3 block(kThreads);
   if (coop) {
     const dim3 grid((unsigned)args.slots * (unsigned)args.wgs_per_row);
-    KernelArgs local = args;
-    void* params[] = {&local};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&rows_kernel<E, true>), grid, block, params,
-                                      0, stream);
+    hipLaunchKernelGGL((rows_kernel<E, true>), grid, block, 0, stream, args);
+  } else {
+    const dim3 grid((unsigned)args.slots);
+    hipLaunchKernelGGL((rows_kernel<E, false>), grid, block, 0, stream, args);
   }
-  const dim3 grid((unsigned)args.slots);
-  hipLaunchKernelGGL((rows_kernel<E, false>), grid, block, 0, stream, args);
   return hipGetLastError();
 }
 
