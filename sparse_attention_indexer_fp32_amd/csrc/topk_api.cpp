@@ -31,7 +31,8 @@ struct DeviceInfo {
   bool supported = false;
   int cus = 0;
   bool coop = false;
-  int occ[2][topk::kNumEpt] = {};   // [coop][ept] resident workgroups per CU
+  int occ[2][topk::kNumEpt] = {};   // [split][ept] resident workgroups per CU
+  int stream_occ = 0;                // streaming kernel: resident workgroups per CU
   std::string arch;
 };
 
@@ -79,6 +80,8 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
         e = topk::rows_occupancy(i, c == 1, &info.occ[c][i]);
         if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
       }
+    e = topk::stream_occupancy(&info.stream_occ);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   }
   *out = &g_devices.emplace(dev, info).first->second;
   return TOPK_SUCCESS;
@@ -131,67 +134,94 @@ int ept_index(int ept) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+enum class Kind { kResident, kSplit, kStream };
+
 struct Plan {
+  Kind kind = Kind::kStream;
   int ept_idx = 0;
-  bool coop = false;
   int64_t G = 1;
   int64_t slots = 1;
 };
 
+const char* kind_name(Kind k) {
+  switch (k) {
+    case Kind::kResident: return "row-per-wg-resident";
+    case Kind::kSplit: return "split-row";
+    case Kind::kStream: return "row-per-wg-stream";
+  }
+  return "?";
+}
+
 // Kernel shape for (batch, width) on this device.
+//  * stream:   one workgroup per row, rows streamed from HBM with a sampled
+//              gate, two rows in flight per CU; persistent over rows.  Used
+//              when the batch alone fills the GPU, or rows are short.
+//  * split:    G workgroups per row holding the row in registers, merged
+//              through global atomics and a per-row barrier; for low-batch
+//              long rows.  Picks the most workgroups per row whose grid still
+//              fits resident.
+//  * resident: one workgroup per row holding the row in registers (testing
+//              and tuning override only).
 topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, Plan* plan) {
   const int64_t B = batch;
   const int64_t Wc = width > 0 ? width : 1;
-  const int64_t row_cap = (int64_t)topk::kThreads * topk::kEptValues[topk::kNumEpt - 1];
+  const int64_t stream_slots = (int64_t)dev.stream_occ * dev.cus;
+  auto split_ept_for = [&](int64_t wgs) {   // smallest E whose G for this width is <= wgs
+    int idx = 0;
+    while (idx < topk::kNumEpt - 1 && (int64_t)topk::kThreads * topk::kEptValues[idx] * wgs < Wc) ++idx;
+    return idx;
+  };
 
   if (g_override_ept || g_override_wgs) {
-    int idx = 0;
-    if (g_override_ept) {
-      idx = ept_index(g_override_ept);
+    if (g_override_wgs == 1 && g_override_ept == 0) {
+      plan->kind = Kind::kStream;
     } else {
-      while (idx < topk::kNumEpt - 1 && (int64_t)topk::kThreads * topk::kEptValues[idx] * g_override_wgs < Wc) ++idx;
-    }
-    const int64_t C = (int64_t)topk::kThreads * topk::kEptValues[idx];
-    int64_t G = ceil_div(Wc, C);
-    if (g_override_wgs > G) G = g_override_wgs;
-    plan->ept_idx = idx;
-    plan->G = G;
-    plan->coop = G > 1;
-  } else {
-    const int64_t cap_single = (int64_t)dev.cus;   // one resident row per CU is already a full wave
-    if (Wc <= row_cap && (B >= 2 * cap_single || Wc <= 8192)) {
-      int idx = 0;
-      while ((int64_t)topk::kThreads * topk::kEptValues[idx] < Wc) ++idx;
+      const int idx = g_override_ept ? ept_index(g_override_ept) : split_ept_for(g_override_wgs);
+      const int64_t C = (int64_t)topk::kThreads * topk::kEptValues[idx];
+      int64_t G = ceil_div(Wc, C);
+      if (g_override_wgs > G) G = g_override_wgs;
       plan->ept_idx = idx;
-      plan->G = 1;
-      plan->coop = false;
-    } else {
-      // Split rows: the most workgroups per row whose grid still fits resident.
-      int chosen = -1;
-      for (int i = 0; i < topk::kNumEpt; ++i) {
-        const int64_t G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[i]);
-        const int64_t cap = (int64_t)dev.occ[1][i] * dev.cus;
-        if (G >= 1 && B * G <= cap) {
-          chosen = i;
-          break;
-        }
+      plan->G = G;
+      plan->kind = G > 1 ? Kind::kSplit : Kind::kResident;
+    }
+  } else if (B >= stream_slots || Wc <= 16384) {
+    plan->kind = Kind::kStream;
+  } else {
+    int chosen = -1;
+    for (int i = 0; i < topk::kNumEpt; ++i) {
+      const int64_t G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[i]);
+      const int64_t cap = (int64_t)dev.occ[1][i] * dev.cus;
+      if (B * G <= cap) {
+        chosen = i;
+        break;
       }
-      if (chosen < 0) chosen = topk::kNumEpt - 1;
+    }
+    if (chosen < 0) {
+      plan->kind = Kind::kStream;   // too many rows to hold resident: stream them
+    } else {
       plan->ept_idx = chosen;
       plan->G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[chosen]);
-      plan->coop = plan->G > 1;
-      if (!plan->coop) plan->ept_idx = chosen;
+      plan->kind = plan->G > 1 ? Kind::kSplit : Kind::kStream;
     }
   }
-  if (plan->coop) {
-    const int64_t cap = (int64_t)dev.occ[1][plan->ept_idx] * dev.cus;
-    if (plan->G > cap)
-      return fail(TOPK_ERROR_UNSUPPORTED, "row width needs more cooperating workgroups than fit resident");
-    int64_t slots = cap / plan->G;
-    if (slots > B) slots = B;
-    plan->slots = slots;
-  } else {
-    plan->slots = B;
+  switch (plan->kind) {
+    case Kind::kStream:
+      plan->G = 1;
+      plan->slots = B < stream_slots ? B : stream_slots;
+      if (plan->slots < 1) plan->slots = 1;
+      break;
+    case Kind::kResident:
+      plan->slots = B;
+      break;
+    case Kind::kSplit: {
+      const int64_t cap = (int64_t)dev.occ[1][plan->ept_idx] * dev.cus;
+      if (plan->G > cap)
+        return fail(TOPK_ERROR_UNSUPPORTED, "row width needs more cooperating workgroups than fit resident");
+      int64_t slots = cap / plan->G;
+      if (slots > B) slots = B;
+      plan->slots = slots;
+      break;
+    }
   }
   return TOPK_SUCCESS;
 }
@@ -251,18 +281,21 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
   a.wgs_per_row = (int32_t)plan.G;
   a.slots = (int32_t)plan.slots;
   a.vec = (width % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
-  if (plan.coop) {
+  if (plan.kind == Kind::kSplit) {
     int64_t capacity = 0;
     st = get_workspace(dev, stream, plan.slots, &a.ws, &capacity);
     if (st != TOPK_SUCCESS) return st;
     a.ws_slots = (int32_t)capacity;
   }
-  e = topk::launch_rows(plan.ept_idx, plan.coop, a, stream);
+  if (plan.kind == Kind::kStream)
+    e = topk::launch_stream_rows(a, stream);
+  else
+    e = topk::launch_rows(plan.ept_idx, plan.kind == Kind::kSplit, a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   char buf[160];
   std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d",
-                plan.coop ? "split-row" : "row-per-wg", topk::kEptValues[plan.ept_idx], (long long)plan.G,
-                (long long)plan.slots, (long long)(plan.slots * plan.G), topk::kThreads, a.vec);
+                kind_name(plan.kind), plan.kind == Kind::kStream ? 0 : topk::kEptValues[plan.ept_idx],
+                (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G), topk::kThreads, a.vec);
   t_last_launch = buf;
   return TOPK_SUCCESS;
 }

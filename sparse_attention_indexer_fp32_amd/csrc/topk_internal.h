@@ -66,4 +66,8 @@ struct KernelArgs {
 hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStream_t stream);
 hipError_t rows_occupancy(int ept_index, bool coop, int* blocks_per_cu);
 
+// Streaming kernel, one workgroup per row, persistent over rows (grid = slots).
+hipError_t launch_stream_rows(const KernelArgs& args, hipStream_t stream);
+hipError_t stream_occupancy(int* blocks_per_cu);
+
 }  // namespace topk

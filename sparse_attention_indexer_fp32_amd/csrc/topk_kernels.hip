@@ -268,15 +268,20 @@ __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass
   }
 }
 
-// Finishes a row from its threshold-bin candidates held in LDS: the remaining
-// radix digits, then the compaction into staging slots [base, base + need).
-__device__ __forceinline__ void finish_candidates(int ncand, int pass_done, uint32_t prefix, int shift, uint32_t need,
-                                  uint32_t base, uint32_t* sh_hist, const uint32_t* sh_ckey,
+// Finishes a row from candidates held in LDS.  (prefix, shift) name the
+// current threshold bin (the candidates' keys >> shift), `cnt` how many keys
+// it holds and `need` how many of its keys are still to be selected; the
+// candidates contain every key of the threshold bin, and may also hold keys
+// above it (those are selected outright).  Refines the bin with the remaining
+// 10-bit digits, then writes the strictly-greater keys to slots
+// [gt_base, n - need_final) and `need_final` keys of the final bin to
+// [n - need_final, n).
+__device__ __forceinline__ void select_candidates(int ncand, uint32_t prefix, int shift, uint32_t cnt,
+                                                  uint32_t need, uint32_t gt_base, uint32_t n,
+                                                  uint32_t* sh_hist, const uint32_t* sh_ckey,
                                                   const int32_t* sh_cpos, int32_t* sh_raw, uint32_t* sh_scan,
                                                   uint32_t* sh_var, int tid) {
-  const uint32_t need0 = need;
-  int mode = kModeTies;
-  for (int pass = pass_done + 1; pass < 3; ++pass) {
+  while (shift > 0 && cnt != need) {
     for (int b = tid; b < kBinsNarrow; b += kThreads) sh_hist[b] = 0;
     __syncthreads();
     for (int i = tid; i < ncand; i += kThreads) {
@@ -285,33 +290,71 @@ __device__ __forceinline__ void finish_candidates(int ncand, int pass_done, uint
     }
     __syncthreads();
     find_threshold(sh_hist, kBinsNarrow, need, sh_scan, sh_var, tid);
-    const uint32_t bin = uniform(sh_var[0]), gt = uniform(sh_var[1]), cnt = uniform(sh_var[2]);
+    const uint32_t bin = uniform(sh_var[0]), gt = uniform(sh_var[1]);
+    cnt = uniform(sh_var[2]);
     need -= gt;
     prefix = (prefix << 10) | bin;
     shift -= 10;
-    if (cnt == need) {
-      mode = kModeTakeAll;
-      break;
-    }
   }
-  (void)mode;  // with shift == 0 the equal keys are identical: any `need` of them
+  // With shift == 0 the keys left in the bin are identical: any `need` of them.
+  const uint32_t gt_end = n - need;
   if (tid == 0) {
-    sh_var[8] = 0;
+    sh_var[8] = gt_base;
     sh_var[9] = 0;
   }
   __syncthreads();
-  const uint32_t gbase = base, ebase = base + (need0 - need);
   for (int i = tid; i < ncand; i += kThreads) {
     const uint32_t x = sh_ckey[i] >> shift;
     if (x > prefix) {
       const uint32_t s = atomicAdd(&sh_var[8], 1u);
-      if (gbase + s < ebase && gbase + s < (uint32_t)kMaxK) sh_raw[gbase + s] = sh_cpos[i];
-    } else if (x == prefix) {
+      if (s < gt_end) sh_raw[s] = sh_cpos[i];
+    } else if (x == prefix && sh_ckey[i] != 0u) {
       const uint32_t e = atomicAdd(&sh_var[9], 1u);
-      if (e < need && ebase + e < (uint32_t)kMaxK) sh_raw[ebase + e] = sh_cpos[i];
+      if (e < need) sh_raw[gt_end + e] = sh_cpos[i];
     }
   }
   __syncthreads();
+}
+
+// Loads V float4 groups of a row chunk into keys: group v of thread tid holds
+// positions cbase + 4*tid + 4096*v + {0..3}.  One dwordx4 buffer load per group
+// when the row is 16-byte aligned, else four dword loads.  The descriptor
+// spans only the valid part of the chunk (whole 16-byte groups when aligned:
+// the width is then a multiple of 4, so they stay inside the row), so the
+// hardware returns 0 past seq_len and past the tensor without a branch; those
+// slots become key 0 ("no element").  All loads are issued before any is used.
+template <int V>
+__device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* rowp, uint32_t cbase,
+                                          uint32_t L, bool vec, int tid) {
+  constexpr uint32_t span = (uint32_t)kThreads * 4u * V;
+  const uint32_t rem = L > cbase ? L - cbase : 0u;
+  const uint32_t nvalid = rem < span ? rem : span;
+  const uint32_t nbytes = vec ? ((nvalid + 3u) & ~3u) * 4u : nvalid * 4u;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rowp) + cbase, (short)0, (int)nbytes, kBufferWord3);
+  const uint32_t voff = (uint32_t)tid * 16u;
+  const int32_t lpos = tid * 4;
+  if (vec) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, v * (kThreads * 16), 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t lim = (int32_t)nvalid - (v * kThreads * 4 + i);   // a scalar
+        key[4 * v + i] = (lpos < lim) ? order_key_bits(x[i]) : 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, v * (kThreads * 16) + 4 * i, 0);
+        const int32_t lim = (int32_t)nvalid - (v * kThreads * 4 + i);
+        key[4 * v + i] = (lpos < lim) ? order_key_bits(x) : 0u;
+      }
+    }
+  }
 }
 
 template <int E, bool COOP>
@@ -358,50 +401,10 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 
     // ---- load this workgroup's share of the row into registers (one HBM read)
     const float* rowp = a.scores + row * W;
-    // Element j of thread tid sits at position c0 + 4*tid + 4096*(j/4) + j%4:
-    // each group of four is one dwordx4 buffer load when the row is 16-byte
-    // aligned, else four dword loads of the same positions.  The buffer
-    // descriptor covers only the valid part of this chunk, so the hardware
-    // bounds check returns 0 past seq_len (and past the tensor) without a
-    // branch; those slots become key 0 ("no element").  All loads are issued
-    // before the first one is consumed.
     const uint32_t c0 = (uint32_t)g * (uint32_t)C;
-    const int64_t rem = L - (int64_t)c0;
-    const uint32_t nvalid = rem <= 0 ? 0u : (rem >= C ? (uint32_t)C : (uint32_t)rem);
     const uint32_t pbase = c0 + (uint32_t)tid * 4u;
     uint32_t key[E];
-    {
-      // With dwordx4 loads the descriptor spans whole 16-byte groups (still
-      // inside the row: the width is a multiple of 4 then), so no load
-      // straddles num_records; positions past seq_len are masked below.
-      const uint32_t nbytes = a.vec ? ((nvalid + 3u) & ~3u) * 4u : nvalid * 4u;
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(rowp) + c0, (short)0, (int)nbytes, kBufferWord3);
-      const uint32_t voff = (uint32_t)tid * 16u;
-      const uint32_t lpos = (uint32_t)tid * 4u;   // position within the chunk
-      if (a.vec) {
-#pragma unroll
-        for (int v = 0; v < E / 4; ++v) {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, v * (kThreads * 16), 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // valid iff lpos + offset < nvalid; the limit is a scalar
-            const int32_t lim = (int32_t)nvalid - (v * kThreads * 4 + i);
-            key[4 * v + i] = ((int32_t)lpos < lim) ? order_key_bits(x[i]) : 0u;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < E / 4; ++v) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, v * (kThreads * 16) + 4 * i, 0);
-            const int32_t lim = (int32_t)nvalid - (v * kThreads * 4 + i);
-            key[4 * v + i] = ((int32_t)lpos < lim) ? order_key_bits(x) : 0u;
-          }
-        }
-      }
-    }
+    load_keys<E / 4>(key, rowp, c0, (uint32_t)L, a.vec != 0, tid);
     auto pos_of = [&](int j) -> int32_t {
       return (int32_t)(pbase + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3));
     };
@@ -528,8 +531,8 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
         sh_cpos[i] = (int32_t)g_load(region + kRegCandPos + i);
       }
       __syncthreads();
-      finish_candidates(ncand, pass, prefix, shift, need, n_gt, sh_hist, sh_ckey, sh_cpos, sh_raw, sh_scan,
-                        sh_var, tid);
+      select_candidates(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
+                        sh_scan, sh_var, tid);
     }
     __syncthreads();
     write_row_output(a, row, L, n, false, sh_raw, tid);
@@ -542,6 +545,259 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     if (tid < 64) g_store(region + kRegCtr + tid, 0u);
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming one-workgroup-per-row kernel (large batches).
+//
+// Holding a 64K row in registers leaves one row per CU and nothing to overlap
+// its radix passes with; streaming keeps two rows in flight per CU instead.
+//   1. Sample: the first kStreamSample positions (16 keys per thread) are
+//      histogrammed in full; the sample's threshold bin is a gate such that at
+//      least n keys of the row lie at or above it.
+//   2. Stream: every key at or above the gate is counted (so the histogram is
+//      exact for every bin >= gate) and appended to an LDS candidate list;
+//      slots come from wave ballots, one LDS atomic per wave per chunk.  When
+//      the list fills, the gate is raised to the threshold bin of the keys
+//      seen so far (still a valid lower bound) and the list is compacted.
+//   3. The threshold bin comes from the exact histogram; the remaining digits
+//      run on the candidates only.
+// If the list overflows anyway (adversarial rows: a single bin holding more
+// keys than the list), the row is redone by re-streaming it from memory with
+// one more digit per pass until the threshold bin fits (exact, slower).
+// ---------------------------------------------------------------------------
+
+constexpr int kStreamCap = 6144;                    // LDS candidates per row
+constexpr int kStreamRefresh = kStreamCap / 2;      // raise the gate past this many
+constexpr int kSampleVecs = 4;                      // sample: 16 keys per thread = 16K positions
+constexpr int kChunkVecs = 2;                       // streamed chunk: 8 keys per thread = 8K positions
+constexpr uint32_t kSampleSpan = (uint32_t)kThreads * 4u * kSampleVecs;
+constexpr uint32_t kChunkSpan = (uint32_t)kThreads * 4u * kChunkVecs;
+
+// Stream-kernel LDS words (sh_var indices).
+enum : int { kVarCandCount = 10, kVarOverflow = 11, kVarGt = 12, kVarEq = 13 };
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Appends the keys whose 12-bit bin is >= gate (key 0 never passes: gate >= 1)
+// to the candidate list, and adds them to the histogram unless already counted.
+template <int N>
+__device__ __forceinline__ void gated_append(const uint32_t (&key)[N], uint32_t cbase, uint32_t gate,
+                                             bool counted, uint32_t* sh_hist, uint32_t* sh_ckey,
+                                             int32_t* sh_cpos, uint32_t* sh_var, int tid) {
+  uint64_t m[N];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    m[j] = __ballot((key[j] >> 20) >= gate);
+    tot += (uint32_t)__popcll(m[j]);
+  }
+  if (tot == 0u) return;
+  uint32_t base = 0;
+  if ((tid & 63) == 0) base = atomicAdd(&sh_var[kVarCandCount], tot);
+  base = __builtin_amdgcn_readfirstlane(base);
+  const uint32_t p0 = cbase + (uint32_t)tid * 4u;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    if (m[j] == 0ull) continue;
+    if ((key[j] >> 20) >= gate) {
+      if (!counted) atomicAdd(&sh_hist[key[j] >> 20], 1u);
+      const uint32_t slot = base + lanes_below(m[j]);
+      if (slot < (uint32_t)kStreamCap) {
+        sh_ckey[slot] = key[j];
+        sh_cpos[slot] = (int32_t)(p0 + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3));
+      }
+    }
+    base += (uint32_t)__popcll(m[j]);
+  }
+}
+
+// Raises the gate to the threshold bin of the keys counted so far (exact for
+// every bin >= gate) and drops the candidates below it.  Uniform; returns the
+// new gate.
+__device__ __forceinline__ uint32_t raise_gate(uint32_t gate, uint32_t n, uint32_t* sh_hist, uint32_t* sh_ckey,
+                                               int32_t* sh_cpos, uint32_t* sh_scan, uint32_t* sh_var, int tid) {
+  find_threshold(sh_hist, kBinsWide, n, sh_scan, sh_var, tid);
+  const uint32_t t = uniform(sh_var[0]);
+  if (t <= gate) return gate;
+  const uint32_t count = uniform(sh_var[kVarCandCount]);
+  const uint32_t ncur = count < (uint32_t)kStreamCap ? count : (uint32_t)kStreamCap;
+  constexpr int R = (kStreamCap + kThreads - 1) / kThreads;
+  uint32_t ck[R];
+  int32_t cp[R];
+  uint32_t keep = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t i = (uint32_t)(tid + r * kThreads);
+    ck[r] = i < ncur ? sh_ckey[i] : 0u;
+    cp[r] = i < ncur ? sh_cpos[i] : 0;
+    keep += (ck[r] >> 20) >= t ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t off = block_exclusive_scan(keep, sh_scan, total, tid);   // barriers: all reads are done
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if ((ck[r] >> 20) >= t) {
+      sh_ckey[off] = ck[r];
+      sh_cpos[off] = cp[r];
+      ++off;
+    }
+  }
+  if (tid == 0) {
+    if (count > (uint32_t)kStreamCap) sh_var[kVarOverflow] = 1u;   // keys were lost: redo the row
+    sh_var[kVarCandCount] = total;
+  }
+  __syncthreads();
+  return t;
+}
+
+// One pass over the row from memory, for the overflow path: with
+// mode 0, histograms the next 10-bit digit of the keys whose key >> shift
+// equals prefix; with mode 1, writes keys above the bin to slots [0, n - need)
+// and collects the bin's keys as candidates; with mode 2 (final digit, or the
+// whole bin is selected), writes keys above the bin to [0, n - need) and
+// `need` keys of the bin to [n - need, n).
+__device__ __forceinline__ void restream_pass(int mode, const float* rowp, uint32_t L, bool vec, uint32_t prefix,
+                                              int shift, uint32_t need, uint32_t n, uint32_t* sh_hist,
+                                              uint32_t* sh_ckey, int32_t* sh_cpos, int32_t* sh_raw,
+                                              uint32_t* sh_var, int tid) {
+  const uint32_t gt_end = n - need;
+  for (uint32_t c = 0; c < L; c += kChunkSpan) {
+    uint32_t key[4 * kChunkVecs];
+    load_keys<kChunkVecs>(key, rowp, c, L, vec, tid);
+    const uint32_t p0 = c + (uint32_t)tid * 4u;
+#pragma unroll
+    for (int j = 0; j < 4 * kChunkVecs; ++j) {
+      const uint32_t x = key[j];
+      if (x == 0u) continue;
+      const uint32_t xp = x >> shift;
+      const int32_t pos = (int32_t)(p0 + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3));
+      if (mode == 0) {
+        if (xp == prefix) atomicAdd(&sh_hist[(x >> (shift - 10)) & 1023u], 1u);
+      } else if (xp > prefix) {
+        const uint32_t s = atomicAdd(&sh_var[kVarGt], 1u);
+        if (s < gt_end) sh_raw[s] = pos;
+      } else if (xp == prefix) {
+        const uint32_t e = atomicAdd(&sh_var[kVarEq], 1u);
+        if (mode == 1) {
+          if (e < (uint32_t)kStreamCap) {
+            sh_ckey[e] = x;
+            sh_cpos[e] = pos;
+          }
+        } else if (e < need) {
+          sh_raw[gt_end + e] = pos;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+stream_rows_kernel(KernelArgs a) {
+  __shared__ uint32_t sh_hist[kBinsWide];
+  __shared__ uint32_t sh_ckey[kStreamCap];
+  __shared__ int32_t sh_cpos[kStreamCap];
+  __shared__ int32_t sh_raw[kMaxK];
+  __shared__ uint32_t sh_scan[kWaves + 1];
+  __shared__ uint32_t sh_var[16];
+
+  const int64_t W = a.width;
+  const int k = a.k;
+  const bool vec = a.vec != 0;
+  for (int64_t row = blockIdx.x; row < a.batch; row += gridDim.x) {
+    const int tid = opaque_tid();
+    const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+    const int64_t L64 = sl < 0 ? 0 : ((int64_t)sl > W ? W : (int64_t)sl);
+    const uint32_t L = (uint32_t)L64;
+    const int n = L64 < (int64_t)k ? (int)L64 : k;
+    if (L64 <= (int64_t)k) {
+      write_row_output(a, row, L64, n, true, sh_raw, tid);
+      continue;
+    }
+    for (int b = tid; b < kBinsWide; b += kThreads) sh_hist[b] = 0;
+    for (int j = tid; j < k; j += kThreads) sh_raw[j] = -1;
+    if (tid < 16) sh_var[tid] = 0;
+    const float* rowp = a.scores + row * W;
+    __syncthreads();
+
+    // 1. sample: full histogram of the first kSampleSpan positions
+    uint32_t sk[4 * kSampleVecs];
+    load_keys<kSampleVecs>(sk, rowp, 0u, L, vec, tid);
+#pragma unroll
+    for (int j = 0; j < 4 * kSampleVecs; ++j)
+      if (sk[j]) atomicAdd(&sh_hist[sk[j] >> 20], 1u);
+    __syncthreads();
+    find_threshold(sh_hist, kBinsWide, (uint32_t)n, sh_scan, sh_var, tid);
+    uint32_t gate = uniform(sh_var[0]) > 1u ? uniform(sh_var[0]) : 1u;
+    gated_append(sk, 0u, gate, true, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
+
+    // 2. stream the rest, two chunks in flight
+    uint32_t ka[4 * kChunkVecs], kb[4 * kChunkVecs];
+    uint32_t c = kSampleSpan;
+    if (c < L) load_keys<kChunkVecs>(ka, rowp, c, L, vec, tid);
+    while (c < L) {
+      const uint32_t cb = c + kChunkSpan;
+      if (cb < L) load_keys<kChunkVecs>(kb, rowp, cb, L, vec, tid);
+      gated_append(ka, c, gate, false, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
+      if (cb < L) {
+        const uint32_t ca = cb + kChunkSpan;
+        if (ca < L) load_keys<kChunkVecs>(ka, rowp, ca, L, vec, tid);
+        gated_append(kb, cb, gate, false, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
+      }
+      c = cb + kChunkSpan;
+      __syncthreads();
+      if (uniform(sh_var[kVarCandCount]) > (uint32_t)kStreamRefresh)
+        gate = raise_gate(gate, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_scan, sh_var, tid);
+    }
+    __syncthreads();
+
+    // 3. threshold bin from the exact histogram, then the candidates
+    find_threshold(sh_hist, kBinsWide, (uint32_t)n, sh_scan, sh_var, tid);
+    const uint32_t t0 = uniform(sh_var[0]), gt0 = uniform(sh_var[1]), cnt0 = uniform(sh_var[2]);
+    const uint32_t count = uniform(sh_var[kVarCandCount]);
+    const bool overflow = uniform(sh_var[kVarOverflow]) != 0u || count > (uint32_t)kStreamCap;
+    if (!overflow) {
+      select_candidates((int)count, t0, 20, cnt0, (uint32_t)n - gt0, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
+                        sh_raw, sh_scan, sh_var, tid);
+    } else {
+      uint32_t prefix = t0, need = (uint32_t)n - gt0, cnt = cnt0;
+      int shift = 20;
+      while (cnt > (uint32_t)kStreamCap && cnt != need && shift > 0) {
+        for (int b = tid; b < kBinsNarrow; b += kThreads) sh_hist[b] = 0;
+        __syncthreads();
+        restream_pass(0, rowp, L, vec, prefix, shift, need, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw, sh_var,
+                      tid);
+        find_threshold(sh_hist, kBinsNarrow, need, sh_scan, sh_var, tid);
+        const uint32_t bin = uniform(sh_var[0]), gt = uniform(sh_var[1]);
+        cnt = uniform(sh_var[2]);
+        need -= gt;
+        prefix = (prefix << 10) | bin;
+        shift -= 10;
+      }
+      if (tid == 0) {
+        sh_var[kVarGt] = 0;
+        sh_var[kVarEq] = 0;
+      }
+      __syncthreads();
+      const bool collect = cnt <= (uint32_t)kStreamCap && cnt != need && shift > 0;
+      restream_pass(collect ? 1 : 2, rowp, L, vec, prefix, shift, need, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
+                    sh_raw, sh_var, tid);
+      if (collect)
+        select_candidates((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist, sh_ckey,
+                          sh_cpos, sh_raw, sh_scan, sh_var, tid);
+    }
+    __syncthreads();
+    write_row_output(a, row, L64, n, false, sh_raw, tid);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_stream(const KernelArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_rows_kernel, dim3((unsigned)args.slots), dim3(kThreads), 0, stream, args);
+  return hipGetLastError();
 }
 
 template <int E>
@@ -580,6 +836,13 @@ hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStre
     case 4: return launch_e<64>(coop, args, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_stream_rows(const KernelArgs& args, hipStream_t stream) { return launch_stream(args, stream); }
+
+hipError_t stream_occupancy(int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(&stream_rows_kernel),
+                                                      kThreads, 0);
 }
 
 hipError_t rows_occupancy(int ept_index, bool coop, int* blocks_per_cu) {

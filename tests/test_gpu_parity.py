@@ -44,8 +44,9 @@ def test_config_c4a_sampled(lib):
 # ---- every kernel shape, forced, on shapes spanning several tiles + a ragged tail
 
 SHAPES = [
-    # (elems_per_thread, wgs_per_row)
-    (4, 0), (4, 3), (8, 0), (8, 2), (16, 0), (16, 5), (32, 0), (32, 2), (64, 0), (64, 2), (64, 1),
+    # (elems_per_thread, wgs_per_row): (0, 1) is the streaming one-workgroup-per-row kernel,
+    # (E, 1) the register-resident one, G > 1 the split-row kernel.
+    (0, 1), (4, 0), (4, 3), (8, 0), (8, 2), (16, 0), (16, 5), (32, 0), (32, 2), (64, 0), (64, 2), (64, 1),
 ]
 
 
@@ -65,7 +66,7 @@ def test_forced_shapes(lib, ept, wgs, kind):
         check(w, out, raw)
 
 
-@pytest.mark.parametrize("ept,wgs", [(4, 0), (16, 3), (64, 1), (32, 2)])
+@pytest.mark.parametrize("ept,wgs", [(0, 1), (4, 0), (16, 3), (64, 1), (32, 2)])
 def test_forced_shapes_aligned(lib, ept, wgs):
     W = 40960                    # multiple of 4: dwordx4 path, partial last workgroup
     seq = [W, W - 3, 4096, 4097, 0, 2047, 2048, 2049, 30000]
@@ -90,6 +91,23 @@ def test_adversarial_rows(lib, kind, W):
     lib.topk_set_dispatch_override(0, 0)
     out, raw = run(lib, w, raw=True)
     check(w, out, raw)
+
+
+@pytest.mark.parametrize("kind", ["const", "neginf", "zeros", "asc", "desc", "wide", "ties", "int", "normal"])
+@pytest.mark.parametrize("W", [9000, 50000, 140001])
+def test_stream_kernel_adversarial(lib, kind, W):
+    """The streaming kernel, including its candidate-overflow re-stream path
+    (constant, -inf-only and ascending rows overflow the LDS candidate list)."""
+    seq = [W, W - 1, W // 3, 2049, 17000, 0]
+    for k in (1, 512, 2048):
+        w = workloads.custom(21 + k, len(seq), W, k, 16, seq_lens=seq, kind=kind)
+        note(f"stream kind={kind} W={W} k={k}")
+        lib.topk_set_dispatch_override(0, 1)
+        try:
+            out, raw = run(lib, w, raw=True)
+        finally:
+            lib.topk_set_dispatch_override(0, 0)
+        check(w, out, raw)
 
 
 @pytest.mark.parametrize("k", [1, 7, 512, 1024, 2047, 2048])
