@@ -87,13 +87,27 @@ __device__ __forceinline__ void g_store(uint32_t* p, uint32_t v) {
 }
 
 // ---- scans -----------------------------------------------------------------
+// DPP controls (gfx9 family).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive sum over the 16 lanes of each DPP row (lane 15 of a row ends with
+// the row total).  Out-of-row sources read as 0.
+__device__ __forceinline__ uint32_t row16_inclusive_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr1, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr2, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr4, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr8, 0xf, 0xf, false);
+  return v;
+}
+
+// Inclusive sum over the 64 lanes of a wave: per-row scans, then the row
+// totals carried across rows with the row-broadcast DPP modes.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int tid) {
-  const int lane = tid & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  (void)tid;
+  v = row16_inclusive_scan(v);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xa, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xc, 0xf, false);
   return v;
 }
 
@@ -119,34 +133,52 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return r;
 }
 
-// Threshold bin of histogram h[0, nb): the highest bin t with
-// sum_{b >= t} h[b] >= need.  Writes sh_var[0] = t, sh_var[1] = count in bins
-// above t, sh_var[2] = h[t].  (If the histogram holds fewer than `need`
+// Threshold bin of histogram h[0, nb), nb = 4096 or 1024: the highest bin t
+// with sum_{b >= t} h[b] >= need.  Writes sh_var[0] = t, sh_var[1] = count in
+// bins above t, sh_var[2] = h[t].  (If the histogram holds fewer than `need`
 // elements -- impossible for valid input -- it reports bin 0 with counts 0.)
-__device__ __forceinline__ void find_threshold(const uint32_t* h, int nb, uint32_t need, uint32_t* sh_scan,
+//
+// Two levels, one barrier in between: every group of 64 bins is summed by a
+// DPP reduction (16 lanes x 4 bins, or a full wave x 1 bin) into sh_coarse;
+// then wave 0 scans the group totals from the top to find the crossing group,
+// and scans that group's 64 bins to find the crossing bin (ballot + first set
+// lane locate both crossings).
+__device__ __forceinline__ void find_threshold(const uint32_t* h, int nb, uint32_t need, uint32_t* sh_coarse,
                                                uint32_t* sh_var, int tid) {
-  const int per = nb / kThreads;
-  const int top = nb - per * tid;   // this thread covers bins [top - per, top), highest first
-  uint32_t s = 0;
-  for (int i = 1; i <= per; ++i) s += h[top - i];
-  if (tid == 0) {
-    sh_var[0] = 0;
-    sh_var[1] = 0;
-    sh_var[2] = 0;
+  const int lane = tid & 63;
+  const int ngroups = nb >> 6;
+  if (nb == kBinsWide) {
+    const int b0 = tid * 4;
+    const uint32_t s = h[b0] + h[b0 + 1] + h[b0 + 2] + h[b0 + 3];
+    const uint32_t r = row16_inclusive_scan(s);
+    if ((lane & 15) == 15) sh_coarse[tid >> 4] = r;
+  } else {
+    const uint32_t r = wave_inclusive_scan(h[tid], tid);
+    if (lane == 63) sh_coarse[tid >> 6] = r;
   }
-  uint32_t total;
-  const uint32_t before = block_exclusive_scan(s, sh_scan, total, tid);
-  if (before < need && before + s >= need) {
-    uint32_t acc = before;
-    for (int i = 1; i <= per; ++i) {
-      const uint32_t c = h[top - i];
-      if (acc + c >= need) {
-        sh_var[0] = (uint32_t)(top - i);
-        sh_var[1] = acc;
-        sh_var[2] = c;
-        break;
-      }
-      acc += c;
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t v = lane < ngroups ? sh_coarse[ngroups - 1 - lane] : 0u;   // lane 0 = highest group
+    const uint32_t cum = wave_inclusive_scan(v, tid);
+    const uint64_t hit = __ballot(lane < ngroups && cum >= need);
+    uint32_t bin = 0, above = 0, cnt = 0;
+    if (hit != 0ull) {
+      const int lg = __builtin_ctzll(hit);
+      const int grp = ngroups - 1 - lg;
+      const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)cum, lg) -
+                              (uint32_t)__builtin_amdgcn_readlane((int)v, lg);
+      const uint32_t fv = h[grp * 64 + 63 - lane];                         // lane 0 = highest bin of the group
+      const uint32_t fcum = wave_inclusive_scan(fv, tid);
+      const uint64_t fhit = __ballot(before + fcum >= need);
+      const int lf = __builtin_ctzll(fhit);
+      bin = (uint32_t)(grp * 64 + 63 - lf);
+      cnt = (uint32_t)__builtin_amdgcn_readlane((int)fv, lf);
+      above = before + (uint32_t)__builtin_amdgcn_readlane((int)fcum, lf) - cnt;
+    }
+    if (lane == 0) {
+      sh_var[0] = bin;
+      sh_var[1] = above;
+      sh_var[2] = cnt;
     }
   }
   __syncthreads();
@@ -316,16 +348,17 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t prefix, in
   __syncthreads();
 }
 
-// Loads V float4 groups of a row chunk into keys: group v of thread tid holds
+// Raw loads of V float4 groups of a row chunk: group v of thread tid holds
 // positions cbase + 4*tid + 4096*v + {0..3}.  One dwordx4 buffer load per group
 // when the row is 16-byte aligned, else four dword loads.  The descriptor
 // spans only the valid part of the chunk (whole 16-byte groups when aligned:
 // the width is then a multiple of 4, so they stay inside the row), so the
-// hardware returns 0 past seq_len and past the tensor without a branch; those
-// slots become key 0 ("no element").  All loads are issued before any is used.
+// hardware returns 0 past seq_len and past the tensor without a branch.
+// Nothing here consumes the data, so the loads stay in flight until the
+// caller's first use (chunks are double-buffered this way).
 template <int V>
-__device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* rowp, uint32_t cbase,
-                                          uint32_t L, bool vec, int tid) {
+__device__ __forceinline__ void load_raw(uint32_t (&raw)[4 * V], const float* rowp, uint32_t cbase, uint32_t L,
+                                         bool vec, int tid) {
   constexpr uint32_t span = (uint32_t)kThreads * 4u * V;
   const uint32_t rem = L > cbase ? L - cbase : 0u;
   const uint32_t nvalid = rem < span ? rem : span;
@@ -333,35 +366,41 @@ __device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* r
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rowp) + cbase, (short)0, (int)nbytes, kBufferWord3);
   const uint32_t voff = (uint32_t)tid * 16u;
-  const int32_t lpos = tid * 4;
   if (vec) {
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, v * (kThreads * 16), 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t lim = (int32_t)nvalid - (v * kThreads * 4 + i);   // a scalar
-        key[4 * v + i] = (lpos < lim) ? order_key_bits(x[i]) : 0u;
-      }
+      for (int i = 0; i < 4; ++i) raw[4 * v + i] = x[i];
     }
   } else {
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
+    for (int v = 0; v < V; ++v)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, v * (kThreads * 16) + 4 * i, 0);
-        const int32_t lim = (int32_t)nvalid - (v * kThreads * 4 + i);
-        key[4 * v + i] = (lpos < lim) ? order_key_bits(x) : 0u;
-      }
-    }
+      for (int i = 0; i < 4; ++i)
+        raw[4 * v + i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, v * (kThreads * 16) + 4 * i, 0);
   }
+}
+
+// Order key of raw slot j of a chunk at cbase, or 0 ("no element") past L.
+__device__ __forceinline__ uint32_t slot_key(uint32_t raw, int j, uint32_t cbase, uint32_t L, int tid) {
+  const int64_t lim = (int64_t)L - (int64_t)cbase - (int64_t)((j >> 2) * kThreads * 4 + (j & 3));   // a scalar
+  return ((int64_t)(tid * 4) < lim) ? order_key_bits(raw) : 0u;
+}
+
+template <int V>
+__device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* rowp, uint32_t cbase, uint32_t L,
+                                          bool vec, int tid) {
+  load_raw<V>(key, rowp, cbase, L, vec, tid);
+#pragma unroll
+  for (int j = 0; j < 4 * V; ++j) key[j] = slot_key(key[j], j, cbase, L, tid);
 }
 
 template <int E, bool COOP>
 __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
   __shared__ uint32_t sh_hist[kBinsWide];
   __shared__ int32_t sh_raw[kMaxK + 64];   // + one trash word per lane
-  __shared__ uint32_t sh_scan[kWaves + 1];
+  __shared__ uint32_t sh_scan[64];   // block-scan wave totals, or the 64 coarse bins of find_threshold
   __shared__ uint32_t sh_var[16];
   __shared__ uint32_t sh_ckey[COOP ? kCandCap : 1];
   __shared__ int32_t sh_cpos[COOP ? kCandCap : 1];
@@ -584,9 +623,12 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 // Appends the keys whose 12-bit bin is >= gate (key 0 never passes: gate >= 1)
 // to the candidate list, and adds them to the histogram unless already counted.
 template <int N>
-__device__ __forceinline__ void gated_append(const uint32_t (&key)[N], uint32_t cbase, uint32_t gate,
+__device__ __forceinline__ void gated_append(const uint32_t (&raw)[N], uint32_t cbase, uint32_t L, uint32_t gate,
                                              bool counted, uint32_t* sh_hist, uint32_t* sh_ckey,
                                              int32_t* sh_cpos, uint32_t* sh_var, int tid) {
+  uint32_t key[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) key[j] = slot_key(raw[j], j, cbase, L, tid);
   uint64_t m[N];
   uint32_t tot = 0;
 #pragma unroll
@@ -616,7 +658,10 @@ __device__ __forceinline__ void gated_append(const uint32_t (&key)[N], uint32_t 
 
 // Raises the gate to the threshold bin of the keys counted so far (exact for
 // every bin >= gate) and drops the candidates below it.  Uniform; returns the
-// new gate.
+// new gate.  The list is compacted in place in rounds of 2 * kThreads
+// entries: a round's entries are read into registers before any is written,
+// and kept entries only move down (to positions below the round's end), so
+// no unread entry is overwritten.
 __device__ __forceinline__ uint32_t raise_gate(uint32_t gate, uint32_t n, uint32_t* sh_hist, uint32_t* sh_ckey,
                                                int32_t* sh_cpos, uint32_t* sh_scan, uint32_t* sh_var, int tid) {
   find_threshold(sh_hist, kBinsWide, n, sh_scan, sh_var, tid);
@@ -624,30 +669,29 @@ __device__ __forceinline__ uint32_t raise_gate(uint32_t gate, uint32_t n, uint32
   if (t <= gate) return gate;
   const uint32_t count = uniform(sh_var[kVarCandCount]);
   const uint32_t ncur = count < (uint32_t)kStreamCap ? count : (uint32_t)kStreamCap;
-  constexpr int R = (kStreamCap + kThreads - 1) / kThreads;
-  uint32_t ck[R];
-  int32_t cp[R];
-  uint32_t keep = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint32_t i = (uint32_t)(tid + r * kThreads);
-    ck[r] = i < ncur ? sh_ckey[i] : 0u;
-    cp[r] = i < ncur ? sh_cpos[i] : 0;
-    keep += (ck[r] >> 20) >= t ? 1u : 0u;
-  }
-  uint32_t total;
-  uint32_t off = block_exclusive_scan(keep, sh_scan, total, tid);   // barriers: all reads are done
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if ((ck[r] >> 20) >= t) {
-      sh_ckey[off] = ck[r];
-      sh_cpos[off] = cp[r];
+  uint32_t kept = 0;   // uniform: entries kept by earlier rounds
+  for (uint32_t r0 = 0; r0 < ncur; r0 += 2u * kThreads) {
+    const uint32_t i0 = r0 + (uint32_t)tid * 2u;
+    const uint32_t k0 = i0 < ncur ? sh_ckey[i0] : 0u, k1 = i0 + 1u < ncur ? sh_ckey[i0 + 1u] : 0u;
+    const int32_t p0 = i0 < ncur ? sh_cpos[i0] : 0, p1 = i0 + 1u < ncur ? sh_cpos[i0 + 1u] : 0;
+    const bool q0 = (k0 >> 20) >= t, q1 = (k1 >> 20) >= t;
+    uint32_t total;
+    uint32_t off = kept + block_exclusive_scan((q0 ? 1u : 0u) + (q1 ? 1u : 0u), sh_scan, total, tid);
+    if (q0) {
+      sh_ckey[off] = k0;
+      sh_cpos[off] = p0;
       ++off;
     }
+    if (q1) {
+      sh_ckey[off] = k1;
+      sh_cpos[off] = p1;
+    }
+    kept += total;
+    __syncthreads();
   }
   if (tid == 0) {
     if (count > (uint32_t)kStreamCap) sh_var[kVarOverflow] = 1u;   // keys were lost: redo the row
-    sh_var[kVarCandCount] = total;
+    sh_var[kVarCandCount] = kept;
   }
   __syncthreads();
   return t;
@@ -695,13 +739,18 @@ __device__ __forceinline__ void restream_pass(int mode, const float* rowp, uint3
   __syncthreads();
 }
 
+__device__ __forceinline__ int64_t row_len(const KernelArgs& a, int64_t row) {
+  const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+  return sl < 0 ? 0 : ((int64_t)sl > a.width ? a.width : (int64_t)sl);
+}
+
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 stream_rows_kernel(KernelArgs a) {
   __shared__ uint32_t sh_hist[kBinsWide];
   __shared__ uint32_t sh_ckey[kStreamCap];
   __shared__ int32_t sh_cpos[kStreamCap];
   __shared__ int32_t sh_raw[kMaxK];
-  __shared__ uint32_t sh_scan[kWaves + 1];
+  __shared__ uint32_t sh_scan[64];   // the 64 coarse bins of find_threshold
   __shared__ uint32_t sh_var[16];
 
   const int64_t W = a.width;
@@ -709,8 +758,7 @@ stream_rows_kernel(KernelArgs a) {
   const bool vec = a.vec != 0;
   for (int64_t row = blockIdx.x; row < a.batch; row += gridDim.x) {
     const int tid = opaque_tid();
-    const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
-    const int64_t L64 = sl < 0 ? 0 : ((int64_t)sl > W ? W : (int64_t)sl);
+    const int64_t L64 = row_len(a, row);
     const uint32_t L = (uint32_t)L64;
     const int n = L64 < (int64_t)k ? (int)L64 : k;
     if (L64 <= (int64_t)k) {
@@ -723,29 +771,32 @@ stream_rows_kernel(KernelArgs a) {
     const float* rowp = a.scores + row * W;
     __syncthreads();
 
-    // 1. sample: full histogram of the first kSampleSpan positions
+    // 1. sample: full histogram of the first kSampleSpan positions (the
+    // first streamed chunk's loads are issued before the sample is used)
     uint32_t sk[4 * kSampleVecs];
-    load_keys<kSampleVecs>(sk, rowp, 0u, L, vec, tid);
+    load_raw<kSampleVecs>(sk, rowp, 0u, L, vec, tid);
+    uint32_t ka[4 * kChunkVecs], kb[4 * kChunkVecs];
+    uint32_t c = kSampleSpan;
+    if (c < L) load_raw<kChunkVecs>(ka, rowp, c, L, vec, tid);
 #pragma unroll
-    for (int j = 0; j < 4 * kSampleVecs; ++j)
-      if (sk[j]) atomicAdd(&sh_hist[sk[j] >> 20], 1u);
+    for (int j = 0; j < 4 * kSampleVecs; ++j) {
+      const uint32_t x = slot_key(sk[j], j, 0u, L, tid);
+      if (x) atomicAdd(&sh_hist[x >> 20], 1u);
+    }
     __syncthreads();
     find_threshold(sh_hist, kBinsWide, (uint32_t)n, sh_scan, sh_var, tid);
     uint32_t gate = uniform(sh_var[0]) > 1u ? uniform(sh_var[0]) : 1u;
-    gated_append(sk, 0u, gate, true, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
+    gated_append(sk, 0u, L, gate, true, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
 
     // 2. stream the rest, two chunks in flight
-    uint32_t ka[4 * kChunkVecs], kb[4 * kChunkVecs];
-    uint32_t c = kSampleSpan;
-    if (c < L) load_keys<kChunkVecs>(ka, rowp, c, L, vec, tid);
     while (c < L) {
       const uint32_t cb = c + kChunkSpan;
-      if (cb < L) load_keys<kChunkVecs>(kb, rowp, cb, L, vec, tid);
-      gated_append(ka, c, gate, false, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
+      if (cb < L) load_raw<kChunkVecs>(kb, rowp, cb, L, vec, tid);
+      gated_append(ka, c, L, gate, false, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
       if (cb < L) {
         const uint32_t ca = cb + kChunkSpan;
-        if (ca < L) load_keys<kChunkVecs>(ka, rowp, ca, L, vec, tid);
-        gated_append(kb, cb, gate, false, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
+        if (ca < L) load_raw<kChunkVecs>(ka, rowp, ca, L, vec, tid);
+        gated_append(kb, cb, L, gate, false, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
       }
       c = cb + kChunkSpan;
       __syncthreads();
