@@ -128,6 +128,19 @@ topk_status_t topk_release_workspaces(void);
  */
 topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_per_row);
 
+/*
+ * Testing and tuning override of the streaming kernel's compiled shape,
+ * process-wide: -1 = automatic (the dispatcher picks by batch and k), else
+ *   0: 1024-thread workgroups, 16K-position sample, 8K-position chunks,
+ *      6144 LDS candidates, 2 workgroups per CU (few rows, k up to 2048,
+ *      rows with many tied keys);
+ *   1: 256-thread workgroups, 8K-position sample, 4K-position chunks,
+ *      1920 LDS candidates, 4 workgroups per CU (large batches, k <= 512).
+ * Either shape is exact for every input; the choice only moves time.
+ * Returns TOPK_ERROR_INVALID_VALUE for other values.
+ */
+topk_status_t topk_set_stream_shape(int32_t shape);
+
 /* Reads (and clears) the device-side fault word of `stream`'s workspace after
  * synchronising the stream: 0 when no cross-workgroup wait ever timed out. */
 topk_status_t topk_debug_fault_word(hipStream_t stream, uint32_t* word);

@@ -16,12 +16,13 @@ from typing import Optional, Tuple
 from .build import LIB_PATH
 
 TOPK_MAX_K = 2048
+STREAM_SHAPES = 2   # compiled streaming-kernel shapes: topk_set_stream_shape accepts -1 and 0..STREAM_SHAPES-1
 STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUPPORTED",
           3: "TOPK_ERROR_OUT_OF_MEMORY", 4: "TOPK_ERROR_LAUNCH"}
 
 EXPORTED = ("topk_transform", "topk_status_string", "topk_last_error", "topk_last_launch",
-            "topk_release_workspaces", "topk_set_dispatch_override", "topk_debug_fault_word",
-            "topk_abi_version")
+            "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape",
+            "topk_debug_fault_word", "topk_abi_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -57,6 +58,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topk_release_workspaces.restype = ctypes.c_int
     lib.topk_set_dispatch_override.argtypes = [c_i32, c_i32]
     lib.topk_set_dispatch_override.restype = ctypes.c_int
+    lib.topk_set_stream_shape.argtypes = [c_i32]
+    lib.topk_set_stream_shape.restype = ctypes.c_int
     lib.topk_debug_fault_word.argtypes = [c_vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.topk_debug_fault_word.restype = ctypes.c_int
     lib.topk_abi_version.argtypes = []
@@ -134,6 +137,10 @@ def topk_release_workspaces() -> None:
 
 def topk_set_dispatch_override(elems_per_thread: int = 0, wgs_per_row: int = 0) -> None:
     _check(load().topk_set_dispatch_override(int(elems_per_thread), int(wgs_per_row)))
+
+
+def topk_set_stream_shape(shape: int = -1) -> None:
+    _check(load().topk_set_stream_shape(int(shape)))
 
 
 def topk_debug_fault_word(stream=None) -> int:

@@ -32,7 +32,7 @@ struct DeviceInfo {
   int cus = 0;
   bool coop = false;
   int occ[2][topk::kNumEpt] = {};   // [split][ept] resident workgroups per CU
-  int stream_occ = 0;                // streaming kernel: resident workgroups per CU
+  int stream_occ[topk::kNumStreamVariants] = {};   // streaming kernel shapes: resident workgroups per CU
   std::string arch;
 };
 
@@ -46,6 +46,7 @@ std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 int g_override_ept = 0;
 int g_override_wgs = 0;
+int g_stream_variant = -1;   // -1: the default streaming shape
 
 topk_status_t fail(topk_status_t st, const std::string& msg) {
   t_last_error = msg;
@@ -80,8 +81,10 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
         e = topk::rows_occupancy(i, c == 1, &info.occ[c][i]);
         if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
       }
-    e = topk::stream_occupancy(&info.stream_occ);
-    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    for (int v = 0; v < topk::kNumStreamVariants; ++v) {
+      e = topk::stream_occupancy(v, &info.stream_occ[v]);
+      if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    }
   }
   *out = &g_devices.emplace(dev, info).first->second;
   return TOPK_SUCCESS;
@@ -136,8 +139,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 enum class Kind { kResident, kSplit, kStream };
 
+// Compiled streaming shapes (TOPK_STREAM_VARIANTS): 0 = 1024-thread
+// workgroups with 6144 LDS candidates, 1 = 256-thread workgroups with 1920.
+constexpr int kStreamWide = 0;
+constexpr int kStreamNarrow = 1;
+
 struct Plan {
   Kind kind = Kind::kStream;
+  int stream_variant = kStreamWide;
   int ept_idx = 0;
   int64_t G = 1;
   int64_t slots = 1;
@@ -152,20 +161,29 @@ const char* kind_name(Kind k) {
   return "?";
 }
 
-// Kernel shape for (batch, width) on this device.
-//  * stream:   one workgroup per row, rows streamed from HBM with a sampled
-//              gate, two rows in flight per CU; persistent over rows.  Used
-//              when the batch alone fills the GPU, or rows are short.
+// Kernel shape for (batch, width, k) on this device.
+//  * stream:   one workgroup per row, rows streamed from HBM past a gate set
+//              from a sample; persistent over rows (a queue hands out the rows
+//              beyond the grid).  Used from half a row per CU up (measured on
+//              MI355X: at 128 rows of 128K it beats the split kernel by a
+//              quarter), or when rows are short.  The 256-thread shape (four
+//              workgroups per CU) when the batch fills its slots and k <= 512
+//              (its 1920-entry list holds the ~2k keys such rows pass), else
+//              the 1024-thread shape.
 //  * split:    G workgroups per row holding the row in registers, merged
-//              through global atomics and a per-row barrier; for low-batch
-//              long rows.  Picks the most workgroups per row whose grid still
-//              fits resident.
+//              through global atomics and a per-row barrier; for fewer, long
+//              rows.  Picks the smallest E whose grid still fits resident.
 //  * resident: one workgroup per row holding the row in registers (testing
 //              and tuning override only).
-topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, Plan* plan) {
+topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, int32_t k, Plan* plan) {
   const int64_t B = batch;
   const int64_t Wc = width > 0 ? width : 1;
-  const int64_t stream_slots = (int64_t)dev.stream_occ * dev.cus;
+  if (g_stream_variant >= 0)
+    plan->stream_variant = g_stream_variant;
+  else
+    plan->stream_variant =
+        (k <= 512 && B >= (int64_t)dev.stream_occ[kStreamNarrow] * dev.cus) ? kStreamNarrow : kStreamWide;
+  const int64_t stream_slots = (int64_t)dev.stream_occ[plan->stream_variant] * dev.cus;
   auto split_ept_for = [&](int64_t wgs) {   // smallest E whose G for this width is <= wgs
     int idx = 0;
     while (idx < topk::kNumEpt - 1 && (int64_t)topk::kThreads * topk::kEptValues[idx] * wgs < Wc) ++idx;
@@ -184,7 +202,7 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, P
       plan->G = G;
       plan->kind = G > 1 ? Kind::kSplit : Kind::kResident;
     }
-  } else if (B >= stream_slots || Wc <= 16384) {
+  } else if (2 * B >= dev.cus || B >= stream_slots || Wc <= 16384) {
     plan->kind = Kind::kStream;
   } else {
     int chosen = -1;
@@ -260,7 +278,7 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
   if (!info->supported) return fail(TOPK_ERROR_UNSUPPORTED, "device " + info->arch + " is not gfx950");
 
   Plan plan;
-  st = plan_launch(*info, batch, width, &plan);
+  st = plan_launch(*info, batch, width, k, &plan);
   if (st != TOPK_SUCCESS) return st;
 
   topk::KernelArgs a;
@@ -281,21 +299,24 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
   a.wgs_per_row = (int32_t)plan.G;
   a.slots = (int32_t)plan.slots;
   a.vec = (width % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
-  if (plan.kind == Kind::kSplit) {
+  if (plan.kind == Kind::kSplit || (plan.kind == Kind::kStream && batch > plan.slots)) {
+    // split rows synchronise through per-slot regions; streamed rows beyond
+    // the grid are handed out through a counter in the header
     int64_t capacity = 0;
-    st = get_workspace(dev, stream, plan.slots, &a.ws, &capacity);
+    st = get_workspace(dev, stream, plan.kind == Kind::kSplit ? plan.slots : 0, &a.ws, &capacity);
     if (st != TOPK_SUCCESS) return st;
     a.ws_slots = (int32_t)capacity;
   }
   if (plan.kind == Kind::kStream)
-    e = topk::launch_stream_rows(a, stream);
+    e = topk::launch_stream_rows(plan.stream_variant, a, stream);
   else
     e = topk::launch_rows(plan.ept_idx, plan.kind == Kind::kSplit, a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   char buf[160];
   std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d",
                 kind_name(plan.kind), plan.kind == Kind::kStream ? 0 : topk::kEptValues[plan.ept_idx],
-                (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G), topk::kThreads, a.vec);
+                (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G),
+                plan.kind == Kind::kStream ? topk::stream_variant_threads(plan.stream_variant) : topk::kThreads, a.vec);
   t_last_launch = buf;
   return TOPK_SUCCESS;
 }
@@ -333,6 +354,14 @@ topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_p
   std::lock_guard<std::mutex> lock(g_mu);
   g_override_ept = elems_per_thread;
   g_override_wgs = wgs_per_row;
+  return TOPK_SUCCESS;
+}
+
+topk_status_t topk_set_stream_shape(int32_t shape) {
+  if (shape < -1 || shape >= topk::kNumStreamVariants)
+    return fail(TOPK_ERROR_INVALID_VALUE, "shape must be -1 (default) or a compiled streaming shape index");
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_stream_variant = shape;
   return TOPK_SUCCESS;
 }
 

@@ -26,6 +26,8 @@ constexpr int kEptValues[kNumEpt] = {4, 8, 16, 32, 64};
 // Every region is left zeroed by the workgroup that finishes its row.
 // ---------------------------------------------------------------------------
 constexpr size_t kHdrWords = 64;        // [0] = fault word (a bounded wait timed out)
+constexpr size_t kHdrRowTicket = 32;    // streaming kernel: rows handed out beyond the first grid's
+constexpr size_t kHdrRowExit = 48;      // streaming kernel: workgroups out of rows
 constexpr size_t kBarWords = 32;        // per slot: [0] arrivals, [1] generation (own 128 B line)
 constexpr size_t kRegHist0 = 0;
 constexpr size_t kRegHist1 = kRegHist0 + kBinsWide;
@@ -49,7 +51,7 @@ struct KernelArgs {
   const int32_t* page_table;  // (batch, pages_per_row)
   int32_t* out;               // (batch, k)
   int32_t* out_raw;           // (batch, k) or nullptr
-  uint32_t* ws;               // workspace (wgs_per_row > 1 only)
+  uint32_t* ws;               // workspace: split rows; streaming rows with batch > grid (row queue)
   int64_t width;
   int64_t pages_per_row;
   int32_t batch;
@@ -66,8 +68,12 @@ struct KernelArgs {
 hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStream_t stream);
 hipError_t rows_occupancy(int ept_index, bool coop, int* blocks_per_cu);
 
-// Streaming kernel, one workgroup per row, persistent over rows (grid = slots).
-hipError_t launch_stream_rows(const KernelArgs& args, hipStream_t stream);
-hipError_t stream_occupancy(int* blocks_per_cu);
+// Streaming kernel, one workgroup per row, persistent over rows (grid =
+// slots).  `variant` selects one of kNumStreamVariants compiled shapes
+// (threads per workgroup, sample and chunk sizes, LDS candidate capacity).
+constexpr int kNumStreamVariants = 2;
+hipError_t launch_stream_rows(int variant, const KernelArgs& args, hipStream_t stream);
+hipError_t stream_occupancy(int variant, int* blocks_per_cu);
+int stream_variant_threads(int variant);
 
 }  // namespace topk

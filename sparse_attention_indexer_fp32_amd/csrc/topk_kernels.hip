@@ -111,51 +111,59 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int tid) {
   return v;
 }
 
-// Exclusive scan over the workgroup in thread order; `total` gets the sum.
-// sh_scan needs kWaves + 1 words.  Contains barriers: call uniformly.
+// Exclusive scan over an NT-thread workgroup in thread order; `total` gets
+// the sum.  sh_scan needs NT/64 + 1 words.  Contains barriers: call uniformly.
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh_scan, uint32_t& total,
                                                         int tid) {
+  constexpr int kW = NT / 64;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const uint32_t inc = wave_inclusive_scan(v, tid);
   if (lane == 63) sh_scan[wid] = inc;
   __syncthreads();
   if (wid == 0) {
-    const uint32_t w = lane < kWaves ? sh_scan[lane] : 0u;
+    const uint32_t w = lane < kW ? sh_scan[lane] : 0u;
     const uint32_t wi = wave_inclusive_scan(w, tid);
-    if (lane < kWaves) sh_scan[lane] = wi - w;
-    if (lane == kWaves - 1) sh_scan[kWaves] = wi;
+    if (lane < kW) sh_scan[lane] = wi - w;
+    if (lane == kW - 1) sh_scan[kW] = wi;
   }
   __syncthreads();
   const uint32_t r = sh_scan[wid] + inc - v;
-  total = sh_scan[kWaves];
+  total = sh_scan[kW];
   __syncthreads();
   return r;
 }
 
-// Threshold bin of histogram h[0, nb), nb = 4096 or 1024: the highest bin t
+// Threshold bin of histogram h[0, NB), NB = 4096 or 1024: the highest bin t
 // with sum_{b >= t} h[b] >= need.  Writes sh_var[0] = t, sh_var[1] = count in
 // bins above t, sh_var[2] = h[t].  (If the histogram holds fewer than `need`
 // elements -- impossible for valid input -- it reports bin 0 with counts 0.)
 //
-// Two levels, one barrier in between: every group of 64 bins is summed by a
-// DPP reduction (16 lanes x 4 bins, or a full wave x 1 bin) into sh_coarse;
-// then wave 0 scans the group totals from the top to find the crossing group,
-// and scans that group's 64 bins to find the crossing bin (ballot + first set
-// lane locate both crossings).
-__device__ __forceinline__ void find_threshold(const uint32_t* h, int nb, uint32_t need, uint32_t* sh_coarse,
+// Two levels, one barrier in between: every group of 64 bins is summed (each
+// of the NT threads sums NB/NT bins, then a DPP row scan or a lane butterfly
+// adds up the threads of a group) into sh_coarse; then wave 0 scans the group
+// totals from the top to find the crossing group, and scans that group's 64
+// bins to find the crossing bin (ballot + first set lane locate both).
+template <int NT, int NB>
+__device__ __forceinline__ void find_threshold(const uint32_t* h, uint32_t need, uint32_t* sh_coarse,
                                                uint32_t* sh_var, int tid) {
+  constexpr int kPer = NB / NT;           // bins per thread
+  constexpr int kTpg = 64 / kPer;         // threads per 64-bin group
+  constexpr int ngroups = NB / 64;
   const int lane = tid & 63;
-  const int ngroups = nb >> 6;
-  if (nb == kBinsWide) {
-    const int b0 = tid * 4;
-    const uint32_t s = h[b0] + h[b0 + 1] + h[b0 + 2] + h[b0 + 3];
-    const uint32_t r = row16_inclusive_scan(s);
-    if ((lane & 15) == 15) sh_coarse[tid >> 4] = r;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) sum += h[tid * kPer + i];
+  if (kTpg == 16) {
+    sum = row16_inclusive_scan(sum);
+  } else if (kTpg == 64) {
+    sum = wave_inclusive_scan(sum, tid);
   } else {
-    const uint32_t r = wave_inclusive_scan(h[tid], tid);
-    if (lane == 63) sh_coarse[tid >> 6] = r;
+#pragma unroll
+    for (int d = 1; d < kTpg; d <<= 1) sum += __shfl_xor(sum, d, 64);
   }
+  if ((tid % kTpg) == (kTpg == 16 || kTpg == 64 ? kTpg - 1 : 0)) sh_coarse[tid / kTpg] = sum;
   __syncthreads();
   if (tid < 64) {
     const uint32_t v = lane < ngroups ? sh_coarse[ngroups - 1 - lane] : 0u;   // lane 0 = highest group
@@ -225,6 +233,7 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, int G, uint32_t* faul
 // Gather + transform pass: slot j < n holds raw position r (trivial rows: r = j);
 // out = page_table[row, r >> log2_page] << log2_page | (r & (page_size - 1)).
 // Slots past n, and any r outside [0, L), give -1.
+template <int NT>
 __device__ __forceinline__ void write_row_output(const KernelArgs& a, int64_t row, int64_t L, int n, bool trivial,
                                                  const int32_t* sh_raw, int tid) {
   const int k = a.k;
@@ -233,7 +242,7 @@ __device__ __forceinline__ void write_row_output(const KernelArgs& a, int64_t ro
   int32_t* o = a.out + row * (int64_t)k;
   int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
   const int32_t* pt = a.page_table + row * a.pages_per_row;
-  for (int j = tid; j < k; j += kThreads) {
+  for (int j = tid; j < k; j += NT) {
     int32_t r = -1;
     if (j < n) r = trivial ? j : sh_raw[j];
     int32_t v = -1;
@@ -274,7 +283,7 @@ __device__ __forceinline__ void hist_pass0(const uint32_t (&key)[E], uint32_t ne
     if (key[j]) atomicAdd(&h[key[j] >> 20], 1u);
   if (S == E) return;
   __syncthreads();
-  find_threshold(h, kBinsWide, need, sh_scan, sh_var, tid);
+  find_threshold<kThreads, kBinsWide>(h, need, sh_scan, sh_var, tid);
   // Bin >= 1 also excludes key 0 (no element).
   const uint32_t gate = uniform(sh_var[0]) > 1u ? uniform(sh_var[0]) : 1u;
 #pragma unroll
@@ -308,20 +317,21 @@ __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass
 // 10-bit digits, then writes the strictly-greater keys to slots
 // [gt_base, n - need_final) and `need_final` keys of the final bin to
 // [n - need_final, n).
+template <int NT>
 __device__ __forceinline__ void select_candidates(int ncand, uint32_t prefix, int shift, uint32_t cnt,
                                                   uint32_t need, uint32_t gt_base, uint32_t n,
                                                   uint32_t* sh_hist, const uint32_t* sh_ckey,
                                                   const int32_t* sh_cpos, int32_t* sh_raw, uint32_t* sh_scan,
                                                   uint32_t* sh_var, int tid) {
   while (shift > 0 && cnt != need) {
-    for (int b = tid; b < kBinsNarrow; b += kThreads) sh_hist[b] = 0;
+    for (int b = tid; b < kBinsNarrow; b += NT) sh_hist[b] = 0;
     __syncthreads();
-    for (int i = tid; i < ncand; i += kThreads) {
+    for (int i = tid; i < ncand; i += NT) {
       const uint32_t x = sh_ckey[i];
       if ((x >> shift) == prefix) atomicAdd(&sh_hist[(x >> (shift - 10)) & 1023u], 1u);
     }
     __syncthreads();
-    find_threshold(sh_hist, kBinsNarrow, need, sh_scan, sh_var, tid);
+    find_threshold<NT, kBinsNarrow>(sh_hist, need, sh_scan, sh_var, tid);
     const uint32_t bin = uniform(sh_var[0]), gt = uniform(sh_var[1]);
     cnt = uniform(sh_var[2]);
     need -= gt;
@@ -335,7 +345,7 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t prefix, in
     sh_var[9] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < ncand; i += kThreads) {
+  for (int i = tid; i < ncand; i += NT) {
     const uint32_t x = sh_ckey[i] >> shift;
     if (x > prefix) {
       const uint32_t s = atomicAdd(&sh_var[8], 1u);
@@ -349,17 +359,17 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t prefix, in
 }
 
 // Raw loads of V float4 groups of a row chunk: group v of thread tid holds
-// positions cbase + 4*tid + 4096*v + {0..3}.  One dwordx4 buffer load per group
+// positions cbase + 4*tid + 4*NT*v + {0..3}.  One dwordx4 buffer load per group
 // when the row is 16-byte aligned, else four dword loads.  The descriptor
 // spans only the valid part of the chunk (whole 16-byte groups when aligned:
 // the width is then a multiple of 4, so they stay inside the row), so the
 // hardware returns 0 past seq_len and past the tensor without a branch.
 // Nothing here consumes the data, so the loads stay in flight until the
 // caller's first use (chunks are double-buffered this way).
-template <int V>
+template <int NT, int V>
 __device__ __forceinline__ void load_raw(uint32_t (&raw)[4 * V], const float* rowp, uint32_t cbase, uint32_t L,
                                          bool vec, int tid) {
-  constexpr uint32_t span = (uint32_t)kThreads * 4u * V;
+  constexpr uint32_t span = (uint32_t)NT * 4u * V;
   const uint32_t rem = L > cbase ? L - cbase : 0u;
   const uint32_t nvalid = rem < span ? rem : span;
   const uint32_t nbytes = vec ? ((nvalid + 3u) & ~3u) * 4u : nvalid * 4u;
@@ -369,7 +379,7 @@ __device__ __forceinline__ void load_raw(uint32_t (&raw)[4 * V], const float* ro
   if (vec) {
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, v * (kThreads * 16), 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, v * (NT * 16), 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) raw[4 * v + i] = x[i];
     }
@@ -378,22 +388,23 @@ __device__ __forceinline__ void load_raw(uint32_t (&raw)[4 * V], const float* ro
     for (int v = 0; v < V; ++v)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        raw[4 * v + i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, v * (kThreads * 16) + 4 * i, 0);
+        raw[4 * v + i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, v * (NT * 16) + 4 * i, 0);
   }
 }
 
 // Order key of raw slot j of a chunk at cbase, or 0 ("no element") past L.
+template <int NT>
 __device__ __forceinline__ uint32_t slot_key(uint32_t raw, int j, uint32_t cbase, uint32_t L, int tid) {
-  const int64_t lim = (int64_t)L - (int64_t)cbase - (int64_t)((j >> 2) * kThreads * 4 + (j & 3));   // a scalar
+  const int64_t lim = (int64_t)L - (int64_t)cbase - (int64_t)((j >> 2) * NT * 4 + (j & 3));   // a scalar
   return ((int64_t)(tid * 4) < lim) ? order_key_bits(raw) : 0u;
 }
 
-template <int V>
+template <int NT, int V>
 __device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* rowp, uint32_t cbase, uint32_t L,
                                           bool vec, int tid) {
-  load_raw<V>(key, rowp, cbase, L, vec, tid);
+  load_raw<NT, V>(key, rowp, cbase, L, vec, tid);
 #pragma unroll
-  for (int j = 0; j < 4 * V; ++j) key[j] = slot_key(key[j], j, cbase, L, tid);
+  for (int j = 0; j < 4 * V; ++j) key[j] = slot_key<NT>(key[j], j, cbase, L, tid);
 }
 
 template <int E, bool COOP>
@@ -423,7 +434,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     const int64_t L = sl < 0 ? 0 : ((int64_t)sl > W ? W : (int64_t)sl);
     const int n = L < (int64_t)k ? (int)L : k;
     if (L <= (int64_t)k) {  // every valid position is selected (uniform over the row's workgroups)
-      if (g == 0) write_row_output(a, row, L, n, true, sh_raw, tid);
+      if (g == 0) write_row_output<kThreads>(a, row, L, n, true, sh_raw, tid);
       continue;
     }
     constexpr bool split = COOP;   // the host launches the split kernel only with G > 1
@@ -443,7 +454,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     const uint32_t c0 = (uint32_t)g * (uint32_t)C;
     const uint32_t pbase = c0 + (uint32_t)tid * 4u;
     uint32_t key[E];
-    load_keys<E / 4>(key, rowp, c0, (uint32_t)L, a.vec != 0, tid);
+    load_keys<kThreads, E / 4>(key, rowp, c0, (uint32_t)L, a.vec != 0, tid);
     auto pos_of = [&](int j) -> int32_t {
       return (int32_t)(pbase + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3));
     };
@@ -469,7 +480,8 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
         for (int b = tid; b < nb; b += kThreads) sh_hist[b] = g_load(gh + b);
         __syncthreads();
       }
-      find_threshold(sh_hist, nb, need, sh_scan, sh_var, tid);
+      if (pass == 0) find_threshold<kThreads, kBinsWide>(sh_hist, need, sh_scan, sh_var, tid);
+      else find_threshold<kThreads, kBinsNarrow>(sh_hist, need, sh_scan, sh_var, tid);
       const uint32_t bin = uniform(sh_var[0]), gt = uniform(sh_var[1]);
       cnt = uniform(sh_var[2]);
       need -= gt;
@@ -502,7 +514,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
       ce += (xp == prefix && x != 0u) ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t off = block_exclusive_scan((cg << 17) | ce, sh_scan, tot, tid);
+    const uint32_t off = block_exclusive_scan<kThreads>((cg << 17) | ce, sh_scan, tot, tid);
     uint32_t off_g = off >> 17, off_e = off & 0x1FFFFu;
     if (split) {
       if (tid == 0) {
@@ -546,7 +558,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 
     if (!split) {
       __syncthreads();
-      write_row_output(a, row, L, n, false, sh_raw, tid);
+      write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid);
       continue;
     }
 
@@ -570,11 +582,11 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
         sh_cpos[i] = (int32_t)g_load(region + kRegCandPos + i);
       }
       __syncthreads();
-      select_candidates(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
+      select_candidates<kThreads>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
                         sh_scan, sh_var, tid);
     }
     __syncthreads();
-    write_row_output(a, row, L, n, false, sh_raw, tid);
+    write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid);
     // leave the region zeroed for the row this slot handles two iterations on
     for (int b = tid; b < kBinsWide; b += kThreads) g_store(region + kRegHist0 + b, 0u);
     for (int b = tid; b < kBinsNarrow; b += kThreads) {
@@ -606,13 +618,6 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 // one more digit per pass until the threshold bin fits (exact, slower).
 // ---------------------------------------------------------------------------
 
-constexpr int kStreamCap = 6144;                    // LDS candidates per row
-constexpr int kStreamRefresh = kStreamCap / 2;      // raise the gate past this many
-constexpr int kSampleVecs = 4;                      // sample: 16 keys per thread = 16K positions
-constexpr int kChunkVecs = 2;                       // streamed chunk: 8 keys per thread = 8K positions
-constexpr uint32_t kSampleSpan = (uint32_t)kThreads * 4u * kSampleVecs;
-constexpr uint32_t kChunkSpan = (uint32_t)kThreads * 4u * kChunkVecs;
-
 // Stream-kernel LDS words (sh_var indices).
 enum : int { kVarCandCount = 10, kVarOverflow = 11, kVarGt = 12, kVarEq = 13 };
 
@@ -620,20 +625,33 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Appends the keys whose 12-bit bin is >= gate (key 0 never passes: gate >= 1)
-// to the candidate list, and adds them to the histogram unless already counted.
-template <int N>
+// How gated_append tests a raw score against the gate key.
+enum : int {
+  kGatePositive = 0,   // every slot valid, gate >= key(+0): raw bits compare as signed ints
+  kGateAny = 1,        // every slot valid
+  kGateChecked = 2,    // slots past L are absent
+};
+
+// Appends the keys >= gate (gate >= 1, so key 0 never passes) of one chunk
+// of raw scores to the candidate list: slots come from one LDS atomic per
+// wave, each passing lane's slot from its rank in the wave's ballot.  Slots
+// past CAP land in the trash entry CAP (the count still grows: overflow).
+// With kGatePositive the test is one signed compare: a float at or above a
+// non-negative gate has a non-negative bit pattern, ordered like its key, and
+// every negative float (sign bit set) is a negative int.
+template <int NT, int CAP, int N, int FORM>
 __device__ __forceinline__ void gated_append(const uint32_t (&raw)[N], uint32_t cbase, uint32_t L, uint32_t gate,
-                                             bool counted, uint32_t* sh_hist, uint32_t* sh_ckey,
-                                             int32_t* sh_cpos, uint32_t* sh_var, int tid) {
-  uint32_t key[N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) key[j] = slot_key(raw[j], j, cbase, L, tid);
+                                             uint32_t* sh_ckey, int32_t* sh_cpos, uint32_t* sh_var, int tid) {
+  const int32_t graw = (int32_t)(gate ^ 0x80000000u);
   uint64_t m[N];
   uint32_t tot = 0;
 #pragma unroll
   for (int j = 0; j < N; ++j) {
-    m[j] = __ballot((key[j] >> 20) >= gate);
+    bool pass;
+    if (FORM == kGatePositive) pass = (int32_t)raw[j] >= graw;
+    else if (FORM == kGateAny) pass = order_key_bits(raw[j]) >= gate;
+    else pass = slot_key<NT>(raw[j], j, cbase, L, tid) >= gate;
+    m[j] = __ballot(pass);
     tot += (uint32_t)__popcll(m[j]);
   }
   if (tot == 0u) return;
@@ -641,42 +659,53 @@ __device__ __forceinline__ void gated_append(const uint32_t (&raw)[N], uint32_t 
   if ((tid & 63) == 0) base = atomicAdd(&sh_var[kVarCandCount], tot);
   base = __builtin_amdgcn_readfirstlane(base);
   const uint32_t p0 = cbase + (uint32_t)tid * 4u;
+  const int lane = tid & 63;
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     if (m[j] == 0ull) continue;
-    if ((key[j] >> 20) >= gate) {
-      if (!counted) atomicAdd(&sh_hist[key[j] >> 20], 1u);
-      const uint32_t slot = base + lanes_below(m[j]);
-      if (slot < (uint32_t)kStreamCap) {
-        sh_ckey[slot] = key[j];
-        sh_cpos[slot] = (int32_t)(p0 + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3));
-      }
+    if ((m[j] >> lane) & 1ull) {
+      uint32_t slot = base + lanes_below(m[j]);
+      slot = slot < (uint32_t)CAP ? slot : (uint32_t)CAP;
+      sh_ckey[slot] = order_key_bits(raw[j]);
+      sh_cpos[slot] = (int32_t)(p0 + (uint32_t)(j >> 2) * (NT * 4) + (uint32_t)(j & 3));
     }
     base += (uint32_t)__popcll(m[j]);
   }
 }
 
-// Raises the gate to the threshold bin of the keys counted so far (exact for
-// every bin >= gate) and drops the candidates below it.  Uniform; returns the
-// new gate.  The list is compacted in place in rounds of 2 * kThreads
-// entries: a round's entries are read into registers before any is written,
-// and kept entries only move down (to positions below the round's end), so
-// no unread entry is overwritten.
+// 12-bit-bin histogram of the first `ncand` candidates' keys (cleared first).
+template <int NT>
+__device__ __forceinline__ void list_histogram(uint32_t ncand, const uint32_t* sh_ckey, uint32_t* sh_hist, int tid) {
+  for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0u;
+  __syncthreads();
+  for (uint32_t i = (uint32_t)tid; i < ncand; i += NT) atomicAdd(&sh_hist[sh_ckey[i] >> 20], 1u);
+  __syncthreads();
+}
+
+// Raises the gate to the lowest key of the threshold bin of the listed keys
+// (every key >= gate seen so far, unless the list has overflowed; a subset
+// still gives a bin that at least n keys of the row reach) and drops the
+// candidates below it.  Uniform; returns the new gate.  The list is compacted in place in rounds of 2 * NT entries: a
+// round's entries are read into registers before any is written, and kept
+// entries only move down (to positions below the round's end), so no unread
+// entry is overwritten.
+template <int NT, int CAP>
 __device__ __forceinline__ uint32_t raise_gate(uint32_t gate, uint32_t n, uint32_t* sh_hist, uint32_t* sh_ckey,
                                                int32_t* sh_cpos, uint32_t* sh_scan, uint32_t* sh_var, int tid) {
-  find_threshold(sh_hist, kBinsWide, n, sh_scan, sh_var, tid);
-  const uint32_t t = uniform(sh_var[0]);
-  if (t <= gate) return gate;
   const uint32_t count = uniform(sh_var[kVarCandCount]);
-  const uint32_t ncur = count < (uint32_t)kStreamCap ? count : (uint32_t)kStreamCap;
+  const uint32_t ncur = count < (uint32_t)CAP ? count : (uint32_t)CAP;
+  list_histogram<NT>(ncur, sh_ckey, sh_hist, tid);
+  find_threshold<NT, kBinsWide>(sh_hist, n, sh_scan, sh_var, tid);
+  const uint32_t t = uniform(sh_var[0]);
+  if (t <= (gate >> 20)) return gate;
   uint32_t kept = 0;   // uniform: entries kept by earlier rounds
-  for (uint32_t r0 = 0; r0 < ncur; r0 += 2u * kThreads) {
+  for (uint32_t r0 = 0; r0 < ncur; r0 += 2u * NT) {
     const uint32_t i0 = r0 + (uint32_t)tid * 2u;
     const uint32_t k0 = i0 < ncur ? sh_ckey[i0] : 0u, k1 = i0 + 1u < ncur ? sh_ckey[i0 + 1u] : 0u;
     const int32_t p0 = i0 < ncur ? sh_cpos[i0] : 0, p1 = i0 + 1u < ncur ? sh_cpos[i0 + 1u] : 0;
     const bool q0 = (k0 >> 20) >= t, q1 = (k1 >> 20) >= t;
     uint32_t total;
-    uint32_t off = kept + block_exclusive_scan((q0 ? 1u : 0u) + (q1 ? 1u : 0u), sh_scan, total, tid);
+    uint32_t off = kept + block_exclusive_scan<NT>((q0 ? 1u : 0u) + (q1 ? 1u : 0u), sh_scan, total, tid);
     if (q0) {
       sh_ckey[off] = k0;
       sh_cpos[off] = p0;
@@ -690,34 +719,44 @@ __device__ __forceinline__ uint32_t raise_gate(uint32_t gate, uint32_t n, uint32
     __syncthreads();
   }
   if (tid == 0) {
-    if (count > (uint32_t)kStreamCap) sh_var[kVarOverflow] = 1u;   // keys were lost: redo the row
+    if (count > (uint32_t)CAP) sh_var[kVarOverflow] = 1u;   // keys were lost: redo the row
     sh_var[kVarCandCount] = kept;
   }
   __syncthreads();
-  return t;
+  return t << 20;
 }
 
-// One pass over the row from memory, for the overflow path: with
-// mode 0, histograms the next 10-bit digit of the keys whose key >> shift
-// equals prefix; with mode 1, writes keys above the bin to slots [0, n - need)
-// and collects the bin's keys as candidates; with mode 2 (final digit, or the
-// whole bin is selected), writes keys above the bin to [0, n - need) and
-// `need` keys of the bin to [n - need, n).
-__device__ __forceinline__ void restream_pass(int mode, const float* rowp, uint32_t L, bool vec, uint32_t prefix,
-                                              int shift, uint32_t need, uint32_t n, uint32_t* sh_hist,
+// One pass over the row from memory, for the overflow path.  Keys below
+// `floor` (>= 1) are treated as absent: when at least n keys lie at or above
+// the streaming gate, the gate is the floor and every count stays consistent
+// with the histogram, which holds only keys >= gate in the gate's own bin.
+// With mode 3, histograms every key's 12-bit bin; with mode 0, histograms the
+// next 10-bit digit of the keys whose key >> shift equals prefix; with mode 1,
+// writes keys above the bin to slots [0, n - need) and collects the bin's keys
+// as candidates; with mode 2 (final digit, or the whole bin is selected),
+// writes keys above the bin to [0, n - need) and `need` keys of the bin to
+// [n - need, n).
+template <int NT, int CAP, int CV>
+__device__ __forceinline__ void restream_pass(int mode, const float* rowp, uint32_t L, bool vec, uint32_t floor,
+                                              uint32_t prefix, int shift, uint32_t need, uint32_t n, uint32_t* sh_hist,
                                               uint32_t* sh_ckey, int32_t* sh_cpos, int32_t* sh_raw,
                                               uint32_t* sh_var, int tid) {
+  constexpr uint32_t span = (uint32_t)NT * 4u * CV;
   const uint32_t gt_end = n - need;
-  for (uint32_t c = 0; c < L; c += kChunkSpan) {
-    uint32_t key[4 * kChunkVecs];
-    load_keys<kChunkVecs>(key, rowp, c, L, vec, tid);
+  for (uint32_t c = 0; c < L; c += span) {
+    uint32_t key[4 * CV];
+    load_keys<NT, CV>(key, rowp, c, L, vec, tid);
     const uint32_t p0 = c + (uint32_t)tid * 4u;
 #pragma unroll
-    for (int j = 0; j < 4 * kChunkVecs; ++j) {
+    for (int j = 0; j < 4 * CV; ++j) {
       const uint32_t x = key[j];
-      if (x == 0u) continue;
+      if (x < floor) continue;
+      if (mode == 3) {
+        atomicAdd(&sh_hist[x >> 20], 1u);
+        continue;
+      }
       const uint32_t xp = x >> shift;
-      const int32_t pos = (int32_t)(p0 + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3));
+      const int32_t pos = (int32_t)(p0 + (uint32_t)(j >> 2) * (NT * 4) + (uint32_t)(j & 3));
       if (mode == 0) {
         if (xp == prefix) atomicAdd(&sh_hist[(x >> (shift - 10)) & 1023u], 1u);
       } else if (xp > prefix) {
@@ -726,7 +765,7 @@ __device__ __forceinline__ void restream_pass(int mode, const float* rowp, uint3
       } else if (xp == prefix) {
         const uint32_t e = atomicAdd(&sh_var[kVarEq], 1u);
         if (mode == 1) {
-          if (e < (uint32_t)kStreamCap) {
+          if (e < (uint32_t)CAP) {
             sh_ckey[e] = x;
             sh_cpos[e] = pos;
           }
@@ -739,89 +778,206 @@ __device__ __forceinline__ void restream_pass(int mode, const float* rowp, uint3
   __syncthreads();
 }
 
+// Wave priority for a queued row: the rank of its ticket within its round of
+// `grid` tickets, in quarters (0 = among the first to finish a row).
+__device__ __forceinline__ void set_row_priority(uint32_t row, uint32_t grid) {
+  const uint32_t q = ((row % grid) * 4u) / grid;
+  if (q == 0u) __builtin_amdgcn_s_setprio(0);
+  else if (q == 1u) __builtin_amdgcn_s_setprio(1);
+  else if (q == 2u) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(3);
+}
+
+// Sample rank the streaming gate is set at.  The first S of a row's L
+// positions hold on average mu = n*S/L of the row's n largest keys (a
+// hypergeometric count); the gate sits at the m-th largest sampled key with
+// m = mu + 7 sqrt(mu) + 6 (at most n).  When the row's large keys are spread
+// along it, fewer than n of its keys lie at or above the gate with
+// probability below 1e-11 for every row shape up to 1M positions and k 2048;
+// such a row is detected at the end and finished exactly from memory (one
+// workgroup re-reads it, so a rare one still costs the whole launch tens of
+// microseconds).  m = n, a gate that holds for any row, when the sample is
+// the row.
+__device__ __forceinline__ uint32_t gate_rank(uint32_t n, uint32_t S, uint32_t L) {
+  const float mu = (float)n * (float)S / (float)L;
+  const float m = mu + 7.0f * sqrtf(mu) + 6.0f;
+  return m < (float)n ? (uint32_t)m : n;
+}
+
 __device__ __forceinline__ int64_t row_len(const KernelArgs& a, int64_t row) {
   const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
   return sl < 0 ? 0 : ((int64_t)sl > a.width ? a.width : (int64_t)sl);
 }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+// ---------------------------------------------------------------------------
+// Streaming one-workgroup-per-row kernel (large batches).
+//
+// Holding a 64K row in registers leaves one row per CU and nothing to overlap
+// its radix passes with; streaming keeps several rows in flight per CU.
+//   1. Sample: the first NT*4*SV positions are histogrammed in full; the
+//      sample's threshold bin is a gate such that at least n keys of the row
+//      lie at or above it.
+//   2. Stream: every key at or above the gate is counted (so the histogram is
+//      exact for every bin >= gate) and appended to an LDS candidate list;
+//      slots come from wave ballots, one LDS atomic per wave per chunk.  When
+//      the list fills, the gate is raised to the threshold bin of the keys
+//      seen so far (still a valid lower bound) and the list is compacted.
+//   3. The threshold bin comes from the exact histogram; the remaining digits
+//      run on the candidates only.
+// If the list overflows anyway (adversarial rows: a single bin holding more
+// keys than the list), the row is redone by re-streaming it from memory with
+// one more digit per pass until the threshold bin fits (exact, slower).
+//
+// Rows beyond the first grid come from a queue (a ticket counter in the
+// workspace header) rather than a fixed stride: workgroups that share a CU
+// are not served memory equally (older waves win), so a fixed two rows each
+// leaves the youngest finishing tens of microseconds after the oldest.  The
+// ticket is taken once a row's streaming ends; the last workgroup to run out
+// of rows puts the counters back to zero for the next launch.  A ticket's
+// rank within its round of `grid` tickets says how many workgroups finished a
+// row before this one; the later it came, the higher the wave priority the
+// workgroup runs its next row at, which offsets the age order of the memory
+// arbitration and evens out the finishing times.
+//
+//
+// NT threads per workgroup, SV / CV float4 groups per thread in the sample /
+// in each streamed chunk, NBUF chunks in flight (a register ring), CAP
+// candidates in LDS, WAVES = waves per SIMD the register budget is set for.
+// ---------------------------------------------------------------------------
+template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 stream_rows_kernel(KernelArgs a) {
+  constexpr uint32_t kSampleSpan = (uint32_t)NT * 4u * SV;
+  constexpr uint32_t kChunkSpan = (uint32_t)NT * 4u * CV;
+  constexpr uint32_t kRefresh = CAP - CAP / 4;   // raise the gate once the list is this full
+  static_assert(CAP >= kBinsNarrow, "the candidate list doubles as the gate's sub-histogram");
   __shared__ uint32_t sh_hist[kBinsWide];
-  __shared__ uint32_t sh_ckey[kStreamCap];
-  __shared__ int32_t sh_cpos[kStreamCap];
+  __shared__ uint32_t sh_ckey[CAP + 1];   // + the trash entry of an overflowing list
+  __shared__ int32_t sh_cpos[CAP + 1];
   __shared__ int32_t sh_raw[kMaxK];
   __shared__ uint32_t sh_scan[64];   // the 64 coarse bins of find_threshold
   __shared__ uint32_t sh_var[16];
+  __shared__ uint32_t sh_next_row;
 
   const int64_t W = a.width;
   const int k = a.k;
   const bool vec = a.vec != 0;
-  for (int64_t row = blockIdx.x; row < a.batch; row += gridDim.x) {
+  // The host passes a workspace only when there are more rows than workgroups.
+  uint32_t* const queue = a.ws != nullptr ? a.ws + kHdrRowTicket : nullptr;
+  const uint32_t grid = gridDim.x;
+  uint32_t row = blockIdx.x;
+  while (row < (uint32_t)a.batch) {
     const int tid = opaque_tid();
     const int64_t L64 = row_len(a, row);
     const uint32_t L = (uint32_t)L64;
     const int n = L64 < (int64_t)k ? (int)L64 : k;
     if (L64 <= (int64_t)k) {
-      write_row_output(a, row, L64, n, true, sh_raw, tid);
+      __syncthreads();   // every wave has read the previous row's ticket
+      if (tid == 0) sh_next_row = queue != nullptr ? grid + g_add_ret(queue, 1u) : row + grid;
+      write_row_output<NT>(a, row, L64, n, true, sh_raw, tid);
+      __syncthreads();
+      row = uniform(sh_next_row);
       continue;
     }
-    for (int b = tid; b < kBinsWide; b += kThreads) sh_hist[b] = 0;
-    for (int j = tid; j < k; j += kThreads) sh_raw[j] = -1;
+    for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
+    for (int j = tid; j < k; j += NT) sh_raw[j] = -1;
     if (tid < 16) sh_var[tid] = 0;
     const float* rowp = a.scores + row * W;
     __syncthreads();
 
     // 1. sample: full histogram of the first kSampleSpan positions (the
-    // first streamed chunk's loads are issued before the sample is used)
-    uint32_t sk[4 * kSampleVecs];
-    load_raw<kSampleVecs>(sk, rowp, 0u, L, vec, tid);
-    uint32_t ka[4 * kChunkVecs], kb[4 * kChunkVecs];
-    uint32_t c = kSampleSpan;
-    if (c < L) load_raw<kChunkVecs>(ka, rowp, c, L, vec, tid);
+    // first NBUF streamed chunks' loads are issued before the sample is used)
+    uint32_t sk[4 * SV];
+    load_raw<NT, SV>(sk, rowp, 0u, L, vec, tid);
+    const uint32_t nch = L > kSampleSpan ? (L - kSampleSpan + kChunkSpan - 1) / kChunkSpan : 0u;
+    uint32_t ring[NBUF][4 * CV];
 #pragma unroll
-    for (int j = 0; j < 4 * kSampleVecs; ++j) {
-      const uint32_t x = slot_key(sk[j], j, 0u, L, tid);
+    for (int b = 0; b < NBUF; ++b)
+      if ((uint32_t)b < nch) load_raw<NT, CV>(ring[b], rowp, kSampleSpan + (uint32_t)b * kChunkSpan, L, vec, tid);
+#pragma unroll
+    for (int j = 0; j < 4 * SV; ++j) {
+      const uint32_t x = slot_key<NT>(sk[j], j, 0u, L, tid);
       if (x) atomicAdd(&sh_hist[x >> 20], 1u);
     }
     __syncthreads();
-    find_threshold(sh_hist, kBinsWide, (uint32_t)n, sh_scan, sh_var, tid);
-    uint32_t gate = uniform(sh_var[0]) > 1u ? uniform(sh_var[0]) : 1u;
-    gated_append(sk, 0u, L, gate, true, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
-
-    // 2. stream the rest, two chunks in flight
-    while (c < L) {
-      const uint32_t cb = c + kChunkSpan;
-      if (cb < L) load_raw<kChunkVecs>(kb, rowp, cb, L, vec, tid);
-      gated_append(ka, c, L, gate, false, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
-      if (cb < L) {
-        const uint32_t ca = cb + kChunkSpan;
-        if (ca < L) load_raw<kChunkVecs>(ka, rowp, ca, L, vec, tid);
-        gated_append(kb, cb, L, gate, false, sh_hist, sh_ckey, sh_cpos, sh_var, tid);
-      }
-      c = cb + kChunkSpan;
-      __syncthreads();
-      if (uniform(sh_var[kVarCandCount]) > (uint32_t)kStreamRefresh)
-        gate = raise_gate(gate, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_scan, sh_var, tid);
+    const uint32_t m = gate_rank((uint32_t)n, L < kSampleSpan ? L : kSampleSpan, L);
+    find_threshold<NT, kBinsWide>(sh_hist, m, sh_scan, sh_var, tid);
+    // The gate is refined inside the sample's bin with the next 10 key bits,
+    // so that about m/S of the streamed keys pass it rather than a whole
+    // bin's worth more.  The (still empty) candidate list holds the
+    // sub-histogram meanwhile.
+    const uint32_t gbin = uniform(sh_var[0]), gneed = m - uniform(sh_var[1]);
+    for (int b = tid; b < kBinsNarrow; b += NT) sh_ckey[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4 * SV; ++j) {
+      const uint32_t x = slot_key<NT>(sk[j], j, 0u, L, tid);
+      if (x != 0u && (x >> 20) == gbin) atomicAdd(&sh_ckey[(x >> 10) & 1023u], 1u);
     }
     __syncthreads();
+    find_threshold<NT, kBinsNarrow>(sh_ckey, gneed, sh_scan, sh_var, tid);
+    uint32_t gate = (gbin << 20) | (uniform(sh_var[0]) << 10);
+    if (gate == 0u) gate = 1u;
+    gated_append<NT, CAP, 4 * SV, kGateChecked>(sk, 0u, L, gate, sh_ckey, sh_cpos, sh_var, tid);
 
-    // 3. threshold bin from the exact histogram, then the candidates
-    find_threshold(sh_hist, kBinsWide, (uint32_t)n, sh_scan, sh_var, tid);
-    const uint32_t t0 = uniform(sh_var[0]), gt0 = uniform(sh_var[1]), cnt0 = uniform(sh_var[2]);
+    // 2. stream the rest through the ring: chunk i + NBUF is requested as soon
+    // as chunk i's registers are consumed
+    for (uint32_t i = 0; i < nch; i += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        const uint32_t idx = i + (uint32_t)b;
+        if (idx < nch) {
+          const uint32_t cbase = kSampleSpan + idx * kChunkSpan;
+          if (cbase + kChunkSpan > L)
+            gated_append<NT, CAP, 4 * CV, kGateChecked>(ring[b], cbase, L, gate, sh_ckey, sh_cpos, sh_var, tid);
+          else if (gate >= 0x80000000u)
+            gated_append<NT, CAP, 4 * CV, kGatePositive>(ring[b], cbase, L, gate, sh_ckey, sh_cpos, sh_var, tid);
+          else
+            gated_append<NT, CAP, 4 * CV, kGateAny>(ring[b], cbase, L, gate, sh_ckey, sh_cpos, sh_var, tid);
+          if (idx + NBUF < nch)
+            load_raw<NT, CV>(ring[b], rowp, kSampleSpan + (idx + NBUF) * kChunkSpan, L, vec, tid);
+        }
+      }
+      __syncthreads();
+      if (uniform(sh_var[kVarCandCount]) > kRefresh)
+        gate = raise_gate<NT, CAP>(gate, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_scan, sh_var, tid);
+    }
+    // next row's ticket; its return is first needed when the row is written
+    uint32_t next = row + grid;
+    if (queue != nullptr && tid == 0) next = grid + g_add_ret(queue, 1u);
+    __syncthreads();
+
+    // 3. The list holds every key >= gate unless it overflowed: its histogram
+    // gives the threshold bin, the remaining digits run on the list.  With
+    // fewer than n keys at or above the gate (the sample overrated the row)
+    // or an overflowed list, the row's histogram is taken from memory (keys
+    // below the gate count only in the first case) and the row finished there.
     const uint32_t count = uniform(sh_var[kVarCandCount]);
-    const bool overflow = uniform(sh_var[kVarOverflow]) != 0u || count > (uint32_t)kStreamCap;
+    const bool low_count = count < (uint32_t)n;
+    const bool overflow = low_count || uniform(sh_var[kVarOverflow]) != 0u || count > (uint32_t)CAP;
+    const uint32_t floor = low_count ? 1u : gate;
     if (!overflow) {
-      select_candidates((int)count, t0, 20, cnt0, (uint32_t)n - gt0, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                        sh_raw, sh_scan, sh_var, tid);
+      list_histogram<NT>(count, sh_ckey, sh_hist, tid);
+    } else {
+      for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
+      __syncthreads();
+      restream_pass<NT, CAP, CV>(3, rowp, L, vec, floor, 0u, 20, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
+                                 sh_var, tid);
+    }
+    find_threshold<NT, kBinsWide>(sh_hist, (uint32_t)n, sh_scan, sh_var, tid);
+    const uint32_t t0 = uniform(sh_var[0]), gt0 = uniform(sh_var[1]), cnt0 = uniform(sh_var[2]);
+    if (!overflow) {
+      select_candidates<NT>((int)count, t0, 20, cnt0, (uint32_t)n - gt0, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
+                            sh_raw, sh_scan, sh_var, tid);
     } else {
       uint32_t prefix = t0, need = (uint32_t)n - gt0, cnt = cnt0;
       int shift = 20;
-      while (cnt > (uint32_t)kStreamCap && cnt != need && shift > 0) {
-        for (int b = tid; b < kBinsNarrow; b += kThreads) sh_hist[b] = 0;
+      while (cnt > (uint32_t)CAP && cnt != need && shift > 0) {
+        for (int b = tid; b < kBinsNarrow; b += NT) sh_hist[b] = 0;
         __syncthreads();
-        restream_pass(0, rowp, L, vec, prefix, shift, need, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw, sh_var,
-                      tid);
-        find_threshold(sh_hist, kBinsNarrow, need, sh_scan, sh_var, tid);
+        restream_pass<NT, CAP, CV>(0, rowp, L, vec, floor, prefix, shift, need, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
+                                   sh_raw, sh_var, tid);
+        find_threshold<NT, kBinsNarrow>(sh_hist, need, sh_scan, sh_var, tid);
         const uint32_t bin = uniform(sh_var[0]), gt = uniform(sh_var[1]);
         cnt = uniform(sh_var[2]);
         need -= gt;
@@ -833,22 +989,59 @@ stream_rows_kernel(KernelArgs a) {
         sh_var[kVarEq] = 0;
       }
       __syncthreads();
-      const bool collect = cnt <= (uint32_t)kStreamCap && cnt != need && shift > 0;
-      restream_pass(collect ? 1 : 2, rowp, L, vec, prefix, shift, need, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                    sh_raw, sh_var, tid);
+      const bool collect = cnt <= (uint32_t)CAP && cnt != need && shift > 0;
+      restream_pass<NT, CAP, CV>(collect ? 1 : 2, rowp, L, vec, floor, prefix, shift, need, (uint32_t)n, sh_hist, sh_ckey,
+                                 sh_cpos, sh_raw, sh_var, tid);
       if (collect)
-        select_candidates((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist, sh_ckey,
-                          sh_cpos, sh_raw, sh_scan, sh_var, tid);
+        select_candidates<NT>((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist,
+                              sh_ckey, sh_cpos, sh_raw, sh_scan, sh_var, tid);
     }
+    if (tid == 0) sh_next_row = next;
     __syncthreads();
-    write_row_output(a, row, L64, n, false, sh_raw, tid);
+    write_row_output<NT>(a, row, L64, n, false, sh_raw, tid);
     __syncthreads();
+    row = uniform(sh_next_row);
+    if (queue != nullptr) set_row_priority(row, grid);
+  }
+  // Every workgroup took its last ticket before counting itself out here, so
+  // the last one out may reset the queue.
+  if (queue != nullptr && threadIdx.x == 0) {
+    if (g_add_ret(a.ws + kHdrRowExit, 1u) == grid - 1u) {
+      g_store(queue, 0u);
+      g_store(a.ws + kHdrRowExit, 0u);
+    }
   }
 }
 
-hipError_t launch_stream(const KernelArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL(stream_rows_kernel, dim3((unsigned)args.slots), dim3(kThreads), 0, stream, args);
-  return hipGetLastError();
+// Streaming-kernel shapes: (threads, sample float4 groups per thread, chunk
+// float4 groups per thread, chunks in flight, LDS candidates, waves per SIMD).
+#define TOPK_STREAM_VARIANTS(X) \
+  X(0, 1024, 4, 2, 2, 6144, 8)  \
+  X(1, 256, 8, 4, 2, 1920, 4)
+
+hipError_t launch_stream_variant(int variant, const KernelArgs& args, hipStream_t stream) {
+  switch (variant) {
+#define TOPK_LAUNCH_CASE(id, nt, sv, cv, nbuf, cap, waves)                                                      \
+  case id:                                                                                              \
+    hipLaunchKernelGGL((stream_rows_kernel<nt, sv, cv, nbuf, cap, waves>), dim3((unsigned)args.slots), dim3(nt), 0, \
+                       stream, args);                                                                   \
+    return hipGetLastError();
+    TOPK_STREAM_VARIANTS(TOPK_LAUNCH_CASE)
+#undef TOPK_LAUNCH_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t occupancy_stream_variant(int variant, int* blocks) {
+  switch (variant) {
+#define TOPK_OCC_CASE(id, nt, sv, cv, nbuf, cap, waves)                                                         \
+  case id:                                                                                              \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                                \
+        blocks, reinterpret_cast<const void*>(&stream_rows_kernel<nt, sv, cv, nbuf, cap, waves>), nt, 0);
+    TOPK_STREAM_VARIANTS(TOPK_OCC_CASE)
+#undef TOPK_OCC_CASE
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int E>
@@ -889,11 +1082,21 @@ hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStre
   }
 }
 
-hipError_t launch_stream_rows(const KernelArgs& args, hipStream_t stream) { return launch_stream(args, stream); }
+hipError_t launch_stream_rows(int variant, const KernelArgs& args, hipStream_t stream) {
+  return launch_stream_variant(variant, args, stream);
+}
 
-hipError_t stream_occupancy(int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(&stream_rows_kernel),
-                                                      kThreads, 0);
+hipError_t stream_occupancy(int variant, int* blocks_per_cu) { return occupancy_stream_variant(variant, blocks_per_cu); }
+
+int stream_variant_threads(int variant) {
+  switch (variant) {
+#define TOPK_NT_CASE(id, nt, sv, cv, nbuf, cap, waves) \
+  case id:                                       \
+    return nt;
+    TOPK_STREAM_VARIANTS(TOPK_NT_CASE)
+#undef TOPK_NT_CASE
+    default: return 0;
+  }
 }
 
 hipError_t rows_occupancy(int ept_index, bool coop, int* blocks_per_cu) {

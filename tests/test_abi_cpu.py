@@ -68,6 +68,15 @@ def test_dispatch_override_validation(lib):
     assert lib.topk_set_dispatch_override(0, 0) == 0
 
 
+def test_stream_shape_validation(lib):
+    """Two compiled streaming shapes (0 and 1); -1 restores automatic choice."""
+    for shape in range(-1, topk.STREAM_SHAPES):
+        assert lib.topk_set_stream_shape(shape) == 0
+    assert lib.topk_set_stream_shape(topk.STREAM_SHAPES) == 1
+    assert lib.topk_set_stream_shape(-2) == 1
+    assert lib.topk_set_stream_shape(-1) == 0
+
+
 def test_python_binding_rejects_bad_tensors():
     import torch
     s = torch.zeros((2, 8), dtype=torch.float32)

@@ -7,6 +7,7 @@ exactly the threshold key; the transform is compared slot by slot.
 import numpy as np
 import pytest
 
+import sparse_attention_indexer_fp32_amd as topk
 import workloads
 from gpu_util import check, check_properties_all_rows, note, run, upload
 
@@ -182,3 +183,83 @@ def test_graph_replay(lib):
 
 def test_fault_word_clear(lib):
     assert lib.topk_debug_fault_word() == 0
+
+
+# ---- streaming kernel: every compiled shape, and the row queue (batch > grid)
+
+STREAM_SHAPES = topk.STREAM_SHAPES
+
+@pytest.mark.parametrize("shape", range(STREAM_SHAPES))
+def test_stream_shapes_row_queue(lib, shape):
+    """More rows than workgroups: rows past the first grid come from the
+    ticket queue.  Ragged lengths (many rows shorter than k) and an unaligned
+    width; the call is repeated to check the queue resets itself."""
+    W = 6001
+    rng = np.random.Generator(np.random.PCG64(900 + shape))
+    B = 2600
+    seq = rng.integers(-5, W + 20, size=B)
+    short = rng.random(B) < 0.25
+    seq[short] = rng.integers(0, 600, size=int(short.sum()))
+    w = workloads.custom(40 + shape, B, W, 512, 16, seq_lens=seq.tolist(), kind="normal")
+    note(f"stream shape={shape} queue B={B} W={W}")
+    lib.topk_set_stream_shape(shape)
+    lib.topk_set_dispatch_override(0, 1)
+    try:
+        t = upload(w)
+        out, raw = run(lib, w, raw=True, tensors=t)
+        note(f"stream shape={shape}: {lib.topk_last_launch()}")
+        check(w, out, raw)
+        for _ in range(2):   # slot order may differ between calls; the selection may not
+            out2, raw2 = run(lib, w, raw=True, tensors=t)
+            check(w, out2, raw2)
+    finally:
+        lib.topk_set_stream_shape(-1)
+        lib.topk_set_dispatch_override(0, 0)
+
+
+@pytest.mark.parametrize("shape", range(STREAM_SHAPES))
+@pytest.mark.parametrize("kind", ["ties", "const", "asc"])
+def test_stream_shapes_adversarial(lib, shape, kind):
+    """Every shape through its gate-raising and overflow paths."""
+    W = 70001
+    seq = [W, W - 1, W // 3, 2049, 17000, 0, 513]
+    for k in (1, 2048):
+        w = workloads.custom(60 + shape + k, len(seq), W, k, 64, seq_lens=seq, kind=kind)
+        note(f"stream shape={shape} kind={kind} k={k}")
+        lib.topk_set_stream_shape(shape)
+        lib.topk_set_dispatch_override(0, 1)
+        try:
+            out, raw = run(lib, w, raw=True)
+        finally:
+            lib.topk_set_stream_shape(-1)
+            lib.topk_set_dispatch_override(0, 0)
+        check(w, out, raw)
+
+
+def test_graph_replay_row_queue(lib):
+    """The row queue inside a replayed HIP graph: it must reset itself on every replay."""
+    import torch
+    w = workloads.custom(8, 3000, 8192, 256, 16, kind="normal")
+    s, sl, pt = upload(w)
+    out = torch.empty((w.batch, w.k), dtype=torch.int32, device=s.device)
+    lib.topk_set_dispatch_override(0, 1)
+    try:
+        g = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)   # workspace allocated outside capture
+            stream.synchronize()
+            note(f"graph queue: {lib.topk_last_launch()}")
+            eager = out.cpu().numpy().copy()
+            check(w, eager, None)
+            with torch.cuda.graph(g, stream=stream):
+                lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)
+        for rep in range(4):
+            out.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            check(w, out.cpu().numpy(), None)
+            lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)   # eager call between replays
+            torch.cuda.synchronize()
+    finally:
+        lib.topk_set_dispatch_override(0, 0)
