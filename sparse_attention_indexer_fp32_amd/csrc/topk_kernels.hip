@@ -887,7 +887,7 @@ stream_rows_kernel(KernelArgs a) {
 
     // 1. sample: full histogram of the first kSampleSpan positions (the
     // first NBUF streamed chunks' loads are issued before the sample is used)
-    uint32_t sk[4 * SV];
+    uint32_t sk[4 * SV];   // the sample's raw scores
     load_raw<NT, SV>(sk, rowp, 0u, L, vec, tid);
     const uint32_t nch = L > kSampleSpan ? (L - kSampleSpan + kChunkSpan - 1) / kChunkSpan : 0u;
     uint32_t ring[NBUF][4 * CV];
@@ -918,11 +918,28 @@ stream_rows_kernel(KernelArgs a) {
     find_threshold<NT, kBinsNarrow>(sh_ckey, gneed, sh_scan, sh_var, tid);
     uint32_t gate = (gbin << 20) | (uniform(sh_var[0]) << 10);
     if (gate == 0u) gate = 1u;
-    gated_append<NT, CAP, 4 * SV, kGateChecked>(sk, 0u, L, gate, sh_ckey, sh_cpos, sh_var, tid);
+    {   // in two halves: fewer ballot masks live at once (register pressure)
+      static_assert(SV % 2 == 0, "the sample is appended in two halves");
+      uint32_t lo[2 * SV], hi[2 * SV];
+#pragma unroll
+      for (int j = 0; j < 2 * SV; ++j) {
+        lo[j] = sk[j];
+        hi[j] = sk[2 * SV + j];
+      }
+      constexpr uint32_t half = (uint32_t)NT * 4u * (SV / 2);
+      gated_append<NT, CAP, 2 * SV, kGateChecked>(lo, 0u, L, gate, sh_ckey, sh_cpos, sh_var, tid);
+      gated_append<NT, CAP, 2 * SV, kGateChecked>(hi, half, L, gate, sh_ckey, sh_cpos, sh_var, tid);
+    }
 
     // 2. stream the rest through the ring: chunk i + NBUF is requested as soon
     // as chunk i's registers are consumed
+    // next row's ticket, taken at the start of the last ring cycle (its return
+    // is first needed when the stream ends)
+    uint32_t next = row + grid;
+    const uint32_t last_cycle = nch > 0u ? ((nch - 1u) / NBUF) * NBUF : 0u;
+    if (queue != nullptr && tid == 0 && nch == 0u) next = grid + g_add_ret(queue, 1u);
     for (uint32_t i = 0; i < nch; i += NBUF) {
+      if (queue != nullptr && tid == 0 && i == last_cycle) next = grid + g_add_ret(queue, 1u);
 #pragma unroll
       for (int b = 0; b < NBUF; ++b) {
         const uint32_t idx = i + (uint32_t)b;
@@ -942,9 +959,7 @@ stream_rows_kernel(KernelArgs a) {
       if (uniform(sh_var[kVarCandCount]) > kRefresh)
         gate = raise_gate<NT, CAP>(gate, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_scan, sh_var, tid);
     }
-    // next row's ticket; its return is first needed when the row is written
-    uint32_t next = row + grid;
-    if (queue != nullptr && tid == 0) next = grid + g_add_ret(queue, 1u);
+    if (tid == 0) sh_next_row = next;
     __syncthreads();
 
     // 3. The list holds every key >= gate unless it overflowed: its histogram
@@ -996,7 +1011,6 @@ stream_rows_kernel(KernelArgs a) {
         select_candidates<NT>((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist,
                               sh_ckey, sh_cpos, sh_raw, sh_scan, sh_var, tid);
     }
-    if (tid == 0) sh_next_row = next;
     __syncthreads();
     write_row_output<NT>(a, row, L64, n, false, sh_raw, tid);
     __syncthreads();
