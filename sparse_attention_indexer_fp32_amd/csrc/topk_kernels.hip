@@ -232,16 +232,17 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, int G, uint32_t* faul
 
 // Gather + transform pass: slot j < n holds raw position r (trivial rows: r = j);
 // out = page_table[row, r >> log2_page] << log2_page | (r & (page_size - 1)).
-// Slots past n, and any r outside [0, L), give -1.
+// Slots past n, and any r outside [0, L), give -1.  `pt_row` is the row's
+// page table, in global memory or an LDS copy of it.
 template <int NT>
 __device__ __forceinline__ void write_row_output(const KernelArgs& a, int64_t row, int64_t L, int n, bool trivial,
-                                                 const int32_t* sh_raw, int tid) {
+                                                 const int32_t* sh_raw, int tid, const int32_t* pt_row = nullptr) {
   const int k = a.k;
   const int s = a.log2_page;
   const uint32_t pmask = (1u << s) - 1u;
   int32_t* o = a.out + row * (int64_t)k;
   int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
-  const int32_t* pt = a.page_table + row * a.pages_per_row;
+  const int32_t* pt = pt_row != nullptr ? pt_row : a.page_table + row * a.pages_per_row;
   for (int j = tid; j < k; j += NT) {
     int32_t r = -1;
     if (j < n) r = trivial ? j : sh_raw[j];
@@ -804,11 +805,6 @@ __device__ __forceinline__ uint32_t gate_rank(uint32_t n, uint32_t S, uint32_t L
   return m < (float)n ? (uint32_t)m : n;
 }
 
-__device__ __forceinline__ int64_t row_len(const KernelArgs& a, int64_t row) {
-  const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
-  return sl < 0 ? 0 : ((int64_t)sl > a.width ? a.width : (int64_t)sl);
-}
-
 // ---------------------------------------------------------------------------
 // Streaming one-workgroup-per-row kernel (large batches).
 //
@@ -843,8 +839,11 @@ __device__ __forceinline__ int64_t row_len(const KernelArgs& a, int64_t row) {
 // NT threads per workgroup, SV / CV float4 groups per thread in the sample /
 // in each streamed chunk, NBUF chunks in flight (a register ring), CAP
 // candidates in LDS, WAVES = waves per SIMD the register budget is set for.
+// With PTL, a row's page table (up to 4 NT entries) is requested before the
+// row is finished and staged in LDS for the output pass, taking the gather's
+// dependent global loads off the row's critical path.
 // ---------------------------------------------------------------------------
-template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES>
+template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool PTL>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 stream_rows_kernel(KernelArgs a) {
   constexpr uint32_t kSampleSpan = (uint32_t)NT * 4u * SV;
@@ -854,10 +853,15 @@ stream_rows_kernel(KernelArgs a) {
   __shared__ uint32_t sh_hist[kBinsWide];
   __shared__ uint32_t sh_ckey[CAP + 1];   // + the trash entry of an overflowing list
   __shared__ int32_t sh_cpos[CAP + 1];
-  __shared__ int32_t sh_raw[kMaxK];
   __shared__ uint32_t sh_scan[64];   // the 64 coarse bins of find_threshold
+  // The selected positions share the histogram's upper half: once the row's
+  // 12-bit threshold bin is known, only 10-bit digits (bins [0, 1024)) are
+  // histogrammed until the row is written.
+  static_assert(kBinsWide - kMaxK >= kBinsNarrow, "selected positions alias the histogram's upper half");
+  int32_t* const sh_raw = reinterpret_cast<int32_t*>(sh_hist + (kBinsWide - kMaxK));
   __shared__ uint32_t sh_var[16];
   __shared__ uint32_t sh_next_row;
+  __shared__ int32_t sh_next_len;   // seq_lens[next row], loaded while this row finishes
 
   const int64_t W = a.width;
   const int k = a.k;
@@ -866,21 +870,26 @@ stream_rows_kernel(KernelArgs a) {
   uint32_t* const queue = a.ws != nullptr ? a.ws + kHdrRowTicket : nullptr;
   const uint32_t grid = gridDim.x;
   uint32_t row = blockIdx.x;
+  int32_t seq = row < (uint32_t)a.batch ? (int32_t)uniform((uint32_t)a.seq_lens[row]) : 0;
   while (row < (uint32_t)a.batch) {
     const int tid = opaque_tid();
-    const int64_t L64 = row_len(a, row);
+    const int64_t L64 = seq < 0 ? 0 : ((int64_t)seq > W ? W : (int64_t)seq);
     const uint32_t L = (uint32_t)L64;
     const int n = L64 < (int64_t)k ? (int)L64 : k;
     if (L64 <= (int64_t)k) {
       __syncthreads();   // every wave has read the previous row's ticket
-      if (tid == 0) sh_next_row = queue != nullptr ? grid + g_add_ret(queue, 1u) : row + grid;
+      if (tid == 0) {
+        const uint32_t nx = queue != nullptr ? grid + g_add_ret(queue, 1u) : row + grid;
+        sh_next_row = nx;
+        sh_next_len = nx < (uint32_t)a.batch ? a.seq_lens[nx] : 0;
+      }
       write_row_output<NT>(a, row, L64, n, true, sh_raw, tid);
       __syncthreads();
       row = uniform(sh_next_row);
+      seq = (int32_t)uniform((uint32_t)sh_next_len);
       continue;
     }
     for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
-    for (int j = tid; j < k; j += NT) sh_raw[j] = -1;
     if (tid < 16) sh_var[tid] = 0;
     const float* rowp = a.scores + row * W;
     __syncthreads();
@@ -959,8 +968,23 @@ stream_rows_kernel(KernelArgs a) {
       if (uniform(sh_var[kVarCandCount]) > kRefresh)
         gate = raise_gate<NT, CAP>(gate, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_scan, sh_var, tid);
     }
-    if (tid == 0) sh_next_row = next;
+    // Every wave's appends are in (the loop's last barrier does this, but a
+    // row that fits in the sample has no loop) before the count is read.
     __syncthreads();
+    // The next row's length and this row's page table are requested now and
+    // first used after the finish below.
+    int32_t next_len = 0;
+    if (tid == 0 && next < (uint32_t)a.batch) next_len = a.seq_lens[next];
+    const bool pt_in_lds = PTL && a.pages_per_row <= (int64_t)(4 * NT);
+    uint32_t ptv[4];
+    if (pt_in_lds) {
+      const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int32_t*>(a.page_table) + (int64_t)row * a.pages_per_row, (short)0,
+          (int)(a.pages_per_row * 4), kBufferWord3);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        ptv[v] = __builtin_amdgcn_raw_buffer_load_b32(prs, (uint32_t)tid * 4u, v * NT * 4, 0);
+    }
 
     // 3. The list holds every key >= gate unless it overflowed: its histogram
     // gives the threshold bin, the remaining digits run on the list.  With
@@ -981,6 +1005,8 @@ stream_rows_kernel(KernelArgs a) {
     }
     find_threshold<NT, kBinsWide>(sh_hist, (uint32_t)n, sh_scan, sh_var, tid);
     const uint32_t t0 = uniform(sh_var[0]), gt0 = uniform(sh_var[1]), cnt0 = uniform(sh_var[2]);
+    for (int j = tid; j < k; j += NT) sh_raw[j] = -1;   // the 12-bit histogram is done with
+    __syncthreads();
     if (!overflow) {
       select_candidates<NT>((int)count, t0, 20, cnt0, (uint32_t)n - gt0, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
                             sh_raw, sh_scan, sh_var, tid);
@@ -1011,10 +1037,22 @@ stream_rows_kernel(KernelArgs a) {
         select_candidates<NT>((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist,
                               sh_ckey, sh_cpos, sh_raw, sh_scan, sh_var, tid);
     }
+    // the candidate list is free again: it holds the page-table row
+    int32_t* const sh_pt = reinterpret_cast<int32_t*>(sh_ckey);
+    static_assert(!PTL || CAP >= 4 * NT, "the candidate list holds a page-table row of up to 4 NT entries");
+    if (pt_in_lds) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sh_pt[tid + v * NT] = (int32_t)ptv[v];
+    }
+    if (tid == 0) {
+      sh_next_row = next;
+      sh_next_len = next_len;
+    }
     __syncthreads();
-    write_row_output<NT>(a, row, L64, n, false, sh_raw, tid);
+    write_row_output<NT>(a, row, L64, n, false, sh_raw, tid, pt_in_lds ? sh_pt : nullptr);
     __syncthreads();
     row = uniform(sh_next_row);
+    seq = (int32_t)uniform((uint32_t)sh_next_len);
     if (queue != nullptr) set_row_priority(row, grid);
   }
   // Every workgroup took its last ticket before counting itself out here, so
@@ -1028,16 +1066,17 @@ stream_rows_kernel(KernelArgs a) {
 }
 
 // Streaming-kernel shapes: (threads, sample float4 groups per thread, chunk
-// float4 groups per thread, chunks in flight, LDS candidates, waves per SIMD).
-#define TOPK_STREAM_VARIANTS(X) \
-  X(0, 1024, 4, 2, 2, 6144, 8)  \
-  X(1, 256, 8, 4, 2, 1920, 4)
+// float4 groups per thread, chunks in flight, LDS candidates, waves per SIMD,
+// page-table row staged in LDS).
+#define TOPK_STREAM_VARIANTS(X)      \
+  X(0, 1024, 4, 2, 2, 6144, 8, false) \
+  X(1, 256, 8, 4, 2, 1920, 4, true)
 
 hipError_t launch_stream_variant(int variant, const KernelArgs& args, hipStream_t stream) {
   switch (variant) {
-#define TOPK_LAUNCH_CASE(id, nt, sv, cv, nbuf, cap, waves)                                                      \
+#define TOPK_LAUNCH_CASE(id, nt, sv, cv, nbuf, cap, waves, ptl)                                                      \
   case id:                                                                                              \
-    hipLaunchKernelGGL((stream_rows_kernel<nt, sv, cv, nbuf, cap, waves>), dim3((unsigned)args.slots), dim3(nt), 0, \
+    hipLaunchKernelGGL((stream_rows_kernel<nt, sv, cv, nbuf, cap, waves, ptl>), dim3((unsigned)args.slots), dim3(nt), 0, \
                        stream, args);                                                                   \
     return hipGetLastError();
     TOPK_STREAM_VARIANTS(TOPK_LAUNCH_CASE)
@@ -1048,10 +1087,10 @@ hipError_t launch_stream_variant(int variant, const KernelArgs& args, hipStream_
 
 hipError_t occupancy_stream_variant(int variant, int* blocks) {
   switch (variant) {
-#define TOPK_OCC_CASE(id, nt, sv, cv, nbuf, cap, waves)                                                         \
+#define TOPK_OCC_CASE(id, nt, sv, cv, nbuf, cap, waves, ptl)                                                         \
   case id:                                                                                              \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                                \
-        blocks, reinterpret_cast<const void*>(&stream_rows_kernel<nt, sv, cv, nbuf, cap, waves>), nt, 0);
+        blocks, reinterpret_cast<const void*>(&stream_rows_kernel<nt, sv, cv, nbuf, cap, waves, ptl>), nt, 0);
     TOPK_STREAM_VARIANTS(TOPK_OCC_CASE)
 #undef TOPK_OCC_CASE
     default: return hipErrorInvalidValue;
@@ -1104,7 +1143,7 @@ hipError_t stream_occupancy(int variant, int* blocks_per_cu) { return occupancy_
 
 int stream_variant_threads(int variant) {
   switch (variant) {
-#define TOPK_NT_CASE(id, nt, sv, cv, nbuf, cap, waves) \
+#define TOPK_NT_CASE(id, nt, sv, cv, nbuf, cap, waves, ptl) \
   case id:                                       \
     return nt;
     TOPK_STREAM_VARIANTS(TOPK_NT_CASE)

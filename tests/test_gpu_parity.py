@@ -263,3 +263,25 @@ def test_graph_replay_row_queue(lib):
             torch.cuda.synchronize()
     finally:
         lib.topk_set_dispatch_override(0, 0)
+
+
+@pytest.mark.parametrize("shape", range(STREAM_SHAPES))
+def test_stream_rows_within_sample_repeated(lib, shape):
+    """Rows no longer than the streaming kernel's sample have no streamed
+    chunks; every one of repeated calls must be exact (regression: the list
+    count was once read before every wave's appends were in, which only a
+    row without chunks exposed, and only on some calls)."""
+    for W in (16384, 8192, 3001):   # shape 0's sample span, shape 1's, shorter
+        seq = [W, W - 1, 2000, 600]
+        w = workloads.custom(70 + shape, len(seq), W, 512, 64, seq_lens=seq, kind="normal")
+        note(f"stream shape={shape} within-sample W={W}")
+        lib.topk_set_stream_shape(shape)
+        lib.topk_set_dispatch_override(0, 1)
+        try:
+            t = upload(w)
+            for rep in range(20):
+                out, raw = run(lib, w, raw=rep % 2 == 0, tensors=t)
+                check(w, out, raw)
+        finally:
+            lib.topk_set_stream_shape(-1)
+            lib.topk_set_dispatch_override(0, 0)
