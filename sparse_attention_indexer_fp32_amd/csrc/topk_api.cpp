@@ -139,6 +139,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 enum class Kind { kResident, kSplit, kStream };
 
+// Preferred upper bound on workgroups sharing one split row.
+constexpr int64_t kMaxSplitWgs = 128;
+
 // Compiled streaming shapes (TOPK_STREAM_VARIANTS): 0 = 1024-thread
 // workgroups with 6144 LDS candidates, 1 = 256-thread workgroups with 1920.
 constexpr int kStreamWide = 0;
@@ -205,15 +208,19 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
   } else if (2 * B >= dev.cus || B >= stream_slots || Wc <= 16384) {
     plan->kind = Kind::kStream;
   } else {
+    // Smallest E whose grid fits resident with at most kMaxSplitWgs
+    // workgroups per row: each extra workgroup adds histogram pushes and
+    // barrier arrivals (measured on a 1M row: 256 workgroups 22 us, 128 19 us).
     int chosen = -1;
-    for (int i = 0; i < topk::kNumEpt; ++i) {
-      const int64_t G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[i]);
-      const int64_t cap = (int64_t)dev.occ[1][i] * dev.cus;
-      if (B * G <= cap) {
-        chosen = i;
-        break;
+    for (int pass = 0; pass < 2 && chosen < 0; ++pass)
+      for (int i = 0; i < topk::kNumEpt; ++i) {
+        const int64_t G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[i]);
+        const int64_t cap = (int64_t)dev.occ[1][i] * dev.cus;
+        if (B * G <= cap && (pass == 1 || G <= kMaxSplitWgs)) {
+          chosen = i;
+          break;
+        }
       }
-    }
     if (chosen < 0) {
       plan->kind = Kind::kStream;   // too many rows to hold resident: stream them
     } else {
@@ -233,7 +240,7 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
       break;
     case Kind::kSplit: {
       const int64_t cap = (int64_t)dev.occ[1][plan->ept_idx] * dev.cus;
-      if (plan->G > cap)
+      if (plan->G > cap || plan->G > (int64_t)topk::kBarGroup * topk::kBarMaxGroups)
         return fail(TOPK_ERROR_UNSUPPORTED, "row width needs more cooperating workgroups than fit resident");
       int64_t slots = cap / plan->G;
       if (slots > B) slots = B;

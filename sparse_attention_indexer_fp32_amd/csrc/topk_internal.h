@@ -28,7 +28,16 @@ constexpr int kEptValues[kNumEpt] = {4, 8, 16, 32, 64};
 constexpr size_t kHdrWords = 64;        // [0] = fault word (a bounded wait timed out)
 constexpr size_t kHdrRowTicket = 32;    // streaming kernel: rows handed out beyond the first grid's
 constexpr size_t kHdrRowExit = 48;      // streaming kernel: workgroups out of rows
-constexpr size_t kBarWords = 32;        // per slot: [0] arrivals, [1] generation (own 128 B line)
+// Per-slot barrier block: an arrival counter per group of kBarGroup
+// workgroups, a counter of completed groups, and the generation, each on its
+// own 128-byte line (arrivals then contend per group, not per row, and the
+// spinners' polls do not share a line with the atomics).
+constexpr int kBarGroup = 8;
+constexpr int kBarMaxGroups = 128;      // workgroups per row <= kBarGroup * kBarMaxGroups
+constexpr size_t kBarLine = 32;         // words per 128-byte line
+constexpr size_t kBarTop = kBarLine * kBarMaxGroups;
+constexpr size_t kBarGen = kBarTop + kBarLine;
+constexpr size_t kBarWords = kBarGen + kBarLine;
 constexpr size_t kRegHist0 = 0;
 constexpr size_t kRegHist1 = kRegHist0 + kBinsWide;
 constexpr size_t kRegHist2 = kRegHist1 + kBinsNarrow;

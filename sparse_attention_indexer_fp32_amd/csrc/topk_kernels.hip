@@ -199,27 +199,43 @@ __device__ __forceinline__ void find_threshold(const uint32_t* h, uint32_t need,
 __device__ __forceinline__ void wave_mem_drain() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Per-row barrier among the G workgroups of one slot.  The grid never exceeds
-// the device's resident-workgroup capacity, so all G are running.  Sense is a
-// generation counter: the last arriver resets the arrival count (drained
-// before it bumps the generation), so the barrier resets itself across calls
-// and graph replays.  The wait is bounded: on timeout the fault word is set
-// and every later wait returns at once, so the kernel always drains.
-__device__ __forceinline__ void row_barrier(uint32_t* bar, int G, uint32_t* fault, int tid) {
+// the device's resident-workgroup capacity, so all G are running.  Workgroup
+// g arrives on its group's counter; the last of a group resets that counter
+// and arrives on the top counter; the last group's closer resets the top and
+// publishes the next generation.  Every reset is drained before the arrival
+// (or publication) that follows it, so the counters are zero again before any
+// workgroup can leave, and the barrier resets itself across calls and graph
+// replays.  Each workgroup tracks the generation it waits for in `gen` (read
+// once per launch: no barrier of the slot can complete before this workgroup
+// has arrived, so the value is stable until then).  The wait is bounded: on
+// timeout the fault word is set, and waits that see it set give up, so the
+// kernel always drains.
+__device__ __forceinline__ void row_barrier(uint32_t* bar, int G, int g, uint32_t& gen, uint32_t* fault, int tid) {
   wave_mem_drain();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t gen = g_load(bar + 1);
-    wave_mem_drain();   // the generation is read before this workgroup's arrival
-    const uint32_t old = g_add_ret(bar, 1u);
-    if (old == (uint32_t)G - 1) {
-      g_store(bar, 0u);
+    ++gen;
+    const int grp = g / kBarGroup;
+    const int ngroups = (G + kBarGroup - 1) / kBarGroup;
+    const uint32_t gsize = (uint32_t)(G - grp * kBarGroup < kBarGroup ? G - grp * kBarGroup : kBarGroup);
+    bool closer = false;
+    if (g_add_ret(bar + (size_t)grp * kBarLine, 1u) == gsize - 1u) {
+      g_store(bar + (size_t)grp * kBarLine, 0u);
       wave_mem_drain();
-      g_add(bar + 1, 1u);
-    } else if (g_load(fault) == 0u) {
+      if (g_add_ret(bar + kBarTop, 1u) == (uint32_t)ngroups - 1u) {
+        g_store(bar + kBarTop, 0u);
+        closer = true;
+      }
+    }
+    if (closer) {
+      wave_mem_drain();
+      g_store(bar + kBarGen, gen);
+    } else {
       uint32_t spins = 0;
-      while (g_load(bar + 1) == gen) {
+      while ((int32_t)(g_load(bar + kBarGen) - gen) < 0) {
         __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
+        ++spins;
+        if (spins > kSpinLimit || ((spins & 1023u) == 0u && g_load(fault) != 0u)) {
           g_store(fault, 1u);
           break;
         }
@@ -276,20 +292,26 @@ struct SampleSlots {
 // For a split row each workgroup gates on its own sample, which is as valid:
 // the row's threshold bin is >= every workgroup's t_s.
 template <int E>
-__device__ __forceinline__ void hist_pass0(const uint32_t (&key)[E], uint32_t need, uint32_t* h,
-                                           uint32_t* sh_scan, uint32_t* sh_var, int tid) {
+// Returns t_s (the lowest bin the row's threshold can be in, as far as this
+// workgroup's keys tell); with `want_gate` false and no sampling, returns 0
+// without searching.
+__device__ __forceinline__ uint32_t hist_pass0(const uint32_t (&key)[E], uint32_t need, uint32_t* h,
+                                               uint32_t* sh_scan, uint32_t* sh_var, int tid, bool want_gate) {
   constexpr int S = SampleSlots<E>::value;
 #pragma unroll
   for (int j = 0; j < S; ++j)
     if (key[j]) atomicAdd(&h[key[j] >> 20], 1u);
-  if (S == E) return;
+  if (S == E && !want_gate) return 0u;
   __syncthreads();
   find_threshold<kThreads, kBinsWide>(h, need, sh_scan, sh_var, tid);
+  const uint32_t ts = uniform(sh_var[0]);
+  if (S == E) return ts;
   // Bin >= 1 also excludes key 0 (no element).
-  const uint32_t gate = uniform(sh_var[0]) > 1u ? uniform(sh_var[0]) : 1u;
+  const uint32_t gate = ts > 1u ? ts : 1u;
 #pragma unroll
   for (int j = S; j < E; ++j)
     if ((key[j] >> 20) >= gate) atomicAdd(&h[key[j] >> 20], 1u);
+  return ts;
 }
 
 template <int E>
@@ -425,6 +447,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
   const int k = a.k;
   uint32_t* fault = a.ws;
   uint32_t* bar = COOP ? a.ws + kHdrWords + (size_t)slot * kBarWords : nullptr;
+  uint32_t gen = (COOP && threadIdx.x == 0) ? g_load(bar + kBarGen) : 0u;   // see row_barrier
 
   int nsplit = 0;   // split rows this slot has finished: picks the workspace region parity
   for (int it = 0;; ++it) {
@@ -468,16 +491,20 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
       for (int b = tid; b < nb; b += kThreads) sh_hist[b] = 0;
       __syncthreads();
       launder(key);
-      if (pass == 0) hist_pass0<E>(key, need, sh_hist, sh_scan, sh_var, tid);
+      // Pass 0 of a split row pushes only bins >= t_s: the row has at least
+      // `need` keys at or above t_s, so its threshold bin is >= t_s, and
+      // every bin the merged search can reach is complete.
+      uint32_t push_from = 0;
+      if (pass == 0) push_from = hist_pass0<E>(key, need, sh_hist, sh_scan, sh_var, tid, split);
       else hist_resident<E>(key, pass, prefix, sh_hist);
       __syncthreads();
       if (split) {
         uint32_t* gh = region + (pass == 0 ? kRegHist0 : pass == 1 ? kRegHist1 : kRegHist2);
         for (int b = tid; b < nb; b += kThreads) {
           const uint32_t c = sh_hist[b];
-          if (c) g_add(gh + b, c);
+          if (c && (uint32_t)b >= push_from) g_add(gh + b, c);
         }
-        row_barrier(bar, G, fault, tid);
+        row_barrier(bar, G, g, gen, fault, tid);
         for (int b = tid; b < nb; b += kThreads) sh_hist[b] = g_load(gh + b);
         __syncthreads();
       }
