@@ -101,6 +101,30 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
                              int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
                              hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row);
 
+/*
+ * Deterministic variant of topk_transform (same arguments, layouts, ownership
+ * and errors).  LiteTopk PR #32094 (Notes) points out that the radix top-k
+ * paths return an exact set in an unspecified order, with threshold ties
+ * filled in atomic-arrival order, so they are not usable where a
+ * deterministic result is required.  Here slots [0, n_b) of row b hold the
+ * selected positions in the order of the plain definition: score descending
+ * (the key order: IEEE order with -0 before +0), equal scores by position
+ * ascending; where the threshold value is cut, the positions taken are the
+ * lowest.  The output is therefore unique: the same for every kernel shape,
+ * launch and device state.  out_idx[b, j] is the transform of out_raw[b, j];
+ * slots [n_b, k) are -1.
+ *
+ * Cost: the row is selected as by topk_transform, then read once more from
+ * memory, and the n_b chosen pairs are sorted in LDS (a bitonic network).
+ * Besides the workspace, one 16-byte record per row is kept per (device,
+ * stream) between the two launches; it is allocated on first use (call once
+ * outside graph capture), grown on demand, and freed by
+ * topk_release_workspaces.
+ */
+topk_status_t topk_transform_sorted(const float* scores, const int32_t* seq_lens, const int32_t* page_table,
+                                    int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
+                                    hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row);
+
 /* Static text for a status code (never NULL). */
 const char* topk_status_string(topk_status_t status);
 

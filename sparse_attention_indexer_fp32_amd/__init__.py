@@ -20,7 +20,7 @@ STREAM_SHAPES = 2   # compiled streaming-kernel shapes: topk_set_stream_shape ac
 STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUPPORTED",
           3: "TOPK_ERROR_OUT_OF_MEMORY", 4: "TOPK_ERROR_LAUNCH"}
 
-EXPORTED = ("topk_transform", "topk_status_string", "topk_last_error", "topk_last_launch",
+EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_status_string", "topk_last_error", "topk_last_launch",
             "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape",
             "topk_debug_fault_word", "topk_abi_version")
 
@@ -46,8 +46,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         pass
     lib = ctypes.CDLL(path)
     c_i32, c_i64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
-    lib.topk_transform.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64]
-    lib.topk_transform.restype = ctypes.c_int
+    for fn in (lib.topk_transform, lib.topk_transform_sorted):
+        fn.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64]
+        fn.restype = ctypes.c_int
     lib.topk_status_string.argtypes = [ctypes.c_int]
     lib.topk_status_string.restype = ctypes.c_char_p
     lib.topk_last_error.argtypes = []
@@ -84,10 +85,23 @@ def topk_transform(scores, seq_lens, page_table, k: int, page_size: int, out=Non
     contiguous on one GPU.  Returns (out (B, k) int32, out_raw (B, k) int32 or
     None).  `out` / `out_raw` may be passed preallocated; `want_raw` allocates
     out_raw when it is not passed.  The call is asynchronous on `stream`
-    (default: torch's current stream of the tensors' device).
+    (default: torch's current stream of the tensors' device).  The selected
+    positions of a row come in no particular order.
     """
+    return _call(load().topk_transform, scores, seq_lens, page_table, k, page_size, out, out_raw, want_raw, stream)
+
+
+def topk_transform_sorted(scores, seq_lens, page_table, k: int, page_size: int, out=None, out_raw=None,
+                          want_raw: bool = False, stream=None) -> Tuple[object, Optional[object]]:
+    """As topk_transform, deterministic: each row's selected positions by score
+    descending, equal scores by position ascending, the lowest tied positions
+    taken at the threshold (the plain definition's order)."""
+    return _call(load().topk_transform_sorted, scores, seq_lens, page_table, k, page_size, out, out_raw, want_raw,
+                 stream)
+
+
+def _call(fn, scores, seq_lens, page_table, k, page_size, out, out_raw, want_raw, stream):
     import torch
-    lib = load()
     if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_contiguous():
         raise ValueError("scores must be a contiguous 2-D float32 tensor")
     B, W = scores.shape
@@ -111,7 +125,7 @@ def topk_transform(scores, seq_lens, page_table, k: int, page_size: int, out=Non
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        st = lib.topk_transform(scores.data_ptr(), seq_lens.data_ptr(), page_table.data_ptr(), int(k),
+        st = fn(scores.data_ptr(), seq_lens.data_ptr(), page_table.data_ptr(), int(k),
                                 int(page_size), out.data_ptr(),
                                 out_raw.data_ptr() if out_raw is not None else None,
                                 ctypes.c_void_p(stream.cuda_stream), int(B), int(W), int(page_table.shape[1]))

@@ -33,6 +33,7 @@ struct DeviceInfo {
   bool coop = false;
   int occ[2][topk::kNumEpt] = {};   // [split][ept] resident workgroups per CU
   int stream_occ[topk::kNumStreamVariants] = {};   // streaming kernel shapes: resident workgroups per CU
+  int sorted_occ = 0;               // sorted finish: resident workgroups per CU
   std::string arch;
 };
 
@@ -44,6 +45,7 @@ struct Workspace {
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::map<std::pair<int, hipStream_t>, Workspace> g_meta;   // sorted mode: records + raw positions ("slots" = words)
 int g_override_ept = 0;
 int g_override_wgs = 0;
 int g_stream_variant = -1;   // -1: the default streaming shape
@@ -85,6 +87,8 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
       e = topk::stream_occupancy(v, &info.stream_occ[v]);
       if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     }
+    e = topk::sorted_occupancy(&info.sorted_occ);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   }
   *out = &g_devices.emplace(dev, info).first->second;
   return TOPK_SUCCESS;
@@ -126,6 +130,35 @@ topk_status_t get_workspace(int dev, hipStream_t stream, int64_t slots, uint32_t
   w.slots = slots;
   *ptr = w.ptr;
   *capacity = w.slots;
+  return TOPK_SUCCESS;
+}
+
+// Caller holds g_mu.  Sorted mode's buffer: per-row selection records, then
+// the selection launch's raw positions (batch x k) when the caller passes no
+// out_raw.  Every row is written by the selection launch before the finish
+// reads it, so the buffer needs no clearing.
+topk_status_t get_meta(int dev, hipStream_t stream, int64_t words, uint32_t** ptr) {
+  Workspace& w = g_meta[std::make_pair(dev, stream)];
+  if (w.ptr && w.slots >= words) {
+    *ptr = w.ptr;
+    return TOPK_SUCCESS;
+  }
+  if (w.ptr) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    (void)hipFree(w.ptr);
+    w.ptr = nullptr;
+    w.slots = 0;
+  }
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, (size_t)words * sizeof(uint32_t));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("selection record hipMalloc: ") + hipGetErrorString(e));
+  }
+  w.ptr = static_cast<uint32_t*>(p);
+  w.slots = words;
+  *ptr = w.ptr;
   return TOPK_SUCCESS;
 }
 
@@ -251,13 +284,9 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
   return TOPK_SUCCESS;
 }
 
-}  // namespace
-
-extern "C" {
-
-topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
-                             int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream,
-                             int32_t batch, int64_t width, int64_t pages_per_row) {
+topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
+                            int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream, int32_t batch,
+                            int64_t width, int64_t pages_per_row, bool sorted) {
   t_last_error.clear();
   if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERROR_INVALID_VALUE, "k must be in [1, 2048]");
   if (page_size < 1 || (page_size & (page_size - 1)) != 0)
@@ -306,6 +335,17 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
   a.wgs_per_row = (int32_t)plan.G;
   a.slots = (int32_t)plan.slots;
   a.vec = (width % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
+  a.meta = nullptr;
+  a.sel = nullptr;
+  if (sorted) {
+    // the selection launch always writes raw positions: the caller's out_raw,
+    // else a scratch area after the records
+    const int64_t rec = (int64_t)batch * (int64_t)topk::kMetaWords;
+    st = get_meta(dev, stream, rec + (out_raw ? 0 : (int64_t)batch * k), &a.meta);
+    if (st != TOPK_SUCCESS) return st;
+    if (!out_raw) a.out_raw = reinterpret_cast<int32_t*>(a.meta + rec);
+    a.sel = a.out_raw;
+  }
   if (plan.kind == Kind::kSplit || (plan.kind == Kind::kStream && batch > plan.slots)) {
     // split rows synchronise through per-slot regions; streamed rows beyond
     // the grid are handed out through a counter in the header
@@ -319,13 +359,45 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
   else
     e = topk::launch_rows(plan.ept_idx, plan.kind == Kind::kSplit, a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  char buf[160];
-  std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d",
+  int64_t sorted_slots = 0;
+  if (sorted) {
+    // the finish reads every row's record once the selection launch is done (stream order)
+    topk::KernelArgs f = a;
+    f.out_raw = out_raw;   // the caller's (or none); f.sel holds the selection launch's positions
+    sorted_slots = (int64_t)info->sorted_occ * info->cus;
+    if (sorted_slots > batch) sorted_slots = batch;
+    if (sorted_slots < 1) sorted_slots = 1;
+    f.slots = (int32_t)sorted_slots;
+    f.wgs_per_row = 1;
+    e = topk::launch_sorted_rows(f, stream);
+    if (e != hipSuccess) return hip_fail(e, "sorted finish launch");
+  }
+  char buf[200];
+  std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s",
                 kind_name(plan.kind), plan.kind == Kind::kStream ? 0 : topk::kEptValues[plan.ept_idx],
                 (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G),
-                plan.kind == Kind::kStream ? topk::stream_variant_threads(plan.stream_variant) : topk::kThreads, a.vec);
+                plan.kind == Kind::kStream ? topk::stream_variant_threads(plan.stream_variant) : topk::kThreads, a.vec,
+                sorted ? " + sorted-finish" : "");
   t_last_launch = buf;
   return TOPK_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
+                             int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream,
+                             int32_t batch, int64_t width, int64_t pages_per_row) {
+  return run_transform(scores, seq_lens, page_table, k, page_size, out_idx, out_raw, stream, batch, width,
+                       pages_per_row, false);
+}
+
+topk_status_t topk_transform_sorted(const float* scores, const int32_t* seq_lens, const int32_t* page_table,
+                                    int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
+                                    hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row) {
+  return run_transform(scores, seq_lens, page_table, k, page_size, out_idx, out_raw, stream, batch, width,
+                       pages_per_row, true);
 }
 
 const char* topk_status_string(topk_status_t status) {
@@ -345,11 +417,14 @@ const char* topk_last_launch(void) { return t_last_launch.c_str(); }
 
 topk_status_t topk_release_workspaces(void) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (g_ws.empty()) return TOPK_SUCCESS;
+  if (g_ws.empty() && g_meta.empty()) return TOPK_SUCCESS;
   hipError_t e = hipDeviceSynchronize();
   for (auto& kv : g_ws)
     if (kv.second.ptr) (void)hipFree(kv.second.ptr);
   g_ws.clear();
+  for (auto& kv : g_meta)
+    if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+  g_meta.clear();
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   return TOPK_SUCCESS;
 }

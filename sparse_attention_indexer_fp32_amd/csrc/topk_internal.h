@@ -54,6 +54,9 @@ inline size_t workspace_words(int64_t slots) {
   return kHdrWords + (size_t)slots * kBarWords + (size_t)slots * 2 * kRegionWords;
 }
 
+// Sorted mode: per-row selection record (prefix, shift, need, floor, cut).
+constexpr size_t kMetaWords = 8;
+
 struct KernelArgs {
   const float* scores;        // (batch, width)
   const int32_t* seq_lens;    // (batch,)
@@ -70,6 +73,8 @@ struct KernelArgs {
   int32_t slots;              // S: rows in flight; grid = S * G
   int32_t ws_slots;           // slots the workspace was laid out for (>= slots)
   int32_t vec;                // rows are 16-byte aligned: use dwordx4 loads
+  uint32_t* meta;             // (batch, kMetaWords): how each row's selection ended, for the sorted finish; or nullptr
+  const int32_t* sel;         // sorted finish: (batch, k) raw positions the selection launch wrote
 };
 
 // ept_index selects kEptValues[ept_index]; coop selects the cross-workgroup
@@ -84,5 +89,11 @@ constexpr int kNumStreamVariants = 2;
 hipError_t launch_stream_rows(int variant, const KernelArgs& args, hipStream_t stream);
 hipError_t stream_occupancy(int variant, int* blocks_per_cu);
 int stream_variant_threads(int variant);
+
+// Sorted finish (deterministic mode): one workgroup per row, persistent over
+// rows (grid = slots); reads the per-row records a selection launch left in
+// `meta` and rewrites the row's outputs in canonical order.
+hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream);
+hipError_t sorted_occupancy(int* blocks_per_cu);
 
 }  // namespace topk

@@ -274,6 +274,23 @@ __device__ __forceinline__ void write_row_output(const KernelArgs& a, int64_t ro
   }
 }
 
+// Records how a row's selection ended, for the sorted finish: every key x of
+// the row with x >= floor and (x >> shift) > prefix was selected, and `need`
+// of the `cnt` with (x >> shift) == prefix.  When cnt == need (the bin is not
+// cut) the selected set is the canonical one, whatever the order.  shift 32
+// with floor 0 and prefix 0 selects every position below the row's length
+// (rows with L <= k).  Called by one thread.
+__device__ __forceinline__ void record_selection(const KernelArgs& a, int64_t row, uint32_t prefix, int shift,
+                                                 uint32_t need, uint32_t cnt, uint32_t floor) {
+  if (a.meta == nullptr) return;
+  uint32_t* m = a.meta + row * kMetaWords;
+  m[0] = prefix;
+  m[1] = (uint32_t)shift;
+  m[2] = need;
+  m[3] = floor;
+  m[4] = cnt != need ? 1u : 0u;
+}
+
 // Histogram of one radix digit over the register-resident keys that match the
 // prefix of the previous digits.
 // Register slots per thread that form the pass-0 sample (see hist_pass0).
@@ -340,9 +357,12 @@ __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass
 // 10-bit digits, then writes the strictly-greater keys to slots
 // [gt_base, n - need_final) and `need_final` keys of the final bin to
 // [n - need_final, n).
+// On return (prefix, shift, cnt, need) describe the final bin: every
+// candidate with (key >> shift) == prefix is of it, cnt of them, `need` of
+// them were selected.
 template <int NT>
-__device__ __forceinline__ void select_candidates(int ncand, uint32_t prefix, int shift, uint32_t cnt,
-                                                  uint32_t need, uint32_t gt_base, uint32_t n,
+__device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, int& shift, uint32_t& cnt,
+                                                  uint32_t& need, uint32_t gt_base, uint32_t n,
                                                   uint32_t* sh_hist, const uint32_t* sh_ckey,
                                                   const int32_t* sh_cpos, int32_t* sh_raw, uint32_t* sh_scan,
                                                   uint32_t* sh_var, int tid) {
@@ -459,6 +479,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     const int n = L < (int64_t)k ? (int)L : k;
     if (L <= (int64_t)k) {  // every valid position is selected (uniform over the row's workgroups)
       if (g == 0) write_row_output<kThreads>(a, row, L, n, true, sh_raw, tid);
+      if (g == 0 && tid == 0) record_selection(a, row, 0u, 32, (uint32_t)n, (uint32_t)n, 0u);
       continue;
     }
     constexpr bool split = COOP;   // the host launches the split kernel only with G > 1
@@ -587,6 +608,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     if (!split) {
       __syncthreads();
       write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid);
+      if (tid == 0) record_selection(a, row, prefix, shift, need, cnt, 1u);
       continue;
     }
 
@@ -615,6 +637,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     }
     __syncthreads();
     write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid);
+    if (tid == 0) record_selection(a, row, prefix, shift, need, cnt, 1u);
     // leave the region zeroed for the row this slot handles two iterations on
     for (int b = tid; b < kBinsWide; b += kThreads) g_store(region + kRegHist0 + b, 0u);
     for (int b = tid; b < kBinsNarrow; b += kThreads) {
@@ -909,6 +932,7 @@ stream_rows_kernel(KernelArgs a) {
         const uint32_t nx = queue != nullptr ? grid + g_add_ret(queue, 1u) : row + grid;
         sh_next_row = nx;
         sh_next_len = nx < (uint32_t)a.batch ? a.seq_lens[nx] : 0;
+        record_selection(a, row, 0u, 32, (uint32_t)n, (uint32_t)n, 0u);
       }
       write_row_output<NT>(a, row, L64, n, true, sh_raw, tid);
       __syncthreads();
@@ -1035,8 +1059,11 @@ stream_rows_kernel(KernelArgs a) {
     for (int j = tid; j < k; j += NT) sh_raw[j] = -1;   // the 12-bit histogram is done with
     __syncthreads();
     if (!overflow) {
-      select_candidates<NT>((int)count, t0, 20, cnt0, (uint32_t)n - gt0, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
+      uint32_t fprefix = t0, fneed = (uint32_t)n - gt0, fcnt = cnt0;
+      int fshift = 20;
+      select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
                             sh_raw, sh_scan, sh_var, tid);
+      if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, gate);
     } else {
       uint32_t prefix = t0, need = (uint32_t)n - gt0, cnt = cnt0;
       int shift = 20;
@@ -1063,6 +1090,7 @@ stream_rows_kernel(KernelArgs a) {
       if (collect)
         select_candidates<NT>((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist,
                               sh_ckey, sh_cpos, sh_raw, sh_scan, sh_var, tid);
+      if (tid == 0) record_selection(a, row, prefix, shift, need, cnt, floor);
     }
     // the candidate list is free again: it holds the page-table row
     int32_t* const sh_pt = reinterpret_cast<int32_t*>(sh_ckey);
@@ -1089,6 +1117,226 @@ stream_rows_kernel(KernelArgs a) {
       g_store(queue, 0u);
       g_store(a.ws + kHdrRowExit, 0u);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sorted finish (deterministic mode).
+//
+// A selection launch recorded, per row, how its threshold ended
+// (record_selection).  This kernel streams the row once more and rewrites the
+// row's outputs in the canonical order: key descending, equal keys by position
+// ascending, and where the threshold bin is cut, the tied positions taken are
+// the lowest.  That is the order the plain definition gives (sort by key
+// descending, then position ascending, take the first n), so the output is
+// unique: equal for every kernel shape, every run.
+//
+// Per row: when the record says the final bin was not cut, the selection
+// launch's positions (`sel`) are already the canonical set: their keys are
+// gathered from the row and the pairs sorted, with no second read of the row.
+// Otherwise the keys above the final bin (exactly n - need of them) go to
+// sh_sort; the bin's members go to a tie list.  When the bin holds more than
+// `need`, the `need` lowest positions are found by an MSB-first radix select
+// on v = ~position (the largest v are the lowest positions; positions are
+// distinct, so it ends with the bin holding exactly what is needed).  If more
+// members than the tie list holds, the same select runs over the row in
+// memory.  The n chosen (key, ~position) pairs are then bitonic-sorted in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kSortTieCap = 4096;
+constexpr int kSortCV = 4;   // float4 groups per thread per streamed chunk
+
+// One pass over the row for the memory fallback of the tie select: with
+// `collect` false, histograms the digit of v = ~position at dshift (12 bits
+// at dshift 20, else 10) of the bin members whose v >> (vshift) == vprefix
+// (vshift 32: all); with `collect` true, appends the members with
+// v >> vshift >= vprefix to sh_sort from slot `base` on.
+__device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp, uint32_t L, bool vec,
+                                                uint32_t prefix, int shift, uint32_t floor, uint32_t vprefix,
+                                                int vshift, int dshift, uint32_t* sh_hist, uint64_t* sh_sort,
+                                                uint32_t base, uint32_t* sh_var, int tid) {
+  constexpr uint32_t span = (uint32_t)kThreads * 4u * kSortCV;
+  for (uint32_t c = 0; c < L; c += span) {
+    uint32_t raw[4 * kSortCV];
+    load_raw<kThreads, kSortCV>(raw, rowp, c, L, vec, tid);
+#pragma unroll
+    for (int j = 0; j < 4 * kSortCV; ++j) {
+      const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3);
+      if (pos >= L) continue;
+      const uint32_t x = order_key_bits(raw[j]);
+      if (x < floor || ((uint64_t)x >> shift) != (uint64_t)prefix) continue;
+      const uint32_t v = ~pos;
+      const uint32_t vp = vshift >= 32 ? 0u : v >> vshift;
+      if (!collect) {
+        if (vshift >= 32 || vp == vprefix) atomicAdd(&sh_hist[(v >> dshift) & (dshift == 20 ? 4095u : 1023u)], 1u);
+      } else if (vp >= vprefix) {
+        const uint32_t s = base + atomicAdd(&sh_var[2], 1u);
+        if (s < (uint32_t)kMaxK) sh_sort[s] = ((uint64_t)x << 32) | (uint64_t)v;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
+  __shared__ uint64_t sh_sort[kMaxK];        // (key << 32) | ~position of the selected
+  __shared__ uint32_t sh_tk[kSortTieCap];    // threshold-bin members: key
+  __shared__ uint32_t sh_tp[kSortTieCap];    //                        position
+  __shared__ uint32_t sh_hist[kBinsWide];
+  __shared__ uint32_t sh_scan[64];
+  __shared__ uint32_t sh_var[16];
+  constexpr uint32_t span = (uint32_t)kThreads * 4u * kSortCV;
+  const int64_t W = a.width;
+  const int k = a.k;
+  const bool vec = a.vec != 0;
+  for (int64_t row = blockIdx.x; row < a.batch; row += gridDim.x) {
+    const int tid = opaque_tid();
+    const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+    const uint32_t L = sl < 0 ? 0u : ((int64_t)sl > W ? (uint32_t)W : (uint32_t)sl);
+    const uint32_t n = L < (uint32_t)k ? L : (uint32_t)k;
+    const uint32_t* m = a.meta + row * kMetaWords;
+    const uint32_t prefix = uniform(m[0]);
+    const int shift = (int)uniform(m[1]);
+    const uint32_t need = uniform(m[2]);
+    const uint32_t floor = uniform(m[3]);
+    const bool cut = uniform(m[4]) != 0u;
+    const float* rowp = a.scores + row * W;
+    if (tid < 16) sh_var[tid] = 0;
+    for (int i = tid; i < kMaxK; i += kThreads) sh_sort[i] = 0ull;   // unfilled slots read as no position
+    __syncthreads();
+    if (!cut) {
+      const int32_t* sel = a.sel + row * (int64_t)k;
+      for (uint32_t j = (uint32_t)tid; j < n; j += kThreads) {
+        const int32_t p = sel[j];
+        if (p >= 0 && (uint32_t)p < L) {
+          const uint32_t x = order_key_bits(__float_as_uint(rowp[p]));
+          sh_sort[j] = ((uint64_t)x << 32) | (uint64_t)(~(uint32_t)p);
+        }
+      }
+      __syncthreads();
+    } else {
+      // 1. keys above the bin -> sh_sort; the bin's members -> tie list
+      for (uint32_t c = 0; c < L; c += span) {
+        uint32_t raw[4 * kSortCV];
+        load_raw<kThreads, kSortCV>(raw, rowp, c, L, vec, tid);
+#pragma unroll
+        for (int j = 0; j < 4 * kSortCV; ++j) {
+          const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3);
+          if (pos >= L) continue;
+          const uint32_t x = order_key_bits(raw[j]);
+          if (x < floor) continue;
+          const uint64_t xp = (uint64_t)x >> shift;
+          if (xp > (uint64_t)prefix) {
+            const uint32_t s = atomicAdd(&sh_var[0], 1u);
+            if (s < (uint32_t)kMaxK) sh_sort[s] = ((uint64_t)x << 32) | (uint64_t)(~pos);
+          } else if (xp == (uint64_t)prefix) {
+            const uint32_t t = atomicAdd(&sh_var[1], 1u);
+            if (t < (uint32_t)kSortTieCap) {
+              sh_tk[t] = x;
+              sh_tp[t] = pos;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t ngt = uniform(sh_var[0]);
+      const uint32_t nties = uniform(sh_var[1]);
+      const uint32_t base = ngt < n ? ngt : n;
+      const bool in_lds = nties <= (uint32_t)kSortTieCap;
+
+      // 2. which bin members: all, or the `need` lowest positions
+      uint32_t vprefix = 0;
+      int vshift = 32;
+      if (nties > need) {
+        uint32_t vneed = need;
+        for (int level = 0; level < 3; ++level) {
+          const int dshift = level == 0 ? 20 : (level == 1 ? 10 : 0);
+          const int nb = level == 0 ? kBinsWide : kBinsNarrow;
+          for (int b = tid; b < nb; b += kThreads) sh_hist[b] = 0;
+          __syncthreads();
+          if (in_lds) {
+            for (uint32_t i = (uint32_t)tid; i < nties; i += kThreads) {
+              const uint32_t v = ~sh_tp[i];
+              if (vshift >= 32 || (v >> vshift) == vprefix)
+                atomicAdd(&sh_hist[(v >> dshift) & (level == 0 ? 4095u : 1023u)], 1u);
+            }
+            __syncthreads();
+          } else {
+            sorted_tie_pass(false, rowp, L, vec, prefix, shift, floor, vprefix, vshift, dshift, sh_hist, sh_sort, 0u,
+                            sh_var, tid);
+          }
+          uint32_t bin, gtc, cnt;
+          if (level == 0) find_threshold<kThreads, kBinsWide>(sh_hist, vneed, sh_scan, sh_var, tid);
+          else find_threshold<kThreads, kBinsNarrow>(sh_hist, vneed, sh_scan, sh_var, tid);
+          bin = uniform(sh_var[0]);
+          gtc = uniform(sh_var[1]);
+          cnt = uniform(sh_var[2]);
+          vneed -= gtc;
+          vprefix = level == 0 ? bin : ((vprefix << 10) | bin);
+          vshift = dshift;
+          if (cnt == vneed) break;   // positions are distinct: at the last digit the bin holds one
+        }
+      }
+
+      // 3. the chosen members join sh_sort after the keys above the bin
+      if (tid == 0) sh_var[2] = 0;
+      __syncthreads();
+      if (in_lds) {
+        for (uint32_t i = (uint32_t)tid; i < nties; i += kThreads) {
+          const uint32_t v = ~sh_tp[i];
+          if (vshift >= 32 || (v >> vshift) >= vprefix) {
+            const uint32_t s = base + atomicAdd(&sh_var[2], 1u);
+            if (s < (uint32_t)kMaxK) sh_sort[s] = ((uint64_t)sh_tk[i] << 32) | (uint64_t)v;
+          }
+        }
+        __syncthreads();
+      } else {
+        sorted_tie_pass(true, rowp, L, vec, prefix, shift, floor, vprefix, vshift, 0, sh_hist, sh_sort, base, sh_var,
+                        tid);
+      }
+
+    }
+
+    // 4. bitonic sort, descending, over the next power of two >= n (pads are 0)
+    uint32_t P = 1;
+    while (P < n) P <<= 1;
+    for (uint32_t size = 2; size <= P; size <<= 1) {
+      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+        for (uint32_t i = (uint32_t)tid; i < P / 2; i += kThreads) {
+          const uint32_t lo = 2 * i - (i & (stride - 1));
+          const uint32_t hi = lo + stride;
+          const bool desc = (lo & size) == 0;
+          const uint64_t x = sh_sort[lo], y = sh_sort[hi];
+          if ((x < y) == desc) {
+            sh_sort[lo] = y;
+            sh_sort[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+
+    // 5. output, transformed through the page table
+    {
+      const int s = a.log2_page;
+      const uint32_t pmask = (1u << s) - 1u;
+      int32_t* o = a.out + row * (int64_t)k;
+      int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
+      const int32_t* pt = a.page_table + row * a.pages_per_row;
+      for (int j = tid; j < k; j += kThreads) {
+        int32_t r = -1, v = -1;
+        if ((uint32_t)j < n) {
+          const uint32_t p = ~(uint32_t)sh_sort[j];
+          if (p < L) {
+            r = (int32_t)p;
+            const int64_t pg = (int64_t)(p >> s);
+            if (pg < a.pages_per_row) v = (int32_t)(((uint32_t)pt[pg] << s) | (p & pmask));
+          }
+        }
+        o[j] = v;
+        if (orw) orw[j] = r;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -1167,6 +1415,16 @@ hipError_t launch_stream_rows(int variant, const KernelArgs& args, hipStream_t s
 }
 
 hipError_t stream_occupancy(int variant, int* blocks_per_cu) { return occupancy_stream_variant(variant, blocks_per_cu); }
+
+hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL(sorted_rows_kernel, dim3((unsigned)args.slots), dim3(kThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t sorted_occupancy(int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(&sorted_rows_kernel),
+                                                      kThreads, 0);
+}
 
 int stream_variant_threads(int variant) {
   switch (variant) {

@@ -1,0 +1,103 @@
+"""GPU parity of the deterministic entry point (topk_transform_sorted).
+
+Its output is unique -- the plain definition's order: key descending, equal
+keys by position ascending, the lowest tied positions taken at the threshold
+-- so both outputs are compared with the oracle's slot for slot, bit-exact,
+through every kernel shape that can do the selection.
+"""
+import numpy as np
+import pytest
+
+import sparse_attention_indexer_fp32_amd as topk
+import workloads
+from gpu_util import SENTINEL, note, upload
+from oracle import topk_transform as oracle_topk
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sorted(lib, w, raw=True, tensors=None):
+    import torch
+    s, sl, pt = tensors if tensors is not None else upload(w)
+    out = torch.full((w.batch, w.k), SENTINEL, dtype=torch.int32, device=s.device)
+    out_raw = torch.full((w.batch, w.k), SENTINEL, dtype=torch.int32, device=s.device) if raw else None
+    lib.topk_transform_sorted(s, sl, pt, w.k, w.page_size, out=out, out_raw=out_raw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (out_raw.cpu().numpy() if raw else None)
+
+
+def check_exact(w, out, raw, rows=None):
+    exp_out, exp_raw, _ = oracle_topk(w.scores, w.seq_lens, w.page_table, w.k, w.page_size, rows=rows)
+    got_out = out if rows is None else out[rows]
+    bad = np.nonzero((got_out != exp_out).any(axis=1))[0]
+    assert bad.size == 0, f"{w.name}: out differs from the oracle in {bad.size} rows (first {bad[:5].tolist()})"
+    if raw is not None:
+        got_raw = raw if rows is None else raw[rows]
+        bad = np.nonzero((got_raw != exp_raw).any(axis=1))[0]
+        assert bad.size == 0, f"{w.name}: raw differs from the oracle in {bad.size} rows (first {bad[:5].tolist()})"
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c3_b4", "c4b", "c5"])
+def test_sorted_configs(lib, name):
+    note(f"sorted config {name}")
+    w = workloads.make(name)
+    lib.topk_set_dispatch_override(0, 0)
+    t = upload(w)
+    out, raw = run_sorted(lib, w, raw=True, tensors=t)
+    note(f"sorted config {name}: {lib.topk_last_launch()}")
+    check_exact(w, out, raw)
+    out2, _ = run_sorted(lib, w, raw=False, tensors=t)
+    assert np.array_equal(out2, out)
+
+
+def test_sorted_c4a_sampled(lib):
+    note("sorted config c4a")
+    w = workloads.c4a()
+    lib.topk_set_dispatch_override(0, 0)
+    out, raw = run_sorted(lib, w, raw=True)
+    note(f"sorted config c4a: {lib.topk_last_launch()}")
+    rng = np.random.Generator(np.random.PCG64(78))
+    rows = sorted(rng.choice(w.batch, size=192, replace=False).tolist())
+    check_exact(w, out, raw, rows=rows)
+
+
+# every selection path: both streaming shapes, split rows, register-resident rows
+SORTED_SHAPES = [("stream", 0, 1, 0), ("stream", 0, 1, 1), ("split", 4, 3, -1), ("split", 16, 0, -1),
+                 ("resident", 16, 1, -1), ("resident", 64, 1, -1)]
+
+
+@pytest.mark.parametrize("path,ept,wgs,shape", SORTED_SHAPES)
+@pytest.mark.parametrize("kind", ["normal", "ties", "const", "asc", "desc", "neginf", "int"])
+def test_sorted_every_path(lib, path, ept, wgs, shape, kind):
+    """Adversarial kinds drive the streaming kernel through its gate raise,
+    overflow and low-count fallbacks, and the finish through its memory tie
+    select (constant rows have more tied members than its LDS list)."""
+    W = 3 * 4096 + 123 if path != "stream" else 50001
+    seq = [W, W - 1, W // 3, 2049, 5000, 0, 513, -2]
+    for k in (1, 700, 2048):
+        w = workloads.custom(300 + ept + wgs + k, len(seq), W, k, 16, seq_lens=seq, kind=kind, table="perm")
+        note(f"sorted path={path} ept={ept} wgs={wgs} shape={shape} kind={kind} k={k}")
+        lib.topk_set_dispatch_override(ept, wgs)
+        lib.topk_set_stream_shape(shape)
+        try:
+            out, raw = run_sorted(lib, w, raw=True)
+        finally:
+            lib.topk_set_dispatch_override(0, 0)
+            lib.topk_set_stream_shape(-1)
+        check_exact(w, out, raw)
+
+
+def test_sorted_matches_unsorted_set(lib):
+    """Same selected set as topk_transform wherever the threshold is not cut
+    (distinct scores: the set is unique), in canonical order."""
+    w = workloads.custom(17, 64, 20000, 512, 64, kind="normal")
+    t = upload(w)
+    import torch
+    s, sl, pt = t
+    o1, r1 = lib.topk_transform(s, sl, pt, w.k, w.page_size, want_raw=True)
+    o2, r2 = lib.topk_transform_sorted(s, sl, pt, w.k, w.page_size, want_raw=True)
+    torch.cuda.synchronize()
+    r1, r2 = r1.cpu().numpy(), r2.cpu().numpy()
+    for b in range(w.batch):
+        assert np.array_equal(np.sort(r1[b]), np.sort(r2[b]))
+    check_exact(w, o2.cpu().numpy(), r2)
