@@ -54,8 +54,9 @@ def test_abi_version_and_status_strings(lib):
     (2048, 1, 0, 0, 0, 0),
     (16, 64, 3, 16, 1, 1),         # null pointers with batch > 0
 ])
-def test_argument_validation_without_device(lib, k, ps, batch, width, pages, expect):
-    st = lib.topk_transform(None, None, None, k, ps, None, None, None, batch, width, pages)
+@pytest.mark.parametrize("entry", ["topk_transform", "topk_transform_sorted"])
+def test_argument_validation_without_device(lib, entry, k, ps, batch, width, pages, expect):
+    st = getattr(lib, entry)(None, None, None, k, ps, None, None, None, batch, width, pages)
     assert st == expect, topk.topk_last_error()
     if expect:
         assert topk.topk_last_error()
