@@ -202,15 +202,15 @@ const char* kind_name(Kind k) {
 //              from a sample; persistent over rows (a queue hands out the rows
 //              beyond the grid).  Used from half a row per CU up (measured on
 //              MI355X: at 128 rows of 128K it beats the split kernel by a
-//              quarter), or when rows are short.  The 256-thread shape (four
+//              quarter).  The 256-thread shape (four
 //              workgroups per CU) when the batch fills its slots and k <= 512
 //              (its 1920-entry list holds the ~2k keys such rows pass), else
 //              the 1024-thread shape.
 //  * split:    G workgroups per row holding the row in registers, merged
 //              through global atomics and a per-row barrier; for fewer, long
 //              rows.  Picks the smallest E whose grid still fits resident.
-//  * resident: one workgroup per row holding the row in registers (testing
-//              and tuning override only).
+//  * resident: one workgroup per row holding the row in registers; for
+//              fewer than half a row per CU of width <= 16K.
 topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, int32_t k, Plan* plan) {
   const int64_t B = batch;
   const int64_t Wc = width > 0 ? width : 1;
@@ -238,8 +238,16 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
       plan->G = G;
       plan->kind = G > 1 ? Kind::kSplit : Kind::kResident;
     }
-  } else if (2 * B >= dev.cus || B >= stream_slots || Wc <= 16384) {
+  } else if (2 * B >= dev.cus || B >= stream_slots) {
     plan->kind = Kind::kStream;
+  } else if (Wc <= (int64_t)topk::kThreads * 16) {
+    // few short rows: one workgroup each, the row in registers (1 x 16K, k 512:
+    // 10.2 us against 12.6 us streamed)
+    int idx = 0;
+    while (idx < topk::kNumEpt - 1 && (int64_t)topk::kThreads * topk::kEptValues[idx] < Wc) ++idx;
+    plan->ept_idx = idx;
+    plan->G = 1;
+    plan->kind = Kind::kResident;
   } else {
     // Smallest E whose grid fits resident with at most kMaxSplitWgs
     // workgroups per row: each extra workgroup adds histogram pushes and
