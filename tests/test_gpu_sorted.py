@@ -67,11 +67,12 @@ SORTED_SHAPES = [("stream", 0, 1, 0), ("stream", 0, 1, 1), ("split", 4, 3, -1), 
 
 
 @pytest.mark.parametrize("path,ept,wgs,shape", SORTED_SHAPES)
-@pytest.mark.parametrize("kind", ["normal", "ties", "const", "asc", "desc", "neginf", "int"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "const", "asc", "desc", "neginf", "int", "zeros", "wide"])
 def test_sorted_every_path(lib, path, ept, wgs, shape, kind):
     """Adversarial kinds drive the streaming kernel through its gate raise,
     overflow and low-count fallbacks, and the finish through its memory tie
-    select (constant rows have more tied members than its LDS list)."""
+    select (constant rows have more tied members than its LDS list); "zeros"
+    orders -0 before +0, "wide" mixes subnormals and infinities."""
     W = 3 * 4096 + 123 if path != "stream" else 50001
     seq = [W, W - 1, W // 3, 2049, 5000, 0, 513, -2]
     for k in (1, 700, 2048):
