@@ -1,13 +1,15 @@
 // C-ABI layer of the fused top-k + page-table transform: argument checks,
 // device checks, the dispatcher that picks a kernel shape from the host-known
 // (batch, width, k) and the device's resident-workgroup capacity, and the
-// per-(device, stream) workspace the split-row kernel synchronises through.
+// per-(device, stream) buffers: the workspace the split-row kernel
+// synchronises through (also the streaming kernel's row queue), and the sorted
+// mode's per-row records.
 //
 // Dispatch follows the pages' lesson that the path must depend on batch and
 // length (SGLang PR #26788 commit notes: one block per row at large batch,
 // several cooperating blocks per row for long rows at small batch), with the
-// thresholds set for MI355X: 256 CUs, 1024-thread workgroups, rows held in
-// VGPRs at 4..64 elements per thread.
+// thresholds measured on MI355X (256 CUs): streaming from half a row per CU
+// up, register-resident rows for a few short ones, split rows otherwise.
 
 #include <hip/hip_runtime_api.h>
 

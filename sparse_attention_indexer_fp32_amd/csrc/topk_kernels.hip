@@ -27,6 +27,13 @@
 //   * Selected positions go to a staging list (LDS, or global when the row is
 //     split); after a barrier one pass gathers the page-table entries and
 //     writes out_idx / out_raw coalesced, -1 padded.
+//   * Large batches stream instead (stream_rows_kernel): one workgroup per
+//     row, a gate set from a sample of the row, the keys at or above it
+//     appended to an LDS candidate list while the rest of the row streams
+//     past in two register-held chunks; the radix digits then run on the
+//     list.  Rows past the grid come from a ticket queue.
+//   * The deterministic entry point adds a second launch (sorted_rows_kernel)
+//     that puts each row's selection in the plain definition's order.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -650,23 +657,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming one-workgroup-per-row kernel (large batches).
-//
-// Holding a 64K row in registers leaves one row per CU and nothing to overlap
-// its radix passes with; streaming keeps two rows in flight per CU instead.
-//   1. Sample: the first kStreamSample positions (16 keys per thread) are
-//      histogrammed in full; the sample's threshold bin is a gate such that at
-//      least n keys of the row lie at or above it.
-//   2. Stream: every key at or above the gate is counted (so the histogram is
-//      exact for every bin >= gate) and appended to an LDS candidate list;
-//      slots come from wave ballots, one LDS atomic per wave per chunk.  When
-//      the list fills, the gate is raised to the threshold bin of the keys
-//      seen so far (still a valid lower bound) and the list is compacted.
-//   3. The threshold bin comes from the exact histogram; the remaining digits
-//      run on the candidates only.
-// If the list overflows anyway (adversarial rows: a single bin holding more
-// keys than the list), the row is redone by re-streaming it from memory with
-// one more digit per pass until the threshold bin fits (exact, slower).
+// Helpers of the streaming kernel (stream_rows_kernel, below).
 // ---------------------------------------------------------------------------
 
 // Stream-kernel LDS words (sh_var indices).
