@@ -367,12 +367,14 @@ __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass
 // On return (prefix, shift, cnt, need) describe the final bin: every
 // candidate with (key >> shift) == prefix is of it, cnt of them, `need` of
 // them were selected.
+// With `fill`, slots [0, n) of sh_raw are first set to -1 (nothing else
+// has written them yet).
 template <int NT>
 __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, int& shift, uint32_t& cnt,
                                                   uint32_t& need, uint32_t gt_base, uint32_t n,
                                                   uint32_t* sh_hist, const uint32_t* sh_ckey,
                                                   const int32_t* sh_cpos, int32_t* sh_raw, uint32_t* sh_scan,
-                                                  uint32_t* sh_var, int tid) {
+                                                  uint32_t* sh_var, int tid, bool fill = false) {
   while (shift > 0 && cnt != need) {
     for (int b = tid; b < kBinsNarrow; b += NT) sh_hist[b] = 0;
     __syncthreads();
@@ -394,6 +396,8 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, i
     sh_var[8] = gt_base;
     sh_var[9] = 0;
   }
+  if (fill)
+    for (uint32_t j = (uint32_t)tid; j < n; j += NT) sh_raw[j] = -1;
   __syncthreads();
   for (int i = tid; i < ncand; i += NT) {
     const uint32_t x = sh_ckey[i] >> shift;
@@ -445,8 +449,9 @@ __device__ __forceinline__ void load_raw(uint32_t (&raw)[4 * V], const float* ro
 // Order key of raw slot j of a chunk at cbase, or 0 ("no element") past L.
 template <int NT>
 __device__ __forceinline__ uint32_t slot_key(uint32_t raw, int j, uint32_t cbase, uint32_t L, int tid) {
-  const int64_t lim = (int64_t)L - (int64_t)cbase - (int64_t)((j >> 2) * NT * 4 + (j & 3));   // a scalar
-  return ((int64_t)(tid * 4) < lim) ? order_key_bits(raw) : 0u;
+  // a scalar; L and cbase are below 2^31 (widths fit int32, cbase <= L + a chunk)
+  const int32_t lim = (int32_t)L - (int32_t)cbase - (int32_t)((j >> 2) * NT * 4 + (j & 3));
+  return (tid * 4 < lim) ? order_key_bits(raw) : 0u;
 }
 
 template <int NT, int V>
@@ -1011,7 +1016,9 @@ stream_rows_kernel(KernelArgs a) {
         gate = raise_gate<NT, CAP>(gate, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_scan, sh_var, tid);
     }
     // Every wave's appends are in (the loop's last barrier does this, but a
-    // row that fits in the sample has no loop) before the count is read.
+    // row that fits in the sample has no loop) before the count is read; the
+    // histogram is cleared for the list under the same barrier.
+    for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
     __syncthreads();
     // The next row's length and this row's page table are requested now and
     // first used after the finish below.
@@ -1038,7 +1045,8 @@ stream_rows_kernel(KernelArgs a) {
     const bool overflow = low_count || uniform(sh_var[kVarOverflow]) != 0u || count > (uint32_t)CAP;
     const uint32_t floor = low_count ? 1u : gate;
     if (!overflow) {
-      list_histogram<NT>(count, sh_ckey, sh_hist, tid);
+      for (uint32_t i = (uint32_t)tid; i < count; i += NT) atomicAdd(&sh_hist[sh_ckey[i] >> 20], 1u);
+      __syncthreads();
     } else {
       for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
       __syncthreads();
@@ -1047,15 +1055,17 @@ stream_rows_kernel(KernelArgs a) {
     }
     find_threshold<NT, kBinsWide>(sh_hist, (uint32_t)n, sh_scan, sh_var, tid);
     const uint32_t t0 = uniform(sh_var[0]), gt0 = uniform(sh_var[1]), cnt0 = uniform(sh_var[2]);
-    for (int j = tid; j < k; j += NT) sh_raw[j] = -1;   // the 12-bit histogram is done with
-    __syncthreads();
+    // From here the 12-bit histogram is done with: its upper half holds the
+    // selected positions (-1 filled before they are written).
     if (!overflow) {
       uint32_t fprefix = t0, fneed = (uint32_t)n - gt0, fcnt = cnt0;
       int fshift = 20;
       select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                            sh_raw, sh_scan, sh_var, tid);
+                            sh_raw, sh_scan, sh_var, tid, true);
       if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, gate);
     } else {
+      for (int j = tid; j < k; j += NT) sh_raw[j] = -1;
+      __syncthreads();
       uint32_t prefix = t0, need = (uint32_t)n - gt0, cnt = cnt0;
       int shift = 20;
       while (cnt > (uint32_t)CAP && cnt != need && shift > 0) {
