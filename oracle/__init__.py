@@ -7,6 +7,7 @@ library.
 from .topk_oracle import (RowInfo, order_key, row_length, select_row, topk_transform,
                           topk_transform_row, transform_positions)
 from .check import check_batch, check_row
+from . import indexer_oracle
 
 __all__ = ["RowInfo", "order_key", "row_length", "select_row", "topk_transform", "topk_transform_row",
-           "transform_positions", "check_batch", "check_row"]
+           "transform_positions", "check_batch", "check_row", "indexer_oracle"]
