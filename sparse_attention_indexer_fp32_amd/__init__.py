@@ -4,8 +4,9 @@ Argument marshalling only: every step of the operation runs in the library's
 HIP kernels.  PyTorch supplies device memory and the current stream.  There is
 no fallback: if the library is not built, or the call fails, this raises.
 
-The C entry points have the same names; see include/topk_transform.h for the
-argument meaning, layouts, ownership and error behaviour.
+The C entry points have the same names; see include/topk_transform.h and
+include/indexer_topk.h for the argument meaning, layouts, ownership and error
+behaviour.
 """
 from __future__ import annotations
 
@@ -22,7 +23,9 @@ STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUP
 
 EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_status_string", "topk_last_error", "topk_last_launch",
             "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape",
-            "topk_debug_fault_word", "topk_abi_version")
+            "topk_debug_fault_word", "topk_abi_version", "indexer_logits", "indexer_topk")
+INDEXER_HEADS = 32
+INDEXER_HEAD_DIM = 128
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -65,6 +68,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topk_debug_fault_word.restype = ctypes.c_int
     lib.topk_abi_version.argtypes = []
     lib.topk_abi_version.restype = c_i32
+    lib.indexer_logits.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64]
+    lib.indexer_logits.restype = ctypes.c_int
+    lib.indexer_topk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i64]
+    lib.indexer_topk.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -168,3 +175,64 @@ def topk_debug_fault_word(stream=None) -> int:
 
 def topk_abi_version() -> int:
     return int(load().topk_abi_version())
+
+
+def _indexer_inputs(q, weights, kv, kv_scale, ks, ke):
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be on a GPU")
+    H, D = INDEXER_HEADS, INDEXER_HEAD_DIM
+    if q.dim() != 3 or tuple(q.shape[1:]) != (H, D) or q.dtype != torch.uint8 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous uint8 (fp8 E4M3 codes) tensor of shape (num_q, 32, 128)")
+    nq = q.shape[0]
+    if weights.shape != (nq, H) or weights.dtype != torch.float32 or not weights.is_contiguous() \
+            or weights.device != dev:
+        raise ValueError("weights must be a contiguous float32 tensor of shape (num_q, 32) on q's device")
+    if kv.dim() != 2 or kv.shape[1] != D or kv.dtype != torch.uint8 or not kv.is_contiguous() or kv.device != dev:
+        raise ValueError("kv must be a contiguous uint8 (fp8 E4M3 codes) tensor of shape (num_kv, 128) on q's device")
+    nkv = kv.shape[0]
+    if kv_scale.shape != (nkv,) or kv_scale.dtype != torch.float32 or kv_scale.device != dev:
+        raise ValueError("kv_scale must be a float32 tensor of shape (num_kv,) on q's device")
+    for name, t in (("ks", ks), ("ke", ke)):
+        if t.shape != (nq,) or t.dtype != torch.int32 or t.device != dev:
+            raise ValueError(f"{name} must be an int32 tensor of shape (num_q,) on q's device")
+    return dev, nq, nkv
+
+
+def indexer_logits(q, weights, kv, kv_scale, ks, ke, width: int, out=None, stream=None):
+    """Dense indexer scores: out[r, c] = score of position ks[r] + c (c < ke[r] - ks[r]
+    and c < width); other entries are left as they are.  Returns out (num_q, width) float32."""
+    import torch
+    dev, nq, nkv = _indexer_inputs(q, weights, kv, kv_scale, ks, ke)
+    if out is None:
+        out = torch.empty((nq, int(width)), dtype=torch.float32, device=dev)
+    elif out.shape != (nq, int(width)) or out.dtype != torch.float32 or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous float32 tensor of shape (num_q, width)")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = load().indexer_logits(q.data_ptr(), weights.data_ptr(), kv.data_ptr(), kv_scale.data_ptr(),
+                                   ks.data_ptr(), ke.data_ptr(), out.data_ptr(), ctypes.c_void_p(stream.cuda_stream),
+                                   int(nq), int(nkv), int(width))
+    _check(st)
+    return out
+
+
+def indexer_topk(q, weights, kv, kv_scale, ks, ke, k: int, out=None, stream=None):
+    """Fused indexer scoring + exact top-k: out (num_q, k) int32 absolute key positions,
+    -1 padded, order within a row unspecified."""
+    import torch
+    dev, nq, nkv = _indexer_inputs(q, weights, kv, kv_scale, ks, ke)
+    if out is None:
+        out = torch.empty((nq, int(k)), dtype=torch.int32, device=dev)
+    elif out.shape != (nq, int(k)) or out.dtype != torch.int32 or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous int32 tensor of shape (num_q, k)")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = load().indexer_topk(q.data_ptr(), weights.data_ptr(), kv.data_ptr(), kv_scale.data_ptr(),
+                                 ks.data_ptr(), ke.data_ptr(), int(k), out.data_ptr(),
+                                 ctypes.c_void_p(stream.cuda_stream), int(nq), int(nkv))
+    _check(st)
+    return out

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libtopk_transform.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["topk_kernels.hip", "topk_api.cpp"]
+SOURCES = ["topk_kernels.hip", "topk_api.cpp", "indexer_kernels.hip", "indexer_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -1,0 +1,235 @@
+// C-ABI layer of the indexer scoring and the fused scoring + exact top-k:
+// argument and device checks, the launch shape (workgroups of 8 query rows;
+// the key range split into windows when there are too few row blocks to fill
+// the device), and the per-(device, stream) candidate buffers.  The exact
+// select over the packed candidates is topk_transform with the candidates'
+// positions as a page table of page size 1, so its output is the positions.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "indexer_internal.h"
+#include "indexer_topk.h"
+#include "topk_internal.h"
+
+namespace {
+
+struct Buffers {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<int, int> g_cus;                                   // device -> CUs (gfx950 only)
+std::map<std::pair<int, hipStream_t>, Buffers> g_bufs;
+
+topk_status_t fail(topk_status_t st, const std::string& msg) {
+  topk::set_last_error(msg.c_str());
+  return st;
+}
+
+topk_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(TOPK_ERROR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Caller holds g_mu.  CUs of the current device, or 0 when it is not gfx950.
+topk_status_t device_cus(int* dev_out, int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  *dev_out = dev;
+  auto it = g_cus.find(dev);
+  if (it == g_cus.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = g_cus.emplace(dev, ok ? prop.multiProcessorCount : 0).first;
+    if (!ok) return fail(TOPK_ERROR_UNSUPPORTED, std::string("device ") + prop.gcnArchName + " is not gfx950");
+  }
+  if (it->second == 0) return fail(TOPK_ERROR_UNSUPPORTED, "device is not gfx950");
+  *cus = it->second;
+  return TOPK_SUCCESS;
+}
+
+// Caller holds g_mu.
+topk_status_t get_buffers(int dev, hipStream_t stream, size_t bytes, void** ptr) {
+  Buffers& b = g_bufs[std::make_pair(dev, stream)];
+  if (b.ptr && b.bytes >= bytes) {
+    *ptr = b.ptr;
+    return TOPK_SUCCESS;
+  }
+  if (b.ptr) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    (void)hipFree(b.ptr);
+    b.ptr = nullptr;
+    b.bytes = 0;
+  }
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("indexer candidate buffers hipMalloc: ") + hipGetErrorString(e));
+  }
+  b.ptr = p;
+  b.bytes = bytes;
+  *ptr = p;
+  return TOPK_SUCCESS;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Windows over [0, num_kv): enough (row block, window) workgroups for two per
+// CU, windows of at least 2048 positions, a multiple of 32 each.
+void plan_windows(int64_t num_q, int64_t num_kv, int cus, int32_t* nwin, int64_t* window) {
+  const int64_t blocks = ceil_div(num_q, indexer::rows_per_workgroup());
+  int64_t n = ceil_div(2 * (int64_t)cus, blocks);
+  const int64_t most = ceil_div(num_kv, 2048);
+  if (n > most) n = most;
+  if (n < 1) n = 1;
+  int64_t w = ceil_div(ceil_div(num_kv, n), 32) * 32;
+  if (w < 32) w = 32;
+  *window = w;
+  *nwin = (int32_t)ceil_div(num_kv > 0 ? num_kv : 1, w);
+}
+
+topk_status_t check_common(const uint8_t* q, const float* weights, const uint8_t* kv, const float* kv_scale,
+                           const int32_t* ks, const int32_t* ke, int32_t num_q, int64_t num_kv) {
+  if (num_q < 0 || num_kv < 0) return fail(TOPK_ERROR_INVALID_VALUE, "num_q and num_kv must be >= 0");
+  if (num_kv > (int64_t)INT32_MAX) return fail(TOPK_ERROR_INVALID_VALUE, "num_kv must fit in int32");
+  if (num_q == 0) return TOPK_SUCCESS;
+  if (!q || !weights || !ks || !ke) return fail(TOPK_ERROR_INVALID_VALUE, "q, weights, ks and ke must be non-null");
+  if (num_kv > 0 && (!kv || !kv_scale))
+    return fail(TOPK_ERROR_INVALID_VALUE, "kv and kv_scale must be non-null when num_kv > 0");
+  if ((reinterpret_cast<uintptr_t>(kv) & 15) != 0 || (reinterpret_cast<uintptr_t>(q) & 15) != 0)
+    return fail(TOPK_ERROR_INVALID_VALUE, "q and kv must be 16-byte aligned");
+  return TOPK_SUCCESS;
+}
+
+}  // namespace
+
+namespace indexer {
+
+bool has_buffers() {
+  std::lock_guard<std::mutex> lock(g_mu);
+  return !g_bufs.empty();
+}
+
+void release_buffers() {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto& kv : g_bufs)
+    if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+  g_bufs.clear();
+}
+
+}  // namespace indexer
+
+extern "C" {
+
+topk_status_t indexer_logits(const uint8_t* q, const float* weights, const uint8_t* kv, const float* kv_scale,
+                             const int32_t* ks, const int32_t* ke, float* logits, hipStream_t stream,
+                             int32_t num_q, int64_t num_kv, int64_t logits_stride) {
+  topk::set_last_error("");
+  topk_status_t st = check_common(q, weights, kv, kv_scale, ks, ke, num_q, num_kv);
+  if (st != TOPK_SUCCESS) return st;
+  if (logits_stride < 0) return fail(TOPK_ERROR_INVALID_VALUE, "logits_stride must be >= 0");
+  if (num_q == 0) return TOPK_SUCCESS;
+  if (!logits && logits_stride > 0) return fail(TOPK_ERROR_INVALID_VALUE, "logits must be non-null");
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0, cus = 0;
+  st = device_cus(&dev, &cus);
+  if (st != TOPK_SUCCESS) return st;
+  if (num_kv == 0 || logits_stride == 0) return TOPK_SUCCESS;
+  indexer::ScanArgs a{};
+  a.q = q;
+  a.weights = weights;
+  a.kv = kv;
+  a.kv_scale = kv_scale;
+  a.ks = ks;
+  a.ke = ke;
+  a.num_q = num_q;
+  a.num_kv = num_kv;
+  plan_windows(num_q, num_kv, cus, &a.nwin, &a.window);
+  a.logits = logits;
+  a.logits_stride = logits_stride;
+  hipError_t e = indexer::launch_logits(a, a.nwin, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer logits launch");
+  char buf[160];
+  std::snprintf(buf, sizeof(buf), "indexer-logits grid=%lldx%d window=%lld",
+                (long long)ceil_div(num_q, indexer::rows_per_workgroup()), a.nwin, (long long)a.window);
+  topk::set_last_launch(buf);
+  return TOPK_SUCCESS;
+}
+
+topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t* kv, const float* kv_scale,
+                           const int32_t* ks, const int32_t* ke, int32_t k, int32_t* out_idx, hipStream_t stream,
+                           int32_t num_q, int64_t num_kv) {
+  topk::set_last_error("");
+  if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERROR_INVALID_VALUE, "k must be in [1, 2048]");
+  topk_status_t st = check_common(q, weights, kv, kv_scale, ks, ke, num_q, num_kv);
+  if (st != TOPK_SUCCESS) return st;
+  if (num_q == 0) return TOPK_SUCCESS;
+  if (!out_idx) return fail(TOPK_ERROR_INVALID_VALUE, "out_idx must be non-null");
+  indexer::ScanArgs a{};
+  int64_t row_cap = 0;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0, cus = 0;
+    st = device_cus(&dev, &cus);
+    if (st != TOPK_SUCCESS) return st;
+    a.q = q;
+    a.weights = weights;
+    a.kv = kv;
+    a.kv_scale = kv_scale;
+    a.ks = ks;
+    a.ke = ke;
+    a.num_q = num_q;
+    a.num_kv = num_kv;
+    a.k = k;
+    plan_windows(num_q, num_kv, cus, &a.nwin, &a.window);
+    // a list never holds more than its window; a capacity below the window
+    // leaves room for k entries plus a tile after every trim
+    int64_t cap = 4 * (int64_t)k > 4096 ? 4 * (int64_t)k : 4096;
+    if (cap > a.window) cap = a.window;
+    a.cap = (int32_t)cap;
+    row_cap = (int64_t)a.nwin * k;
+    a.row_cap = row_cap;
+    const size_t lists = (size_t)num_q * a.nwin * (size_t)cap;
+    const size_t packed = (size_t)num_q * (size_t)row_cap;
+    const size_t bytes = lists * 8 + packed * 8 + (size_t)num_q * 4 + 256;
+    void* base = nullptr;
+    st = get_buffers(dev, stream, bytes, &base);
+    if (st != TOPK_SUCCESS) return st;
+    char* p = static_cast<char*>(base);
+    a.cand_score = reinterpret_cast<float*>(p);
+    p += lists * 4;
+    a.cand_pos = reinterpret_cast<int32_t*>(p);
+    p += lists * 4;
+    a.row_score = reinterpret_cast<float*>(p);
+    p += packed * 4;
+    a.row_pos = reinterpret_cast<int32_t*>(p);
+    p += packed * 4;
+    a.row_count = reinterpret_cast<int32_t*>(p);
+    hipError_t e = indexer::launch_scan(a, a.nwin, stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer scan launch");
+  }
+  // exact select over the packed candidates; the positions act as a page
+  // table of page size 1, so out_idx receives them directly
+  st = topk_transform(a.row_score, a.row_count, a.row_pos, k, 1, out_idx, nullptr, stream, num_q, row_cap, row_cap);
+  if (st != TOPK_SUCCESS) return st;
+  char buf[200];
+  std::snprintf(buf, sizeof(buf), "indexer-topk grid=%lldx%d window=%lld cap=%d + select %s",
+                (long long)ceil_div(num_q, indexer::rows_per_workgroup()), a.nwin, (long long)a.window, a.cap,
+                topk_last_launch());
+  topk::set_last_launch(buf);
+  return TOPK_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,446 @@
+// Indexer scoring on gfx950: the step before the top-k (LiteTopk PR #32094
+// "Add LiteTopk fused indexer top-k prefill path for SM100": Summary and the
+// Background list; the Validation section's reference formula).
+//
+//   score[r, j] = s[j] * sum_h w[r, h] * relu(q[r, h, :] . kv[j, :]),
+//   j in row r's key range [ks[r], ke[r]), H = 32 heads of D = 128 (GLM shape).
+//
+// Two kernels share one scoring routine, so they produce the same fp32 value
+// for every (row, position):
+//   * logits_kernel<false> writes the scores densely (row-relative columns):
+//     the dense path whose [rows, length] buffer the fused path avoids;
+//   * logits_kernel<true> is the fused scan: each wave keeps, per row, a
+//     compact candidate list in global memory behind a gate that only
+//     tightens, and the lists are then reduced by the exact top-k.
+//
+// Matrix cores.  q and kv arrive as fp8 E4M3 codes.  gfx950's fp8 matrix
+// instructions sum their products with less than fp32 precision (measured:
+// up to ~2^-12 of the sum of |products| on wide-range inputs), while every
+// E4M3 value is exact in bf16 and the bf16 instruction sums like fp32.  So
+// both operands are widened to bf16 (hardware conversion, exact) and the
+// contraction runs on v_mfma_f32_32x32x16_bf16: M = the 32 heads of one query
+// row, N = 32 key positions, K = 128 in eight steps.  That gives a score
+// within a few fp32 rounding errors of the exact value, at half the fp8 peak.
+//
+// Tiling.  A workgroup of 4 waves owns 8 query rows (2 per wave, their q held
+// in registers as bf16) and a window of key positions.  Key tiles of 32
+// positions are loaded once per workgroup (16 bytes per thread), widened to
+// bf16 into LDS (double-buffered, 16-byte chunks XOR-swizzled by position so
+// the 32 positions a half-wave reads fall in different banks), and read by
+// all four waves.  The epilogue (relu, head weights, the partner half-wave's
+// 16 heads, the position's scale) runs on the accumulator registers.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "indexer_internal.h"
+
+namespace indexer {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kHeads = 32;
+constexpr int kDim = 128;
+constexpr int kTile = 32;             // key positions per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 2;
+constexpr int kRowsPerWg = kWaves * kRowsPerWave;
+constexpr int kTileBytesBf16 = kTile * kDim * 2;   // 8 KB
+constexpr int kHistBins = 2048;
+
+// order key of an fp32 value: unsigned order == value order (-0 below +0)
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// Eight fp8 codes (two dwords) -> eight bf16 values, exact.
+__device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// LDS byte offset of 16-byte chunk c (0..15) of position n's bf16 row.
+__device__ __forceinline__ int tile_offset(int n, int c) { return n * (kDim * 2) + ((c ^ (n & 15)) << 4); }
+
+// A lane's view of one query row: head h = lane % 32 and the half hb = lane / 32
+// of the head dimension it feeds, as bf16, ready for the eight K steps; and
+// the 16 head weights its accumulator rows carry.
+struct RowOperand {
+  bf16x8 a[8];
+  float w[16];
+};
+
+// Step s of the contraction pairs, on both operands, the 8 values
+// d = hb * 64 + s * 8 + (0..7) of the lane's half: every d in [0, 128) is used
+// exactly once, and A and B agree on which d sits in which slot.
+__device__ __forceinline__ void load_row(const uint8_t* q, const float* weights, int64_t row, bool live, int lane,
+                                         RowOperand& op) {
+  const int h = lane & 31, hb = lane >> 5;
+  if (live) {
+    const uint4* src = reinterpret_cast<const uint4*>(q + (row * kHeads + h) * kDim + hb * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = src[i];
+      op.a[2 * i] = widen8(v.x, v.y);
+      op.a[2 * i + 1] = widen8(v.z, v.w);
+    }
+    // accumulator register r of this lane holds head (r / 4) * 8 + hb * 4 + r % 4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) op.w[r] = weights[row * kHeads + (r >> 2) * 8 + hb * 4 + (r & 3)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) op.a[i] = bf16x8{};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) op.w[r] = 0.f;
+  }
+}
+
+// Scores of one query row against the staged tile.  Every lane returns the
+// score of position n = lane % 32 of the tile (both half-waves hold it).
+__device__ __forceinline__ float score_tile(const RowOperand& op, const bf16x8 (&b)[8], float scale) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.a[s], b[s], acc, 0, 0, 0);
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part = fmaf(op.w[r], fmaxf(acc[r], 0.f), part);
+  // the other 16 heads of the same position sit in lane ^ 32
+  const float other = __shfl_xor(part, 32);
+  return (part + other) * scale;
+}
+
+struct RowRange {
+  int64_t lo, hi;   // [lo, hi) of key positions, clamped; hi <= lo when empty
+};
+
+__device__ __forceinline__ RowRange row_range(const ScanArgs& a, int64_t row) {
+  RowRange r{0, 0};
+  if (row < a.num_q) {
+    int64_t lo = a.ks[row], hi = a.ke[row];
+    lo = lo < 0 ? 0 : (lo > a.num_kv ? a.num_kv : lo);
+    hi = hi < 0 ? 0 : (hi > a.num_kv ? a.num_kv : hi);
+    r.lo = lo;
+    r.hi = hi;
+  }
+  return r;
+}
+
+// ---- candidate lists (fused scan) -------------------------------------------------------------
+//
+// Row r's list in window w holds (score, position) pairs at
+// cand_score / cand_pos + ((r * nwin + w) * cap).  The gate is an order key;
+// positions whose key is >= gate are appended.  Invariant: for every position
+// of the window seen so far that is not in the list, the list holds at least
+// k entries whose keys are >= its key -- so the list's top-k is a top-k of
+// everything seen (LiteTopk PR #32094: the threshold only tightens, stays at or
+// below the true k-th best, and a stale gate admits extras but drops nothing).
+
+__device__ __forceinline__ int wave_prefix(uint64_t mask, int lane) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Wave-level: the bin t of hist[0..bins) (bins a multiple of 64) with
+// count(bins > t) < need <= count(bins >= t).  Returns t; *above = count(> t),
+// *in_bin = hist[t].  Requires sum(hist) >= need >= 1.
+__device__ int find_bin(const uint32_t* hist, int bins, uint32_t need, int lane, uint32_t* above, uint32_t* in_bin) {
+  const int per = bins / 64;
+  uint32_t own = 0;
+  for (int i = 0; i < per; ++i) own += hist[lane * per + i];
+  // exclusive suffix sum over lanes (lanes above this one)
+  uint32_t incl = own;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t v = __shfl_down(incl, d);
+    if (lane + d < 64) incl += v;
+  }
+  const uint32_t excl = incl - own;
+  const bool mine = excl < need && need <= incl;
+  const uint64_t m = __ballot(mine);
+  const int src = (int)__builtin_ctzll(m);   // exactly one lane
+  uint32_t t = 0, ab = 0, ib = 0;
+  if (lane == src) {
+    uint32_t acc = excl;
+    for (int i = per - 1; i >= 0; --i) {
+      const uint32_t c = hist[lane * per + i];
+      if (acc + c >= need) {
+        t = (uint32_t)(lane * per + i);
+        ab = acc;
+        ib = c;
+        break;
+      }
+      acc += c;
+    }
+  }
+  *above = (uint32_t)__shfl((int)ab, src);
+  *in_bin = (uint32_t)__shfl((int)ib, src);
+  return __shfl((int)t, src);
+}
+
+__device__ __forceinline__ void clear_hist(uint32_t* hist, int bins, int lane) {
+  for (int i = lane; i < bins; i += 64) hist[i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Histogram of the keys in the list that match `prefix` above bit `lo_bit + width`.
+__device__ void list_hist(const float* sc, int count, uint32_t* hist, int lane, int shift, uint32_t mask,
+                          int match_shift, uint32_t match) {
+  clear_hist(hist, (int)mask + 1 < 64 ? 64 : (int)mask + 1, lane);
+  for (int i = lane; i < count; i += 64) {
+    const uint32_t key = order_key(sc[i]);
+    if (match_shift >= 32 || (key >> match_shift) == match) atomicAdd(&hist[(key >> shift) & mask], 1u);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Shrinks a list of `count` > need entries.  Exact mode keeps every entry
+// whose key is above the need-th largest key T and the first (in list order)
+// of those equal to T, need entries in all, and sets gate = T + 1.  Otherwise,
+// when the 11-bit bin holding the need-th key leaves at most `room` entries at
+// or above its lower edge, it keeps those and sets gate = that edge.  Returns
+// the new count.  The list's earlier stores of this wave are made visible to
+// its loads first.
+__device__ __attribute__((noinline)) int compact_list(float* sc, int32_t* ps, int count, uint32_t need, int room, bool exact_only,
+                            uint32_t* hist, int lane, uint32_t* gate) {
+  __threadfence();
+  uint32_t above = 0, in_bin = 0;
+  list_hist(sc, count, hist, lane, 21, 0x7FF, 32, 0);
+  const uint32_t t1 = (uint32_t)find_bin(hist, 2048, need, lane, &above, &in_bin);
+  uint32_t lo_key;   // keep keys >= lo_key (all) ...
+  uint32_t eq_key = 0;   // ... except that only the first `eq_need` equal to eq_key are kept
+  uint32_t eq_need = 0xFFFFFFFFu;
+  uint32_t new_gate;
+  if (!exact_only && above + in_bin <= (uint32_t)room) {
+    lo_key = t1 << 21;
+    new_gate = lo_key;
+  } else {
+    uint32_t above2 = 0, in2 = 0, above3 = 0, in3 = 0;
+    list_hist(sc, count, hist, lane, 10, 0x7FF, 21, t1);
+    const uint32_t t2 = (uint32_t)find_bin(hist, 2048, need - above, lane, &above2, &in2);
+    const uint32_t p2 = (t1 << 11) | t2;
+    list_hist(sc, count, hist, lane, 0, 0x3FF, 10, p2);
+    const uint32_t t3 = (uint32_t)find_bin(hist, 1024, need - above - above2, lane, &above3, &in3);
+    const uint32_t T = (p2 << 10) | t3;
+    lo_key = T;
+    eq_key = T;
+    eq_need = need - above - above2 - above3;
+    new_gate = T == 0xFFFFFFFFu ? T : T + 1;
+  }
+  // in-place, order-preserving: the write index never passes the read index
+  int out = 0;
+  uint32_t eq_seen = 0;
+  for (int base = 0; base < count; base += 64) {
+    const int i = base + lane;
+    float s = 0.f;
+    int32_t p = 0;
+    uint32_t key = 0;
+    if (i < count) {
+      s = sc[i];
+      p = ps[i];
+      key = order_key(s);
+    }
+    const bool eq = i < count && key == eq_key && eq_need != 0xFFFFFFFFu;
+    const uint64_t eqm = __ballot(eq);
+    const uint32_t eq_rank = eq_seen + (uint32_t)wave_prefix(eqm, lane);
+    eq_seen += (uint32_t)__builtin_popcountll(eqm);
+    const bool keep = i < count && key >= lo_key && (!eq || eq_rank < eq_need);
+    const uint64_t km = __ballot(keep);
+    if (keep) {
+      const int o = out + wave_prefix(km, lane);
+      sc[o] = s;
+      ps[o] = p;
+    }
+    out += __builtin_popcountll(km);
+  }
+  *gate = new_gate;
+  return out;
+}
+
+}  // namespace
+
+template <bool kFused>
+__global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t sh_tile[2][kTileBytesBf16];
+  __shared__ float sh_scale[2][kTile];
+  __shared__ uint32_t sh_hist[kFused ? kWaves : 1][kFused ? kHistBins : 1];
+  __shared__ int64_t sh_span[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWg;
+  const int w = blockIdx.y;
+
+  // The workgroup's span: the union of its rows' ranges, cut to its window.
+  if (tid < 64) {
+    int64_t lo = INT64_MAX, hi = 0;
+    if (tid < kRowsPerWg) {
+      const RowRange rr = row_range(a, row0 + tid);
+      if (rr.hi > rr.lo) {
+        lo = rr.lo;
+        hi = rr.hi;
+      }
+    }
+    for (int d = 1; d < kRowsPerWg; d <<= 1) {
+      const int64_t l2 = __shfl_xor(lo, d), h2 = __shfl_xor(hi, d);
+      lo = l2 < lo ? l2 : lo;
+      hi = h2 > hi ? h2 : hi;
+    }
+    if (tid == 0) {
+      const int64_t wlo = (int64_t)w * a.window, whi = wlo + a.window;
+      sh_span[0] = lo > wlo ? lo : wlo;
+      sh_span[1] = hi < whi ? hi : whi;
+    }
+  }
+  __syncthreads();
+  const int64_t span_lo = sh_span[0] & ~(int64_t)(kTile - 1);
+  const int64_t span_hi = sh_span[1];
+
+  RowOperand rows[kRowsPerWave];
+  RowRange rr[kRowsPerWave];
+  int64_t rix[kRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    rix[i] = row0 + wave * kRowsPerWave + i;
+    rr[i] = row_range(a, rix[i]);
+    load_row(a.q, a.weights, rix[i], rix[i] < a.num_q, lane, rows[i]);
+  }
+
+  // fused scan state, wave-uniform
+  uint32_t gate[kRowsPerWave];
+  int count[kRowsPerWave];
+  float* lsc[kRowsPerWave];
+  int32_t* lps[kRowsPerWave];
+  if (kFused) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      gate[i] = 0;
+      count[i] = 0;
+      const int64_t seg = (rix[i] * a.nwin + w) * (int64_t)a.cap;
+      lsc[i] = a.cand_score + seg;
+      lps[i] = a.cand_pos + seg;
+    }
+  }
+
+  if (span_lo < span_hi) {
+    // staging: thread t moves 16 fp8 bytes of position t / 8, dims (t % 8) * 16 ..
+    const int sn = tid >> 3, sc = tid & 7;
+    uint4 raw = {0, 0, 0, 0};
+    float rscale = 0.f;
+    auto fetch = [&](int64_t base) {
+      const int64_t j = base + sn;
+      if (j < a.num_kv) {
+        raw = *reinterpret_cast<const uint4*>(a.kv + j * kDim + sc * 16);
+        rscale = a.kv_scale[j];
+      } else {
+        raw = uint4{0, 0, 0, 0};
+        rscale = 0.f;
+      }
+    };
+    auto stage = [&](int buf) {
+      uint8_t* t = sh_tile[buf];
+      *reinterpret_cast<bf16x8*>(t + tile_offset(sn, 2 * sc)) = widen8(raw.x, raw.y);
+      *reinterpret_cast<bf16x8*>(t + tile_offset(sn, 2 * sc + 1)) = widen8(raw.z, raw.w);
+      if (sc == 0) sh_scale[buf][sn] = rscale;
+    };
+    fetch(span_lo);
+    stage(0);
+    __syncthreads();
+    int buf = 0;
+    const int n = lane & 31, hb = lane >> 5;
+    for (int64_t base = span_lo; base < span_hi; base += kTile, buf ^= 1) {
+      const bool more = base + kTile < span_hi;
+      if (more) fetch(base + kTile);
+      bf16x8 b[8];
+      const uint8_t* t = sh_tile[buf];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) b[s] = *reinterpret_cast<const bf16x8*>(t + tile_offset(n, hb * 8 + s));
+      const float scale = sh_scale[buf][n];
+      const int64_t j = base + n;
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        if (base >= rr[i].hi || base + kTile <= rr[i].lo) continue;   // wave-uniform
+        const float score = score_tile(rows[i], b, scale);
+        const bool valid = hb == 0 && j >= rr[i].lo && j < rr[i].hi;
+        if (!kFused) {
+          const int64_t c = j - rr[i].lo;
+          if (valid && c < a.logits_stride) a.logits[rix[i] * a.logits_stride + c] = score;
+        } else {
+          const uint32_t key = order_key(score);
+          uint64_t m = __ballot(valid && key >= gate[i]);
+          int np = __builtin_popcountll(m);
+          if (count[i] + np > a.cap) {
+            count[i] = compact_list(lsc[i], lps[i], count[i], (uint32_t)a.k, a.cap / 2, false, sh_hist[wave], lane,
+                                    &gate[i]);
+            m = __ballot(valid && key >= gate[i]);
+            np = __builtin_popcountll(m);
+          }
+          if (valid && key >= gate[i]) {
+            const int o = count[i] + wave_prefix(m, lane);
+            lsc[i][o] = score;
+            lps[i][o] = (int32_t)j;
+          }
+          count[i] += np;
+        }
+      }
+      if (more) stage(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (kFused) {
+    // final trim to at most k entries, then hand the list to the row's area
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      if (rix[i] >= a.num_q) continue;
+      if (count[i] > a.k)
+        count[i] = compact_list(lsc[i], lps[i], count[i], (uint32_t)a.k, 0, true, sh_hist[wave], lane, &gate[i]);
+      if (count[i] == 0) continue;
+      int off = 0;
+      if (lane == 0) off = atomicAdd(&a.row_count[rix[i]], count[i]);
+      off = __shfl(off, 0);
+      __threadfence();
+      float* dsc = a.row_score + rix[i] * a.row_cap + off;
+      int32_t* dps = a.row_pos + rix[i] * a.row_cap + off;
+      for (int e = lane; e < count[i]; e += 64) {
+        dsc[e] = lsc[i][e];
+        dps[e] = lps[i][e];
+      }
+    }
+  }
+}
+
+__global__ void zero_counts_kernel(int32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_logits(const ScanArgs& a, int nwin, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.num_q + kRowsPerWg - 1) / kRowsPerWg), (unsigned)nwin);
+  hipLaunchKernelGGL(logits_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanArgs& a, int nwin, hipStream_t stream) {
+  const int64_t n = a.num_q;
+  hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.row_count, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((a.num_q + kRowsPerWg - 1) / kRowsPerWg), (unsigned)nwin);
+  hipLaunchKernelGGL(logits_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+int rows_per_workgroup() { return kRowsPerWg; }
+
+}  // namespace indexer

@@ -21,6 +21,7 @@
 #include <string>
 #include <utility>
 
+#include "indexer_internal.h"
 #include "topk_internal.h"
 #include "topk_transform.h"
 
@@ -394,6 +395,11 @@ topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const 
 
 }  // namespace
 
+namespace topk {
+void set_last_error(const char* msg) { t_last_error = msg; }
+void set_last_launch(const char* msg) { t_last_launch = msg; }
+}  // namespace topk
+
 extern "C" {
 
 topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
@@ -427,8 +433,9 @@ const char* topk_last_launch(void) { return t_last_launch.c_str(); }
 
 topk_status_t topk_release_workspaces(void) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (g_ws.empty() && g_meta.empty()) return TOPK_SUCCESS;
+  if (g_ws.empty() && g_meta.empty() && !indexer::has_buffers()) return TOPK_SUCCESS;
   hipError_t e = hipDeviceSynchronize();
+  indexer::release_buffers();
   for (auto& kv : g_ws)
     if (kv.second.ptr) (void)hipFree(kv.second.ptr);
   g_ws.clear();

@@ -8,6 +8,10 @@
 
 namespace topk {
 
+// Per-host-thread status text shared by every entry point of the library.
+void set_last_error(const char* msg);
+void set_last_launch(const char* msg);
+
 constexpr int kThreads = 1024;          // threads per workgroup (16 wave64s)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 2048;

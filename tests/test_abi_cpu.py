@@ -9,13 +9,15 @@ import pytest
 import sparse_attention_indexer_fp32_amd as topk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "topk_transform.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("topk_transform.h", "indexer_topk.h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(topk_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:topk|indexer)_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert "topk_transform" in names and len(names) >= 8
+    assert "topk_transform" in names and "indexer_topk" in names and len(names) >= 10
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(topk.EXPORTED)
@@ -86,3 +88,27 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         topk.topk_transform(s.double(), torch.zeros(2, dtype=torch.int32), torch.zeros((2, 1), dtype=torch.int32),
                             4, 8)
+
+
+@pytest.mark.parametrize("k,num_q,num_kv,expect", [
+    (0, 1, 16, 1),            # k below range
+    (2049, 1, 16, 1),         # k above range
+    (16, -1, 16, 1),          # negative rows
+    (16, 1, -1, 1),           # negative key count
+    (16, 1, 2**31, 1),        # key count beyond int32
+    (16, 0, 16, 0),           # no rows: no-op success
+    (16, 3, 16, 1),           # null pointers with rows
+])
+def test_indexer_topk_validation_without_device(lib, k, num_q, num_kv, expect):
+    st = lib.indexer_topk(None, None, None, None, None, None, k, None, None, num_q, num_kv)
+    assert st == expect, topk.topk_last_error()
+    if expect:
+        assert topk.topk_last_error()
+
+
+@pytest.mark.parametrize("num_q,num_kv,stride,expect", [
+    (-1, 16, 16, 1), (1, -1, 16, 1), (1, 16, -1, 1), (0, 16, 16, 0), (2, 16, 16, 1),
+])
+def test_indexer_logits_validation_without_device(lib, num_q, num_kv, stride, expect):
+    st = lib.indexer_logits(None, None, None, None, None, None, None, None, num_q, num_kv, stride)
+    assert st == expect, topk.topk_last_error()

@@ -1,0 +1,211 @@
+"""GPU parity of the indexer scoring (indexer_logits) and the fused scoring +
+exact top-k (indexer_topk) against the CPU oracle, through the C ABI.
+
+Scores: every written logit is compared with the oracle's float64 score within
+the oracle's derived fp32 error bound for that position (fp8 products exact,
+D + H + 2 roundings).  Selections: the page's tie-tolerant exactness test
+(LiteTopk PR #32094, Validation) with the tolerance set to twice the largest
+bound of the row, plus count, -1 padding, uniqueness and range.  The fused
+path is also checked, without the oracle, to be an exact top-k of the GPU's
+own logits (same fp32 values, both kernels share one scoring routine).
+"""
+import numpy as np
+import pytest
+
+from gpu_util import note
+from oracle import indexer_oracle as ix
+from workloads import indexer as wl
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["odd_widths_k512", "short_8x1k_k2048", "flat_8x16k_k2048", "ragged_3req_k2048", "single_32x32k_k512"]
+
+
+def _upload(w):
+    import torch
+    dev = torch.device("cuda", 0)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return t(w.q), t(w.weights), t(w.kv), t(w.kv_scale), t(w.ks), t(w.ke)
+
+
+def _lengths(w):
+    lo = np.clip(w.ks.astype(np.int64), 0, w.num_kv)
+    hi = np.clip(w.ke.astype(np.int64), 0, w.num_kv)
+    return lo, np.maximum(hi - lo, 0)
+
+
+def _logits(lib, w, tensors=None):
+    import torch
+    tensors = tensors or _upload(w)
+    lo, L = _lengths(w)
+    width = int(max(1, L.max()))
+    out = torch.full((w.num_q, width), float("nan"), dtype=torch.float32, device="cuda")
+    lib.indexer_logits(*tensors, width, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _row_eps(w, r):
+    pos = ix.key_range(int(w.ks[r]), int(w.ke[r]), w.num_kv)
+    b = ix.fp32_error_bound(w.q[r], w.weights[r], w.kv, w.kv_scale, pos)
+    return 2.0 * float(b.max()) if len(b) else 0.0
+
+
+def _check_logits(w, got, rows):
+    lo, L = _lengths(w)
+    for r in rows:
+        pos = ix.key_range(int(w.ks[r]), int(w.ke[r]), w.num_kv)
+        exact = ix.indexer_scores_row(w.q[r], w.weights[r], w.kv, w.kv_scale, pos)
+        bound = ix.fp32_error_bound(w.q[r], w.weights[r], w.kv, w.kv_scale, pos)
+        g = got[r, :L[r]].astype(np.float64)
+        assert np.all(np.isfinite(g)), f"{w.name} row {r}: unwritten or non-finite logits"
+        err = np.abs(g - exact)
+        bad = np.nonzero(err > bound)[0]
+        assert len(bad) == 0, (f"{w.name} row {r}: {len(bad)} logits outside the bound, first at {bad[0]}: "
+                               f"{g[bad[0]]!r} vs {exact[bad[0]]!r} (bound {bound[bad[0]]!r})")
+        assert np.all(np.isnan(got[r, L[r]:])), f"{w.name} row {r}: written past the row's length"
+
+
+def _check_topk(w, out, rows):
+    lo, L = _lengths(w)
+    for r in rows:
+        pos = ix.key_range(int(w.ks[r]), int(w.ke[r]), w.num_kv)
+        exact = ix.indexer_scores_row(w.q[r], w.weights[r], w.kv, w.kv_scale, pos)
+        errs = ix.check_indexer_row(exact, pos.start, w.k, out[r], _row_eps(w, r))
+        assert not errs, f"{w.name} row {r}: " + "; ".join(errs)
+
+
+def _check_exact_on_logits(w, out, logits):
+    """Without the oracle: the selection is an exact top-n of the GPU's own fp32 logits."""
+    lo, L = _lengths(w)
+    for r in range(w.num_q):
+        n = min(w.k, int(L[r]))
+        sel = out[r, :n].astype(np.int64) - lo[r]
+        assert np.all(out[r, n:] == -1), f"row {r}: padding"
+        assert len(np.unique(sel)) == n and np.all((sel >= 0) & (sel < L[r])), f"row {r}: invalid positions"
+        if n == 0 or n == L[r]:
+            continue
+        row = logits[r, :L[r]]
+        mask = np.zeros(L[r], bool)
+        mask[sel] = True
+        assert row[mask].min() >= row[~mask].max(), f"row {r}: not a top-{n} of the GPU logits"
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_logits_vs_oracle(lib, name):
+    w = wl.make_config(name)
+    note(f"indexer_logits {name} num_q={w.num_q} num_kv={w.num_kv}")
+    got = _logits(lib, w)
+    _check_logits(w, got, range(w.num_q))
+
+
+def test_logits_every_fp8_code(lib):
+    """Key j holds the j-th finite E4M3 code on dimension 5; head 0 sees +1 and
+    head 1 sees -1 there, with weights 1 and 2: score = relu(v) + 2 relu(-v),
+    exact in fp32 -- the widening of every code, subnormals and zeros included."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    n = len(codes)
+    kv = np.zeros((n, 128), np.uint8)
+    kv[:, 5] = codes
+    q = np.zeros((1, 32, 128), np.uint8)
+    q[0, 0, 5] = 0x38
+    q[0, 1, 5] = 0xB8
+    wts = np.zeros((1, 32), np.float32)
+    wts[0, 0], wts[0, 1] = 1.0, 2.0
+    w = wl.IndexerWorkload("fp8_codes", q, wts, kv, np.ones(n, np.float32), np.array([0], np.int32),
+                           np.array([n], np.int32), k=8, seed=0)
+    note("indexer_logits every fp8 code")
+    got = _logits(lib, w)[0, :n].astype(np.float64)
+    v = ix.fp8_e4m3_decode(codes)
+    assert np.array_equal(got, np.maximum(v, 0) + 2 * np.maximum(-v, 0))
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_indexer_topk_vs_oracle(lib, name):
+    import torch
+    w = wl.make_config(name)
+    note(f"indexer_topk {name} num_q={w.num_q} num_kv={w.num_kv} k={w.k}")
+    tensors = _upload(w)
+    out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    lib.indexer_topk(*tensors, w.k, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    _check_topk(w, o, range(w.num_q))
+    _check_exact_on_logits(w, o, _logits(lib, w, tensors))
+
+
+@pytest.mark.parametrize("requests,k,distinct", [
+    ([(16, 131072)], 64, None),      # long rows, small k: many gate trims
+    ([(8, 65536)], 2048, None),      # trims at the largest k
+    ([(8, 40000)], 16, 4),           # four distinct key rows: crowded bins, exact trims
+    ([(3, 70000), (5, 9000)], 300, 64),
+])
+def test_indexer_topk_trims(lib, requests, k, distinct):
+    """Rows much longer than the candidate capacity, so the lists are trimmed
+    and the gate raised many times; with few distinct keys the trims take the
+    exact (tie-cutting) path."""
+    import torch
+    w = wl.make(requests, k, seed=7100 + k)
+    if distinct:
+        rng = np.random.default_rng(k)
+        rows = w.kv[:distinct].copy()
+        w.kv = rows[rng.integers(0, distinct, w.num_kv)]
+        w.kv_scale = np.ones(w.num_kv, np.float32)
+    note(f"indexer_topk trims requests={requests} k={k} distinct={distinct}")
+    tensors = _upload(w)
+    out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    lib.indexer_topk(*tensors, w.k, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    _check_topk(w, o, range(w.num_q))
+    _check_exact_on_logits(w, o, _logits(lib, w, tensors))
+
+
+def test_indexer_edge_ranges(lib):
+    """Empty, inverted, clamped and shorter-than-k ranges; rows not a multiple of 8."""
+    import torch
+    w = wl.make([(5, 3000)], 256, seed=7200)
+    w.ks = np.array([0, 100, 2000, -50, 2990], np.int32)
+    w.ke = np.array([0, 90, 9999, 40, 3000], np.int32)   # empty, inverted, past the end, before 0, 10 positions
+    note("indexer_topk edge ranges")
+    tensors = _upload(w)
+    out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    lib.indexer_topk(*tensors, w.k, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[0] == -1) and np.all(o[1] == -1)
+    _check_topk(w, o, range(w.num_q))
+    _check_logits(w, _logits(lib, w, tensors), range(w.num_q))
+
+
+def test_indexer_repeat_calls_and_smaller_input(lib):
+    """A second call on a smaller batch reuses the buffers and clears its counters."""
+    import torch
+    for reqs in ([(24, 20000)], [(6, 5000)]):
+        w = wl.make(reqs, 512, seed=7300 + reqs[0][0])
+        note(f"indexer_topk repeat {reqs}")
+        tensors = _upload(w)
+        out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+        lib.indexer_topk(*tensors, w.k, out=out)
+        torch.cuda.synchronize()
+        _check_topk(w, out.cpu().numpy(), range(w.num_q))
+
+
+def test_indexer_prefill_full_size_sampled(lib):
+    """The performance shape (8192 query rows over 262144 keys, top-2048):
+    sampled rows against the oracle, and every row's size-independent properties."""
+    import torch
+    w = wl.make_config("prefill_8192x256k_k2048")
+    note("indexer_topk prefill 8192 x 262144 k=2048 (sampled)")
+    tensors = _upload(w)
+    out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    lib.indexer_topk(*tensors, w.k, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    lo, L = _lengths(w)
+    for r in range(w.num_q):
+        n = min(w.k, int(L[r]))
+        assert np.all(o[r, n:] == -1)
+        head = o[r, :n].astype(np.int64)
+        assert len(np.unique(head)) == n and np.all((head >= lo[r]) & (head < lo[r] + L[r]))
+    _check_topk(w, o, [0, 1, 2047, 4095, 6000, 8190, 8191])
