@@ -92,6 +92,16 @@ topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t
                            const int32_t* ks, const int32_t* ke, int32_t k, int32_t* out_idx, hipStream_t stream,
                            int32_t num_q, int64_t num_kv);
 
+/*
+ * Testing and tuning override, process-wide: the number of key positions each
+ * workgroup's window covers (the key range is split into windows so that
+ * short batches still fill the device).  0 = automatic; otherwise a positive
+ * multiple of 64.  Any window gives the same result; the choice only moves
+ * time and how often the candidate lists are trimmed.
+ * Returns TOPK_ERROR_INVALID_VALUE for other values.
+ */
+topk_status_t indexer_set_window_override(int64_t window);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,8 @@ STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUP
 
 EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_status_string", "topk_last_error", "topk_last_launch",
             "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape",
-            "topk_debug_fault_word", "topk_abi_version", "indexer_logits", "indexer_topk")
+            "topk_debug_fault_word", "topk_abi_version", "indexer_logits", "indexer_topk",
+            "indexer_set_window_override")
 INDEXER_HEADS = 32
 INDEXER_HEAD_DIM = 128
 
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.indexer_logits.restype = ctypes.c_int
     lib.indexer_topk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i64]
     lib.indexer_topk.restype = ctypes.c_int
+    lib.indexer_set_window_override.argtypes = [c_i64]
+    lib.indexer_set_window_override.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -236,3 +239,8 @@ def indexer_topk(q, weights, kv, kv_scale, ks, ke, k: int, out=None, stream=None
                                  ctypes.c_void_p(stream.cuda_stream), int(nq), int(nkv))
     _check(st)
     return out
+
+
+def indexer_set_window_override(window: int = 0) -> None:
+    """Key positions per workgroup window (0 = automatic; else a multiple of 64)."""
+    _check(load().indexer_set_window_override(int(window)))

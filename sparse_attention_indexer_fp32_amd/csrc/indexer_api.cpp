@@ -28,6 +28,7 @@ struct Buffers {
 std::mutex g_mu;
 std::map<int, int> g_cus;                                   // device -> CUs (gfx950 only)
 std::map<std::pair<int, hipStream_t>, Buffers> g_bufs;
+int64_t g_window_override = 0;                              // 0: automatic
 
 topk_status_t fail(topk_status_t st, const std::string& msg) {
   topk::set_last_error(msg.c_str());
@@ -87,15 +88,21 @@ topk_status_t get_buffers(int dev, hipStream_t stream, size_t bytes, void** ptr)
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Windows over [0, num_kv): enough (row block, window) workgroups for two per
-// CU, windows of at least 2048 positions, a multiple of 32 each.
+// CU, windows of at least 2048 positions, a multiple of 64 each (the kernels
+// stage 64 positions at a time and must not cross a window's edge).
 void plan_windows(int64_t num_q, int64_t num_kv, int cus, int32_t* nwin, int64_t* window) {
+  if (g_window_override > 0) {
+    *window = g_window_override;
+    *nwin = (int32_t)ceil_div(num_kv > 0 ? num_kv : 1, g_window_override);
+    return;
+  }
   const int64_t blocks = ceil_div(num_q, indexer::rows_per_workgroup());
   int64_t n = ceil_div(2 * (int64_t)cus, blocks);
   const int64_t most = ceil_div(num_kv, 2048);
   if (n > most) n = most;
   if (n < 1) n = 1;
-  int64_t w = ceil_div(ceil_div(num_kv, n), 32) * 32;
-  if (w < 32) w = 32;
+  int64_t w = ceil_div(ceil_div(num_kv, n), 64) * 64;
+  if (w < 64) w = 64;
   *window = w;
   *nwin = (int32_t)ceil_div(num_kv > 0 ? num_kv : 1, w);
 }
@@ -229,6 +236,14 @@ topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t
                 (long long)ceil_div(num_q, indexer::rows_per_workgroup()), a.nwin, (long long)a.window, a.cap,
                 topk_last_launch());
   topk::set_last_launch(buf);
+  return TOPK_SUCCESS;
+}
+
+topk_status_t indexer_set_window_override(int64_t window) {
+  if (window < 0 || window % 64 != 0 || window > (int64_t)INT32_MAX)
+    return fail(TOPK_ERROR_INVALID_VALUE, "window must be 0 or a positive multiple of 64");
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_window_override = window;
   return TOPK_SUCCESS;
 }
 

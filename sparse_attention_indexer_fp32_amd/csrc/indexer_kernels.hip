@@ -106,12 +106,12 @@ __device__ __forceinline__ void load_row(const uint8_t* q, const float* weights,
   }
 }
 
-// Scores of one query row against the staged tile.  Every lane returns the
-// score of position n = lane % 32 of the tile (both half-waves hold it).
-__device__ __forceinline__ float score_tile(const RowOperand& op, const bf16x8 (&b)[8], float scale) {
-  f32x16 acc = {};
-#pragma unroll
-  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.a[s], b[s], acc, 0, 0, 0);
+// Epilogue of one query row against a tile: relu of each head's dot
+// product, the head weights, the partner half-wave's 16 heads, the position's
+// scale.  Every lane returns the score of position n = lane % 32 of the tile
+// (both half-waves hold it).  The order of the operations is fixed, so every
+// kernel that calls this gets the same fp32 value.
+__device__ __forceinline__ float finish_score(const RowOperand& op, const f32x16& acc, float scale) {
   float part = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) part = fmaf(op.w[r], fmaxf(acc[r], 0.f), part);
@@ -194,12 +194,28 @@ __device__ __forceinline__ void clear_hist(uint32_t* hist, int bins, int lane) {
 }
 
 // Histogram of the keys in the list that match `prefix` above bit `lo_bit + width`.
+// The list passes keep kListBatch loads per lane in flight: the list was just
+// written and its reads come from L2, so one load at a time would make a trim
+// a chain of memory latencies while the workgroup's other waves wait.
+constexpr int kListBatch = 8;
+
 __device__ void list_hist(const float* sc, int count, uint32_t* hist, int lane, int shift, uint32_t mask,
                           int match_shift, uint32_t match) {
   clear_hist(hist, (int)mask + 1 < 64 ? 64 : (int)mask + 1, lane);
-  for (int i = lane; i < count; i += 64) {
-    const uint32_t key = order_key(sc[i]);
-    if (match_shift >= 32 || (key >> match_shift) == match) atomicAdd(&hist[(key >> shift) & mask], 1u);
+  for (int base = 0; base < count; base += 64 * kListBatch) {
+    float v[kListBatch];
+#pragma unroll
+    for (int b = 0; b < kListBatch; ++b) {
+      const int i = base + b * 64 + lane;
+      v[b] = i < count ? sc[i] : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < kListBatch; ++b) {
+      const int i = base + b * 64 + lane;
+      const uint32_t key = order_key(v[b]);
+      if (i < count && (match_shift >= 32 || (key >> match_shift) == match))
+        atomicAdd(&hist[(key >> shift) & mask], 1u);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -238,31 +254,38 @@ __device__ __attribute__((noinline)) int compact_list(float* sc, int32_t* ps, in
     eq_need = need - above - above2 - above3;
     new_gate = T == 0xFFFFFFFFu ? T : T + 1;
   }
-  // in-place, order-preserving: the write index never passes the read index
+  // In place and order-preserving.  A batch is loaded before any of it is
+  // written, and the entries of element b of a batch go to indices below
+  // base + (b + 1) * 64, under every index a later element or batch reads.
   int out = 0;
   uint32_t eq_seen = 0;
-  for (int base = 0; base < count; base += 64) {
-    const int i = base + lane;
-    float s = 0.f;
-    int32_t p = 0;
-    uint32_t key = 0;
-    if (i < count) {
-      s = sc[i];
-      p = ps[i];
-      key = order_key(s);
+  const bool cut = eq_need != 0xFFFFFFFFu;
+  for (int base = 0; base < count; base += 64 * kListBatch) {
+    float sv[kListBatch];
+    int32_t pv[kListBatch];
+#pragma unroll
+    for (int b = 0; b < kListBatch; ++b) {
+      const int i = base + b * 64 + lane;
+      sv[b] = i < count ? sc[i] : 0.f;
+      pv[b] = i < count ? ps[i] : 0;
     }
-    const bool eq = i < count && key == eq_key && eq_need != 0xFFFFFFFFu;
-    const uint64_t eqm = __ballot(eq);
-    const uint32_t eq_rank = eq_seen + (uint32_t)wave_prefix(eqm, lane);
-    eq_seen += (uint32_t)__builtin_popcountll(eqm);
-    const bool keep = i < count && key >= lo_key && (!eq || eq_rank < eq_need);
-    const uint64_t km = __ballot(keep);
-    if (keep) {
-      const int o = out + wave_prefix(km, lane);
-      sc[o] = s;
-      ps[o] = p;
+#pragma unroll
+    for (int b = 0; b < kListBatch; ++b) {
+      const int i = base + b * 64 + lane;
+      const uint32_t key = order_key(sv[b]);
+      const bool eq = cut && i < count && key == eq_key;
+      const uint64_t eqm = __ballot(eq);
+      const uint32_t eq_rank = eq_seen + (uint32_t)wave_prefix(eqm, lane);
+      eq_seen += (uint32_t)__builtin_popcountll(eqm);
+      const bool keep = i < count && key >= lo_key && (!eq || eq_rank < eq_need);
+      const uint64_t km = __ballot(keep);
+      if (keep) {
+        const int o = out + wave_prefix(km, lane);
+        sc[o] = sv[b];
+        ps[o] = pv[b];
+      }
+      out += __builtin_popcountll(km);
     }
-    out += __builtin_popcountll(km);
   }
   *gate = new_gate;
   return out;
@@ -270,14 +293,30 @@ __device__ __attribute__((noinline)) int compact_list(float* sc, int32_t* ps, in
 
 }  // namespace
 
+// Key positions staged per barrier: two 32-position MFMA tiles.
+constexpr int kStage = 2 * kTile;
+constexpr int kStageBytesBf16 = kStage * kDim * 2;   // 16 KB
+
+// One thread's share of a stage in flight: 32 fp8 bytes of position t / 4
+// (dims (t % 4) * 32 ..) and, for t % 4 == 0, that position's scale.
+struct Ring {
+  uint4 r0, r1;
+  float s;
+};
+
 template <bool kFused>
 __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t sh_tile[2][kTileBytesBf16];
-  __shared__ float sh_scale[2][kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t sh_tile[2][kStageBytesBf16];
+  __shared__ float sh_scale[2][kStage];
   __shared__ uint32_t sh_hist[kFused ? kWaves : 1][kFused ? kHistBins : 1];
+  // a stage's appends, per wave and row, before they go to the global list
+  __shared__ float sh_app_score[kFused ? kWaves : 1][kRowsPerWave][kFused ? kStage : 1];
+  __shared__ int32_t sh_app_pos[kFused ? kWaves : 1][kRowsPerWave][kFused ? kStage : 1];
   __shared__ int64_t sh_span[2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform, so the row indices, ranges and list pointers derived from it live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWg;
   const int w = blockIdx.y;
 
@@ -303,7 +342,9 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
     }
   }
   __syncthreads();
-  const int64_t span_lo = sh_span[0] & ~(int64_t)(kTile - 1);
+  // stages start on multiples of 64; windows are multiples of 64 as well, so
+  // a stage never reaches into a neighbouring window
+  const int64_t span_lo = sh_span[0] & ~(int64_t)(kStage - 1);
   const int64_t span_hi = sh_span[1];
 
   RowOperand rows[kRowsPerWave];
@@ -316,84 +357,131 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
     load_row(a.q, a.weights, rix[i], rix[i] < a.num_q, lane, rows[i]);
   }
 
-  // fused scan state, wave-uniform
+  // fused scan state, wave-uniform: gate, list length, appends staged in LDS
   uint32_t gate[kRowsPerWave];
   int count[kRowsPerWave];
-  float* lsc[kRowsPerWave];
-  int32_t* lps[kRowsPerWave];
+  int staged[kRowsPerWave];
   if (kFused) {
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       gate[i] = 0;
       count[i] = 0;
-      const int64_t seg = (rix[i] * a.nwin + w) * (int64_t)a.cap;
-      lsc[i] = a.cand_score + seg;
-      lps[i] = a.cand_pos + seg;
+      staged[i] = 0;
     }
   }
+  auto list_score = [&](int i) { return a.cand_score + (rix[i] * a.nwin + w) * (int64_t)a.cap; };
+  auto list_pos = [&](int i) { return a.cand_pos + (rix[i] * a.nwin + w) * (int64_t)a.cap; };
 
   if (span_lo < span_hi) {
-    // staging: thread t moves 16 fp8 bytes of position t / 8, dims (t % 8) * 16 ..
-    const int sn = tid >> 3, sc = tid & 7;
-    uint4 raw = {0, 0, 0, 0};
-    float rscale = 0.f;
-    auto fetch = [&](int64_t base) {
+    const int sn = tid >> 2, sc = tid & 3;
+    auto fetch = [&](Ring& R, int64_t base) {
       const int64_t j = base + sn;
-      if (j < a.num_kv) {
-        raw = *reinterpret_cast<const uint4*>(a.kv + j * kDim + sc * 16);
-        rscale = a.kv_scale[j];
+      if (base < span_hi && j < a.num_kv) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.kv + j * kDim + sc * 32);
+        R.r0 = src[0];
+        R.r1 = src[1];
+        R.s = sc == 0 ? a.kv_scale[j] : 0.f;
       } else {
-        raw = uint4{0, 0, 0, 0};
-        rscale = 0.f;
+        R.r0 = uint4{0, 0, 0, 0};
+        R.r1 = uint4{0, 0, 0, 0};
+        R.s = 0.f;
       }
     };
-    auto stage = [&](int buf) {
+    auto stage = [&](const Ring& R, int buf) {
       uint8_t* t = sh_tile[buf];
-      *reinterpret_cast<bf16x8*>(t + tile_offset(sn, 2 * sc)) = widen8(raw.x, raw.y);
-      *reinterpret_cast<bf16x8*>(t + tile_offset(sn, 2 * sc + 1)) = widen8(raw.z, raw.w);
-      if (sc == 0) sh_scale[buf][sn] = rscale;
+      *reinterpret_cast<bf16x8*>(t + tile_offset(sn, 4 * sc)) = widen8(R.r0.x, R.r0.y);
+      *reinterpret_cast<bf16x8*>(t + tile_offset(sn, 4 * sc + 1)) = widen8(R.r0.z, R.r0.w);
+      *reinterpret_cast<bf16x8*>(t + tile_offset(sn, 4 * sc + 2)) = widen8(R.r1.x, R.r1.y);
+      *reinterpret_cast<bf16x8*>(t + tile_offset(sn, 4 * sc + 3)) = widen8(R.r1.z, R.r1.w);
+      if (sc == 0) sh_scale[buf][sn] = R.s;
     };
-    fetch(span_lo);
-    stage(0);
-    __syncthreads();
-    int buf = 0;
     const int n = lane & 31, hb = lane >> 5;
-    for (int64_t base = span_lo; base < span_hi; base += kTile, buf ^= 1) {
-      const bool more = base + kTile < span_hi;
-      if (more) fetch(base + kTile);
-      bf16x8 b[8];
+    auto compute = [&](int64_t base, int buf) {
+      bool live = false;
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) live |= base < rr[i].hi && base + kStage > rr[i].lo;
+      if (!live) return;   // wave-uniform
       const uint8_t* t = sh_tile[buf];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) b[s] = *reinterpret_cast<const bf16x8*>(t + tile_offset(n, hb * 8 + s));
-      const float scale = sh_scale[buf][n];
-      const int64_t j = base + n;
+      for (int half = 0; half < 2; ++half) {
+        const int nb = half * kTile + n;
+        bf16x8 b[8];
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) {
-        if (base >= rr[i].hi || base + kTile <= rr[i].lo) continue;   // wave-uniform
-        const float score = score_tile(rows[i], b, scale);
-        const bool valid = hb == 0 && j >= rr[i].lo && j < rr[i].hi;
-        if (!kFused) {
-          const int64_t c = j - rr[i].lo;
-          if (valid && c < a.logits_stride) a.logits[rix[i] * a.logits_stride + c] = score;
-        } else {
-          const uint32_t key = order_key(score);
-          uint64_t m = __ballot(valid && key >= gate[i]);
-          int np = __builtin_popcountll(m);
-          if (count[i] + np > a.cap) {
-            count[i] = compact_list(lsc[i], lps[i], count[i], (uint32_t)a.k, a.cap / 2, false, sh_hist[wave], lane,
-                                    &gate[i]);
-            m = __ballot(valid && key >= gate[i]);
-            np = __builtin_popcountll(m);
+        for (int s = 0; s < 8; ++s) b[s] = *reinterpret_cast<const bf16x8*>(t + tile_offset(nb, hb * 8 + s));
+        const float scale = sh_scale[buf][nb];
+        f32x16 acc[kRowsPerWave];
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) acc[i] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+          for (int i = 0; i < kRowsPerWave; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows[i].a[s], b[s], acc[i], 0, 0, 0);
+        float score[kRowsPerWave];
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) score[i] = finish_score(rows[i], acc[i], scale);
+        const int64_t j = base + nb;
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          const bool valid = hb == 0 && j >= rr[i].lo && j < rr[i].hi;
+          if (!kFused) {
+            const int64_t c = j - rr[i].lo;
+            if (valid && c < a.logits_stride) a.logits[rix[i] * a.logits_stride + c] = score[i];
+          } else {
+            // staged in LDS; flush() writes them to the list once the next
+            // loads are issued, so no wait on their stores stalls the loop
+            const uint32_t key = order_key(score[i]);
+            const bool pass = valid && key >= gate[i];
+            const uint64_t m = __ballot(pass);
+            if (pass) {
+              const int o = staged[i] + wave_prefix(m, lane);
+              sh_app_score[wave][i][o] = score[i];
+              sh_app_pos[wave][i][o] = (int32_t)j;
+            }
+            staged[i] += __builtin_popcountll(m);
           }
-          if (valid && key >= gate[i]) {
-            const int o = count[i] + wave_prefix(m, lane);
-            lsc[i][o] = score;
-            lps[i][o] = (int32_t)j;
-          }
-          count[i] += np;
         }
       }
-      if (more) stage(buf ^ 1);
+    };
+    // Appends the staged entries to the lists (at most kStage per row per
+    // stage), then trims any list that could not take another stage.  Either
+    // the list is shorter than its window (then it cannot overflow, and a trim
+    // happens only above k entries) or its capacity is at least 4k and 4096,
+    // so a trim leaves it at most half full.
+    auto flush = [&]() {
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        if (staged[i] == 0) continue;   // wave-uniform
+        if (lane < staged[i]) {
+          list_score(i)[count[i] + lane] = sh_app_score[wave][i][lane];
+          list_pos(i)[count[i] + lane] = sh_app_pos[wave][i][lane];
+        }
+        count[i] += staged[i];
+        staged[i] = 0;
+        if (count[i] > a.cap - kStage && count[i] > a.k)
+          count[i] = compact_list(list_score(i), list_pos(i), count[i], (uint32_t)a.k, a.cap / 2, false,
+                                  sh_hist[wave], lane, &gate[i]);
+      }
+    };
+    // Two stages in flight in registers: the stage computed now, the next one
+    // already in LDS, and the two after it loading.
+    Ring r0, r1;
+    fetch(r0, span_lo);
+    stage(r0, 0);
+    fetch(r1, span_lo + kStage);
+    fetch(r0, span_lo + 2 * kStage);
+    __syncthreads();
+    for (int64_t base = span_lo; base < span_hi; base += 2 * kStage) {
+      compute(base, 0);
+      stage(r1, 1);
+      fetch(r1, base + 3 * kStage);
+      if (kFused) flush();
+      __syncthreads();
+      if (base + kStage >= span_hi) break;
+      compute(base + kStage, 1);
+      stage(r0, 0);
+      fetch(r0, base + 4 * kStage);
+      if (kFused) flush();
       __syncthreads();
     }
   }
@@ -403,8 +491,10 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       if (rix[i] >= a.num_q) continue;
+      float* lsc = list_score(i);
+      int32_t* lps = list_pos(i);
       if (count[i] > a.k)
-        count[i] = compact_list(lsc[i], lps[i], count[i], (uint32_t)a.k, 0, true, sh_hist[wave], lane, &gate[i]);
+        count[i] = compact_list(lsc, lps, count[i], (uint32_t)a.k, 0, true, sh_hist[wave], lane, &gate[i]);
       if (count[i] == 0) continue;
       int off = 0;
       if (lane == 0) off = atomicAdd(&a.row_count[rix[i]], count[i]);
@@ -412,9 +502,23 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
       __threadfence();
       float* dsc = a.row_score + rix[i] * a.row_cap + off;
       int32_t* dps = a.row_pos + rix[i] * a.row_cap + off;
-      for (int e = lane; e < count[i]; e += 64) {
-        dsc[e] = lsc[i][e];
-        dps[e] = lps[i][e];
+      for (int base = 0; base < count[i]; base += 64 * kListBatch) {
+        float sv[kListBatch];
+        int32_t pv[kListBatch];
+#pragma unroll
+        for (int b = 0; b < kListBatch; ++b) {
+          const int e = base + b * 64 + lane;
+          sv[b] = e < count[i] ? lsc[e] : 0.f;
+          pv[b] = e < count[i] ? lps[e] : 0;
+        }
+#pragma unroll
+        for (int b = 0; b < kListBatch; ++b) {
+          const int e = base + b * 64 + lane;
+          if (e < count[i]) {
+            dsc[e] = sv[b];
+            dps[e] = pv[b];
+          }
+        }
       }
     }
   }

@@ -112,3 +112,11 @@ def test_indexer_topk_validation_without_device(lib, k, num_q, num_kv, expect):
 def test_indexer_logits_validation_without_device(lib, num_q, num_kv, stride, expect):
     st = lib.indexer_logits(None, None, None, None, None, None, None, None, num_q, num_kv, stride)
     assert st == expect, topk.topk_last_error()
+
+
+def test_indexer_window_override_validation(lib):
+    assert lib.indexer_set_window_override(33) == 1
+    assert lib.indexer_set_window_override(96) == 1
+    assert lib.indexer_set_window_override(-32) == 1
+    assert lib.indexer_set_window_override(4096) == 0
+    assert lib.indexer_set_window_override(0) == 0

@@ -134,28 +134,35 @@ def test_indexer_topk_vs_oracle(lib, name):
     _check_exact_on_logits(w, o, _logits(lib, w, tensors))
 
 
-@pytest.mark.parametrize("requests,k,distinct", [
-    ([(16, 131072)], 64, None),      # long rows, small k: many gate trims
-    ([(8, 65536)], 2048, None),      # trims at the largest k
-    ([(8, 40000)], 16, 4),           # four distinct key rows: crowded bins, exact trims
-    ([(3, 70000), (5, 9000)], 300, 64),
+@pytest.mark.parametrize("requests,k,distinct,window", [
+    ([(16, 131072)], 64, None, 0),           # automatic windows
+    ([(16, 131072)], 64, None, 1 << 20),     # one window: the lists are trimmed many times
+    ([(8, 65536)], 2048, None, 1 << 20),     # trims at the largest k
+    ([(8, 65536)], 2048, None, 24576),       # three windows merged by the select
+    ([(8, 40000)], 16, 4, 1 << 20),          # four distinct key rows: crowded bins, exact trims
+    ([(3, 70000), (5, 9000)], 300, 64, 1 << 20),
+    ([(3, 70000), (5, 9000)], 300, 64, 8192),
 ])
-def test_indexer_topk_trims(lib, requests, k, distinct):
+def test_indexer_topk_trims(lib, requests, k, distinct, window):
     """Rows much longer than the candidate capacity, so the lists are trimmed
     and the gate raised many times; with few distinct keys the trims take the
     exact (tie-cutting) path."""
     import torch
+    lib.indexer_set_window_override(window)
     w = wl.make(requests, k, seed=7100 + k)
     if distinct:
         rng = np.random.default_rng(k)
         rows = w.kv[:distinct].copy()
         w.kv = rows[rng.integers(0, distinct, w.num_kv)]
         w.kv_scale = np.ones(w.num_kv, np.float32)
-    note(f"indexer_topk trims requests={requests} k={k} distinct={distinct}")
+    note(f"indexer_topk trims requests={requests} k={k} distinct={distinct} window={window}")
     tensors = _upload(w)
     out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
-    lib.indexer_topk(*tensors, w.k, out=out)
-    torch.cuda.synchronize()
+    try:
+        lib.indexer_topk(*tensors, w.k, out=out)
+        torch.cuda.synchronize()
+    finally:
+        lib.indexer_set_window_override(0)
     o = out.cpu().numpy()
     _check_topk(w, o, range(w.num_q))
     _check_exact_on_logits(w, o, _logits(lib, w, tensors))
