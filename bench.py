@@ -17,6 +17,12 @@ benchmark rotates every read tensor for the same reason).
 The CPU baseline is the oracle (numpy, one core) on a bounded sample of rows of
 the same workload.
 
+A second object, "indexer", times the step before the top-k on the prefill
+shape of LiteTopk PR #32094 (8192 query rows over 262144 keys, H 32, D 128,
+fp8 inputs, top-2048): the fused scoring + exact top-k (indexer_topk) against
+the dense path (indexer_logits, then topk_transform over the dense scores),
+with the scoring kernels' matrix-core throughput against the bf16 dense peak.
+
 Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
@@ -33,6 +39,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (the scoring kernels' contraction type)
 ROTATE_BYTES = 1.25 * (1 << 30)
 METRIC = "top-k+transform µs/call at b=1,L=1M,k=2048; effective HBM GB/s at b=2048,L=64K"
 
@@ -147,6 +154,63 @@ def counters_run(topk) -> int:
     return 0
 
 
+def indexer_leg(topk, steps: int, warmup: int) -> dict:
+    """Fused vs dense indexer scoring + top-k on the prefill shape; HIP-event
+    averages over `steps` calls on the stream the calls are queued on."""
+    import numpy as np
+    import torch
+    from workloads import indexer as wl
+    w = wl.make_config("prefill_8192x256k_k2048")
+    dev = torch.device("cuda", 0)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, wt, kv, sc, ks, ke = t(w.q), t(w.weights), t(w.kv), t(w.kv_scale), t(w.ks), t(w.ke)
+    lo = np.clip(w.ks.astype(np.int64), 0, w.num_kv)
+    L = np.maximum(np.clip(w.ke.astype(np.int64), 0, w.num_kv) - lo, 0)
+    width = int(L.max())
+    flops = 2.0 * wl.HEADS * wl.HEAD_DIM * float(L.sum())
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    out = torch.empty((w.num_q, w.k), dtype=torch.int32, device=dev)
+    fused_ms = timed(lambda: topk.indexer_topk(q, wt, kv, sc, ks, ke, w.k, out=out))
+    fused_launch = topk.topk_last_launch()
+    logits = torch.empty((w.num_q, width), dtype=torch.float32, device=dev)
+    logits_ms = timed(lambda: topk.indexer_logits(q, wt, kv, sc, ks, ke, width, out=logits))
+    seq = t(L.astype(np.int32))
+    ps = 64
+    pt = torch.arange((width + ps - 1) // ps, dtype=torch.int32, device=dev).repeat(w.num_q, 1).contiguous()
+    out2 = torch.empty((w.num_q, w.k), dtype=torch.int32, device=dev)
+    select_ms = timed(lambda: topk.topk_transform(logits, seq, pt, w.k, ps, out=out2))
+    del logits, pt
+    torch.cuda.empty_cache()
+    dense_ms = logits_ms + select_ms
+    tf = lambda ms: flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "num_q": w.num_q, "num_kv": w.num_kv, "k": w.k, "heads": wl.HEADS,
+        "head_dim": wl.HEAD_DIM, "pairs_scored": int(L.sum()), "steps": steps, "warmup": warmup,
+        "fused_ms": round(fused_ms, 3), "fused_launch": fused_launch,
+        "dense_logits_ms": round(logits_ms, 3), "dense_select_ms": round(select_ms, 3),
+        "dense_total_ms": round(dense_ms, 3), "fused_speedup_vs_dense": round(dense_ms / fused_ms, 3),
+        "dense_logits_bytes_avoided": int(w.num_q) * width * 4,
+        "roofline": {"bound": "mfma", "dtype": "bf16 (fp8 widened exactly)", "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "fused_achieved": round(tf(fused_ms), 1),
+                     "fused_frac": round(tf(fused_ms) / BF16_PEAK_TFLOPS, 4),
+                     "logits_achieved": round(tf(logits_ms), 1),
+                     "logits_frac": round(tf(logits_ms) / BF16_PEAK_TFLOPS, 4)},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +218,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true", help="also time every workload (table on stderr)")
+    ap.add_argument("--no-indexer", action="store_true", help="skip the fused indexer scoring + top-k leg")
     ap.add_argument("--counters", action="store_true",
                     help="only run the headline kernel 4 times on rotated inputs, then 2 plain device copies of "
                          "256 MiB (the calibration for HBM byte counters); for rocprofv3 --pmc passes")
@@ -225,6 +290,8 @@ def main() -> int:
             del sx
             torch.cuda.empty_cache()
 
+    indexer = None if args.no_indexer else indexer_leg(topk, steps=5, warmup=2)
+
     cpu = None if args.no_cpu else cpu_baseline(w)
 
     result = {
@@ -257,6 +324,8 @@ def main() -> int:
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }
+    if indexer is not None:
+        result["indexer"] = indexer
     if extra:
         result["other_workloads"] = extra
     print(json.dumps(result), flush=True)
