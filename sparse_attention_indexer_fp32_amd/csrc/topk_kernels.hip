@@ -57,6 +57,10 @@ __device__ __forceinline__ uint32_t order_key_bits(uint32_t u) {
 // no swizzle; loads past num_records return zero.
 constexpr int kBufferWord3 = 0x00020000;
 
+// Cache-policy operand of the buffer loads (gfx950: bit 1 = nt, non-temporal).
+constexpr int kLoadStream = 2;
+constexpr int kLoadReuse = 0;
+
 // The thread index through an empty asm, so values derived from it are
 // recomputed where they are used instead of being hoisted out of the row loop
 // (LICM would otherwise keep dozens of per-element addresses live in VGPRs).
@@ -420,7 +424,11 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, i
 // hardware returns 0 past seq_len and past the tensor without a branch.
 // Nothing here consumes the data, so the loads stay in flight until the
 // caller's first use (chunks are double-buffered this way).
-template <int NT, int V>
+// AUX is the loads' cache policy: kLoadStream (nt) for a row's first read,
+// whose lines are not used again, kLoadReuse for the reads that revisit a
+// row.  Measured on MI355X with this row-per-workgroup layout, nt loads read
+// 537 MB at 6.9-7.1 TB/s against 6.1-6.3 TB/s for default-policy loads.
+template <int NT, int V, int AUX = kLoadStream>
 __device__ __forceinline__ void load_raw(uint32_t (&raw)[4 * V], const float* rowp, uint32_t cbase, uint32_t L,
                                          bool vec, int tid) {
   constexpr uint32_t span = (uint32_t)NT * 4u * V;
@@ -433,7 +441,7 @@ __device__ __forceinline__ void load_raw(uint32_t (&raw)[4 * V], const float* ro
   if (vec) {
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, v * (NT * 16), 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, v * (NT * 16), AUX);
 #pragma unroll
       for (int i = 0; i < 4; ++i) raw[4 * v + i] = x[i];
     }
@@ -442,7 +450,7 @@ __device__ __forceinline__ void load_raw(uint32_t (&raw)[4 * V], const float* ro
     for (int v = 0; v < V; ++v)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        raw[4 * v + i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, v * (NT * 16) + 4 * i, 0);
+        raw[4 * v + i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, v * (NT * 16) + 4 * i, AUX);
   }
 }
 
@@ -454,10 +462,10 @@ __device__ __forceinline__ uint32_t slot_key(uint32_t raw, int j, uint32_t cbase
   return (tid * 4 < lim) ? order_key_bits(raw) : 0u;
 }
 
-template <int NT, int V>
+template <int NT, int V, int AUX = kLoadStream>
 __device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* rowp, uint32_t cbase, uint32_t L,
                                           bool vec, int tid) {
-  load_raw<NT, V>(key, rowp, cbase, L, vec, tid);
+  load_raw<NT, V, AUX>(key, rowp, cbase, L, vec, tid);
 #pragma unroll
   for (int j = 0; j < 4 * V; ++j) key[j] = slot_key<NT>(key[j], j, cbase, L, tid);
 }
@@ -792,7 +800,7 @@ __device__ __forceinline__ void restream_pass(int mode, const float* rowp, uint3
   const uint32_t gt_end = n - need;
   for (uint32_t c = 0; c < L; c += span) {
     uint32_t key[4 * CV];
-    load_keys<NT, CV>(key, rowp, c, L, vec, tid);
+    load_keys<NT, CV, kLoadReuse>(key, rowp, c, L, vec, tid);
     const uint32_t p0 = c + (uint32_t)tid * 4u;
 #pragma unroll
     for (int j = 0; j < 4 * CV; ++j) {
@@ -1158,7 +1166,7 @@ __device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp,
   constexpr uint32_t span = (uint32_t)kThreads * 4u * kSortCV;
   for (uint32_t c = 0; c < L; c += span) {
     uint32_t raw[4 * kSortCV];
-    load_raw<kThreads, kSortCV>(raw, rowp, c, L, vec, tid);
+    load_raw<kThreads, kSortCV, kLoadReuse>(raw, rowp, c, L, vec, tid);
 #pragma unroll
     for (int j = 0; j < 4 * kSortCV; ++j) {
       const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3);
@@ -1218,7 +1226,7 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
       // 1. keys above the bin -> sh_sort; the bin's members -> tie list
       for (uint32_t c = 0; c < L; c += span) {
         uint32_t raw[4 * kSortCV];
-        load_raw<kThreads, kSortCV>(raw, rowp, c, L, vec, tid);
+        load_raw<kThreads, kSortCV, kLoadReuse>(raw, rowp, c, L, vec, tid);
 #pragma unroll
         for (int j = 0; j < 4 * kSortCV; ++j) {
           const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3);
