@@ -265,7 +265,7 @@ def main() -> int:
 
     extra = {}
     if args.all:
-        for name in ("c1", "c2", "c3_b4", "c3_b8", "c4b", "c5"):
+        for name in ("c1", "c2", "c3_b4", "c3_b8", "c4b", "c5", "mixed"):
             wx = workloads.make(name)
             bx = algorithmic_bytes(wx, raw=wx.want_raw)
             inx = wx.scores.nbytes + wx.seq_lens.nbytes + wx.page_table.nbytes

@@ -211,7 +211,9 @@ const char* kind_name(Kind k) {
 //              the 1024-thread shape.
 //  * split:    G workgroups per row holding the row in registers, merged
 //              through global atomics and a per-row barrier; for fewer, long
-//              rows.  Picks the smallest E whose grid still fits resident.
+//              rows.  Picks the smallest E whose grid still fits resident;
+//              when none does, E = 64 with the rows cycled over the resident
+//              slots, if that is estimated faster than streaming them.
 //  * resident: one workgroup per row holding the row in registers; for
 //              fewer than half a row per CU of width <= 16K.
 topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, int32_t k, Plan* plan) {
@@ -265,6 +267,26 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
           break;
         }
       }
+    if (chosen < 0) {
+      // No E holds every row resident at once.  The rows can still run as
+      // split rows cycled over cap / G slots (E = 64: the fewest workgroups
+      // per row), or stream one row per workgroup.  Measured on MI355X at
+      // k 2048: a split iteration of full 64K-position workgroups takes
+      // ~36 us; a streamed row moves ~27 GB/s on its one workgroup, plus
+      // ~10 us.  The cheaper estimate wins: 32 x 1M rows 73 us split against
+      // 153 us streamed, 4 x 1M + 28 x 16K 53 against 136, 16 x 2M 72
+      // against 277; but 100 x 256K 73 against 54, and 120 x 512K (k 512)
+      // 120 against 81, stay streamed.
+      const int i = topk::kNumEpt - 1;
+      const int64_t G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[i]);
+      const int64_t cap = (int64_t)dev.occ[1][i] * dev.cus;
+      const int64_t slots = cap / G;
+      if (G > 1 && slots >= 1 && G <= (int64_t)topk::kBarGroup * topk::kBarMaxGroups) {
+        const double t_split = 36.0 * (double)ceil_div(B, slots);
+        const double t_stream = 4.0 * (double)Wc / 27000.0 + 10.0;
+        if (t_split < t_stream) chosen = i;
+      }
+    }
     if (chosen < 0) {
       plan->kind = Kind::kStream;   // too many rows to hold resident: stream them
     } else {

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 # ---- the five benchmark workloads at full size ------------------------------
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c3_b4", "c3_b8", "c4b", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c3_b4", "c3_b8", "c4b", "c5", "mixed"])
 def test_config_full(lib, name):
     note(f"config {name}")
     w = workloads.make(name)
@@ -151,6 +151,26 @@ def test_repeated_split_rows_stress(lib):
         note(f"stress rep={rep} B={B} kind={kind}")
         out, raw = run(lib, w, raw=rep % 2 == 0)
         check(w, out, raw)
+    assert lib.topk_debug_fault_word() == 0
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_split_rows_cycled_over_slots(lib, kind):
+    """More long rows than the split kernel holds resident at once, at a batch
+    below half a row per CU: the dispatcher cycles split rows over the resident
+    slots (each slot alternates its two workspace regions) rather than
+    streaming one row per workgroup.  Long, short, empty and exactly-k rows mix
+    within a slot's sequence."""
+    import re
+    W = 1 << 20
+    seq = [W, 16384, W - 3, 0, 5000, W, 2048, 700000, 2049, W - 64] + [W - 17 * i for i in range(14)]
+    w = workloads.custom(808 + len(kind), len(seq), W, 2048, 64, seq_lens=seq, kind=kind, table="perm")
+    note(f"cycled split rows kind={kind} B={len(seq)} W={W}")
+    out, raw = run(lib, w, raw=True)
+    launch = lib.topk_last_launch()
+    m = re.search(r"slots=(\d+)", launch)
+    assert launch.startswith("split-row") and m and int(m.group(1)) < w.batch, launch
+    check(w, out, raw)
     assert lib.topk_debug_fault_word() == 0
 
 

@@ -37,7 +37,7 @@ def check_exact(w, out, raw, rows=None):
         assert bad.size == 0, f"{w.name}: raw differs from the oracle in {bad.size} rows (first {bad[:5].tolist()})"
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c3_b4", "c4b", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c3_b4", "c4b", "c5", "mixed"])
 def test_sorted_configs(lib, name):
     note(f"sorted config {name}")
     w = workloads.make(name)

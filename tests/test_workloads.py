@@ -61,3 +61,12 @@ def test_custom_kinds():
         w = workloads.custom(1, 3, 1000, 64, 16, seq_lens=[0, 500, 1000], kind=kind)
         assert w.scores.shape == (3, 1000) and w.page_table.shape == (3, 63)
         assert np.all(np.isposinf(w.scores[1, 500:]))
+
+
+def test_mixed_structure():
+    w = workloads.mixed()
+    assert w.k == 2048 and w.page_size == 64 and w.scores.shape == (32, 1 << 20)
+    assert w.seq_lens.tolist() == [1 << 20] * 4 + [16384] * 28
+    assert np.all(np.isposinf(w.scores[4:, 16384:]))
+    assert np.all(w.page_table[4:, 256:] == workloads.INT32_MIN)
+    assert np.unique(w.page_table[0]).size == w.page_table.shape[1]

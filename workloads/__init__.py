@@ -221,6 +221,25 @@ def c5(seed: int = 5000) -> Workload:
                     "short rows, ps=16 permuted table", scores, seq, pt, k, ps, False, seed)
 
 
+def mixed(seed: int = 6000) -> Workload:
+    """Mixed long/short decode batch: batch 32 of width 1,048,576, rows 0..3 at
+    the full width and rows 4..31 at 16384, k 2048, N(0,1), page_size 64,
+    random permutation page table per row.  The batch is below half a row per
+    CU, yet its widest rows do not all fit the split kernel resident at once:
+    the case a dispatcher that only knows the batch shape has to place.
+    (SGLang PR #26788's commit notes report such valleys for half-long batches
+    and a length-aware schedule as the fix.)"""
+    rng = _rng(seed)
+    B, W, k, ps = 32, 1 << 20, 2048, 64
+    seq = np.full(B, 16384, dtype=np.int32)
+    seq[:4] = W
+    scores = rng.standard_normal((B, W), dtype=np.float32)
+    poison_scores(scores, seq)
+    pt = permutation_table(rng, B, W // ps, seq, ps)
+    return Workload("mixed_b32_4x1M_28x16K_k2048", "batch=32 width=1048576: 4 rows of 1M, 28 of 16K, k=2048 N(0,1) "
+                    "ps=64 permuted table", scores, seq, pt, k, ps, False, seed)
+
+
 CONFIGS = {
     "c1": c1,
     "c2": c2,
@@ -230,6 +249,7 @@ CONFIGS = {
     "c4a": c4a,
     "c4b": c4b,
     "c5": c5,
+    "mixed": mixed,
 }
 
 
