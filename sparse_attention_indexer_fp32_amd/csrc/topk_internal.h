@@ -51,8 +51,7 @@ constexpr size_t kCtrEqual = 16;        // tie slots / candidates appended
 constexpr size_t kCtrExit = 32;         // workgroups done with the row
 constexpr size_t kRegCandKey = kRegCtr + 64;
 constexpr size_t kRegCandPos = kRegCandKey + kCandCap;
-constexpr size_t kRegRaw = kRegCandPos + kCandCap;
-constexpr size_t kRegionWords = kRegRaw + kMaxK;
+constexpr size_t kRegionWords = kRegCandPos + kCandCap;
 
 inline size_t workspace_words(int64_t slots) {
   return kHdrWords + (size_t)slots * kBarWords + (size_t)slots * 2 * kRegionWords;

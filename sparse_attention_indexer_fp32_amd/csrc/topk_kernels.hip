@@ -260,17 +260,18 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, int G, int g, uint32_
 // Gather + transform pass: slot j < n holds raw position r (trivial rows: r = j);
 // out = page_table[row, r >> log2_page] << log2_page | (r & (page_size - 1)).
 // Slots past n, and any r outside [0, L), give -1.  `pt_row` is the row's
-// page table, in global memory or an LDS copy of it.
+// page table, in global memory or an LDS copy of it.  Writes slots [from, k).
 template <int NT>
 __device__ __forceinline__ void write_row_output(const KernelArgs& a, int64_t row, int64_t L, int n, bool trivial,
-                                                 const int32_t* sh_raw, int tid, const int32_t* pt_row = nullptr) {
+                                                 const int32_t* sh_raw, int tid, const int32_t* pt_row = nullptr,
+                                                 int from = 0) {
   const int k = a.k;
   const int s = a.log2_page;
   const uint32_t pmask = (1u << s) - 1u;
   int32_t* o = a.out + row * (int64_t)k;
   int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
   const int32_t* pt = pt_row != nullptr ? pt_row : a.page_table + row * a.pages_per_row;
-  for (int j = tid; j < k; j += NT) {
+  for (int j = from + tid; j < k; j += NT) {
     int32_t r = -1;
     if (j < n) r = trivial ? j : sh_raw[j];
     int32_t v = -1;
@@ -283,6 +284,19 @@ __device__ __forceinline__ void write_row_output(const KernelArgs& a, int64_t ro
     o[j] = v;
     if (orw) orw[j] = r;
   }
+}
+
+// Position r of the row (in [0, L)) straight to output slot j, through the
+// same transform as write_row_output.  Split rows: each workgroup writes the
+// slots its own keys took, so no workgroup gathers the whole row's output.
+__device__ __forceinline__ void write_slot(const KernelArgs& a, int64_t row, uint32_t j, int32_t r) {
+  const int s = a.log2_page;
+  const int64_t pg = (int64_t)(r >> s);
+  int32_t v = -1;
+  if (pg < a.pages_per_row)
+    v = (int32_t)(((uint32_t)a.page_table[row * a.pages_per_row + pg] << s) | ((uint32_t)r & ((1u << s) - 1u)));
+  a.out[row * (int64_t)a.k + j] = v;
+  if (a.out_raw) a.out_raw[row * (int64_t)a.k + j] = r;
 }
 
 // Records how a row's selection ended, for the sorted finish: every key x of
@@ -590,6 +604,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
         const uint32_t tg = tot >> 17, te = tot & 0x1FFFFu;
         sh_var[4] = tg ? g_add_ret(region + kRegCtr + kCtrGreater, tg) : 0u;
         sh_var[5] = te ? g_add_ret(region + kRegCtr + kCtrEqual, te) : 0u;
+        sh_var[7] = 0u;   // this workgroup's (slot, position) pairs staged below
       }
       __syncthreads();
       off_g += uniform(sh_var[4]);
@@ -599,6 +614,15 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     // lanes holds a key at or above the threshold prefix.  Inside, lanes that
     // have nothing to store write a private trash word instead of branching.
     const uint32_t trash = (uint32_t)kMaxK + (uint32_t)(tid & 63);
+    // Split rows stage each final (slot, position) pair in LDS (sh_ckey /
+    // sh_raw; a row has n <= kMaxK slots, so fewer pairs than either holds)
+    // and write them after the loop: a page-table gather per selected key
+    // inside the loop would make each register slot wait out a load.
+    auto stage_slot = [&](uint32_t slot, int32_t pos) {
+      const uint32_t li = atomicAdd(&sh_var[7], 1u);
+      sh_ckey[li] = slot;
+      sh_raw[li] = pos;
+    };
     launder(key);   // recompute the compares here instead of keeping 2E masks from the counting loop
 #pragma unroll
     for (int j = 0; j < E; ++j) {
@@ -614,15 +638,22 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
         const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : trash);
         sh_raw[slot] = pos_of(j);
       } else if (mode == kModeCands) {
-        if (isg && sg < n_gt) g_store(region + kRegRaw + sg, (uint32_t)pos_of(j));
+        if (isg && sg < n_gt) stage_slot(sg, pos_of(j));
         if (ise && se < (uint32_t)kCandCap) {
           g_store(region + kRegCandKey + se, x);
           g_store(region + kRegCandPos + se, (uint32_t)pos_of(j));
         }
       } else {
         const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : 0xFFFFFFFFu);
-        if (slot != 0xFFFFFFFFu) g_store(region + kRegRaw + slot, (uint32_t)pos_of(j));
+        if (slot != 0xFFFFFFFFu) stage_slot(slot, pos_of(j));
       }
+    }
+    if (split) {
+      // The staged slots are final: write them through the page table, every
+      // gather in flight at once.
+      __syncthreads();
+      const uint32_t nsel = uniform(sh_var[7]);
+      for (uint32_t i = (uint32_t)tid; i < nsel; i += kThreads) write_slot(a, row, sh_ckey[i], sh_raw[i]);
     }
 
     if (!split) {
@@ -643,8 +674,9 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     __syncthreads();
     if (!uniform(sh_var[6])) continue;
 
-    const uint32_t filled = mode == kModeCands ? n_gt : (uint32_t)n;
-    for (uint32_t j = tid; j < filled; j += kThreads) sh_raw[j] = (int32_t)g_load(region + kRegRaw + j);
+    // A split row has L > k, so n = k: every slot below n_gt (all n of them
+    // outside the candidates mode) was written by the workgroup whose key
+    // took it; the candidates fill [n_gt, n).
     if (mode == kModeCands) {
       const int ncand = (int)(cnt < (uint32_t)kCandCap ? cnt : (uint32_t)kCandCap);
       for (int i = tid; i < ncand; i += kThreads) {
@@ -654,9 +686,9 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
       __syncthreads();
       select_candidates<kThreads>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
                         sh_scan, sh_var, tid);
+      __syncthreads();
+      write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid, nullptr, (int)n_gt);
     }
-    __syncthreads();
-    write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid);
     if (tid == 0) record_selection(a, row, prefix, shift, need, cnt, 1u);
     // leave the region zeroed for the row this slot handles two iterations on
     for (int b = tid; b < kBinsWide; b += kThreads) g_store(region + kRegHist0 + b, 0u);
