@@ -111,12 +111,24 @@ __device__ __forceinline__ void load_row(const uint8_t* q, const float* weights,
 // scale.  Every lane returns the score of position n = lane % 32 of the tile
 // (both half-waves hold it).  The order of the operations is fixed, so every
 // kernel that calls this gets the same fp32 value.
-__device__ __forceinline__ float finish_score(const RowOperand& op, const f32x16& acc, float scale) {
+//
+// relu is a signed-integer max of the value's bits with 0: negative floats
+// (and -0) have negative bit patterns and become +0, the rest pass unchanged.
+// That is max(x, 0) for every non-NaN x in one instruction (a float max of an
+// accumulator costs a quieting max first); a -0 from the float form could not
+// change the sum either, which starts at +0.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+__device__ __forceinline__ float finish_score(const RowOperand& op, const f32x16& acc, float scale, int lane) {
   float part = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) part = fmaf(op.w[r], fmaxf(acc[r], 0.f), part);
-  // the other 16 heads of the same position sit in lane ^ 32
-  const float other = __shfl_xor(part, 32);
+  for (int r = 0; r < 16; ++r) part = fmaf(op.w[r], relu(acc[r]), part);
+  // The other 16 heads of the same position sit in lane ^ 32.  The swap
+  // exchanges the upper half-wave of its first operand with the lower
+  // half-wave of its second: with both = part, lane l < 32 finds lane l + 32
+  // in the second result and lane l >= 32 finds lane l - 32 in the first.
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+  const float other = __uint_as_float(lane < 32 ? sw[1] : sw[0]);
   return (part + other) * scale;
 }
 
@@ -419,7 +431,7 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
             acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows[i].a[s], b[s], acc[i], 0, 0, 0);
         float score[kRowsPerWave];
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) score[i] = finish_score(rows[i], acc[i], scale);
+        for (int i = 0; i < kRowsPerWave; ++i) score[i] = finish_score(rows[i], acc[i], scale, lane);
         const int64_t j = base + nb;
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
