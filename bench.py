@@ -154,6 +154,26 @@ def counters_run(topk) -> int:
     return 0
 
 
+def indexer_counters_run(topk) -> int:
+    """Dispatches to profile with SQ counters: 2 calls each of the dense
+    scoring kernel and the fused scan on a causal prefill of 1024 query rows
+    over 65536 keys (H 32, D 128, top-2048)."""
+    import numpy as np
+    import torch
+    from workloads import indexer as wl
+    w = wl.make([(1024, 65536)], 2048, seed=99)
+    dev = torch.device("cuda", 0)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, wt, kv, sc, ks, ke = t(w.q), t(w.weights), t(w.kv), t(w.kv_scale), t(w.ks), t(w.ke)
+    for _ in range(2):
+        topk.indexer_logits(q, wt, kv, sc, ks, ke, 65536)
+        topk.indexer_topk(q, wt, kv, sc, ks, ke, w.k)
+    torch.cuda.synchronize()
+    print(json.dumps({"indexer_counters_run": True, "num_q": w.num_q, "num_kv": w.num_kv, "k": w.k,
+                      "calls_each": 2}), flush=True)
+    return 0
+
+
 def indexer_leg(topk, steps: int, warmup: int) -> dict:
     """Fused vs dense indexer scoring + top-k on the prefill shape; HIP-event
     averages over `steps` calls on the stream the calls are queued on."""
@@ -222,6 +242,9 @@ def main() -> int:
     ap.add_argument("--counters", action="store_true",
                     help="only run the headline kernel 4 times on rotated inputs, then 2 plain device copies of "
                          "256 MiB (the calibration for HBM byte counters); for rocprofv3 --pmc passes")
+    ap.add_argument("--indexer-counters", action="store_true",
+                    help="only run the indexer scoring kernels twice each on a 1024 x 65536 prefill; "
+                         "for rocprofv3 --pmc passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the operation is per-row and this build runs on a single "
@@ -238,6 +261,8 @@ def main() -> int:
     props = torch.cuda.get_device_properties(0)
     if args.counters:
         return counters_run(topk)
+    if args.indexer_counters:
+        return indexer_counters_run(topk)
 
     # ---- headline: bandwidth workload (batch 2048 x 65536, k 512) -----------------
     w = workloads.c4a()
