@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 from .build import LIB_PATH
 
 TOPK_MAX_K = 2048
-STREAM_SHAPES = 2   # compiled streaming-kernel shapes: topk_set_stream_shape accepts -1 and 0..STREAM_SHAPES-1
+STREAM_SHAPES = 3   # compiled streaming-kernel shapes: topk_set_stream_shape accepts -1 and 0..STREAM_SHAPES-1
 STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUPPORTED",
           3: "TOPK_ERROR_OUT_OF_MEMORY", 4: "TOPK_ERROR_LAUNCH"}
 

@@ -179,9 +179,12 @@ enum class Kind { kResident, kSplit, kStream };
 constexpr int64_t kMaxSplitWgs = 128;
 
 // Compiled streaming shapes (TOPK_STREAM_VARIANTS): 0 = 1024-thread
-// workgroups with 6144 LDS candidates, 1 = 256-thread workgroups with 1920.
+// workgroups with 6144 LDS candidates, two per CU; 1 = 256-thread workgroups
+// with 1920, four per CU; 2 = 1024-thread workgroups, one per CU, with three
+// 16K-position chunks (192 KB) in flight instead of two 8K ones.
 constexpr int kStreamWide = 0;
 constexpr int kStreamNarrow = 1;
+constexpr int kStreamDeep = 2;
 
 struct Plan {
   Kind kind = Kind::kStream;
@@ -219,11 +222,19 @@ const char* kind_name(Kind k) {
 topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, int32_t k, Plan* plan) {
   const int64_t B = batch;
   const int64_t Wc = width > 0 ? width : 1;
+  // The deep shape for at most one row per two CUs of width >= 128K: each
+  // row's workgroup streams alone, limited by what it keeps in flight
+  // (measured on MI355X: 128 x 128K, k 512: 27.9 against 29.4 us; 128 x 128K
+  // ties, k 1024: 32.5 against 33.9 us; but 256 x 128K: 38.1 against 33.3 us
+  // and 128 x 64K: 24.1 against 23.6 us).
   if (g_stream_variant >= 0)
     plan->stream_variant = g_stream_variant;
+  else if (k <= 512 && B >= (int64_t)dev.stream_occ[kStreamNarrow] * dev.cus)
+    plan->stream_variant = kStreamNarrow;
+  else if (2 * B <= (int64_t)dev.cus && Wc >= 131072)
+    plan->stream_variant = kStreamDeep;
   else
-    plan->stream_variant =
-        (k <= 512 && B >= (int64_t)dev.stream_occ[kStreamNarrow] * dev.cus) ? kStreamNarrow : kStreamWide;
+    plan->stream_variant = kStreamWide;
   const int64_t stream_slots = (int64_t)dev.stream_occ[plan->stream_variant] * dev.cus;
   auto split_ept_for = [&](int64_t wgs) {   // smallest E whose G for this width is <= wgs
     int idx = 0;

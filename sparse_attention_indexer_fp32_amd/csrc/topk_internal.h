@@ -88,7 +88,7 @@ hipError_t rows_occupancy(int ept_index, bool coop, int* blocks_per_cu);
 // Streaming kernel, one workgroup per row, persistent over rows (grid =
 // slots).  `variant` selects one of kNumStreamVariants compiled shapes
 // (threads per workgroup, sample and chunk sizes, LDS candidate capacity).
-constexpr int kNumStreamVariants = 2;
+constexpr int kNumStreamVariants = 3;
 hipError_t launch_stream_rows(int variant, const KernelArgs& args, hipStream_t stream);
 hipError_t stream_occupancy(int variant, int* blocks_per_cu);
 int stream_variant_threads(int variant);

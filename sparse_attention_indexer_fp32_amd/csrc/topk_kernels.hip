@@ -1386,7 +1386,8 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
 // page-table row staged in LDS).
 #define TOPK_STREAM_VARIANTS(X)      \
   X(0, 1024, 4, 2, 2, 6144, 8, false) \
-  X(1, 256, 8, 4, 2, 1920, 4, true)
+  X(1, 256, 8, 4, 2, 1920, 4, true)   \
+  X(2, 1024, 4, 4, 3, 6144, 4, true)
 
 hipError_t launch_stream_variant(int variant, const KernelArgs& args, hipStream_t stream) {
   switch (variant) {
