@@ -159,8 +159,11 @@ topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_p
  *      6144 LDS candidates, 2 workgroups per CU (few rows, k up to 2048,
  *      rows with many tied keys);
  *   1: 256-thread workgroups, 8K-position sample, 4K-position chunks,
- *      1920 LDS candidates, 4 workgroups per CU (large batches, k <= 512).
- * Either shape is exact for every input; the choice only moves time.
+ *      1920 LDS candidates, 4 workgroups per CU (large batches, k <= 512);
+ *   2: 1024-thread workgroups, 16K-position sample, three 16K-position
+ *      chunks in flight, 6144 LDS candidates, 1 workgroup per CU (at most
+ *      one row per two CUs, rows of 128K positions and more).
+ * Every shape is exact for every input; the choice only moves time.
  * Returns TOPK_ERROR_INVALID_VALUE for other values.
  */
 topk_status_t topk_set_stream_shape(int32_t shape);

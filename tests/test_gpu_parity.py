@@ -291,7 +291,7 @@ def test_stream_rows_within_sample_repeated(lib, shape):
     chunks; every one of repeated calls must be exact (regression: the list
     count was once read before every wave's appends were in, which only a
     row without chunks exposed, and only on some calls)."""
-    for W in (16384, 8192, 3001):   # shape 0's sample span, shape 1's, shorter
+    for W in (16384, 8192, 3001):   # the sample span of shapes 0 and 2, shape 1's, shorter
         seq = [W, W - 1, 2000, 600]
         w = workloads.custom(70 + shape, len(seq), W, 512, 64, seq_lens=seq, kind="normal")
         note(f"stream shape={shape} within-sample W={W}")

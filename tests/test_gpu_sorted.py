@@ -61,9 +61,9 @@ def test_sorted_c4a_sampled(lib):
     check_exact(w, out, raw, rows=rows)
 
 
-# every selection path: both streaming shapes, split rows, register-resident rows
-SORTED_SHAPES = [("stream", 0, 1, 0), ("stream", 0, 1, 1), ("split", 4, 3, -1), ("split", 16, 0, -1),
-                 ("resident", 16, 1, -1), ("resident", 64, 1, -1)]
+# every selection path: each streaming shape, split rows, register-resident rows
+SORTED_SHAPES = [("stream", 0, 1, 0), ("stream", 0, 1, 1), ("stream", 0, 1, 2), ("split", 4, 3, -1),
+                 ("split", 16, 0, -1), ("resident", 16, 1, -1), ("resident", 64, 1, -1)]
 
 
 @pytest.mark.parametrize("path,ept,wgs,shape", SORTED_SHAPES)
