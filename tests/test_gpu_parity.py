@@ -174,6 +174,55 @@ def test_split_rows_cycled_over_slots(lib, kind):
     assert lib.topk_debug_fault_word() == 0
 
 
+def test_split_rows_cycled_repeated_and_graph(lib):
+    """Split rows cycled over the slots, several rows per slot: long, short and
+    trivial (L <= k) rows in any order, so each slot's two workspace regions
+    alternate over a mixed sequence; repeated calls with two length patterns,
+    and replays of a captured graph with eager calls between them (every
+    region and barrier must be back to its initial state after each call)."""
+    import re
+    import torch
+    W = 600000
+    rng = np.random.Generator(np.random.PCG64(4242))
+    choices = [W, W // 3, 70000, 20000, 3000, 1500, 0]
+    seqs = [rng.choice(choices, size=80).tolist() for _ in range(2)]
+    ws = [workloads.custom(700 + i, 80, W, 2048, 64, seq_lens=sq, kind="normal", table="perm") for i, sq in
+          enumerate(seqs)]
+    tens = [upload(w) for w in ws]
+    lib.topk_set_dispatch_override(64, 0)
+    try:
+        outs = []
+        for rep in range(3):
+            for w, t in zip(ws, tens):
+                note(f"cycled split rows rep={rep} seed={w.seed}")
+                out, raw = run(lib, w, raw=True, tensors=t)
+                launch = lib.topk_last_launch()
+                m = re.search(r"slots=(\d+)", launch)
+                assert launch.startswith("split-row ept=64") and int(m.group(1)) < w.batch, launch
+                check(w, out, raw)
+        w, (s, sl, pt) = ws[0], tens[0]
+        out = torch.empty((w.batch, w.k), dtype=torch.int32, device=s.device)
+        g = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)   # the side stream's workspace
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)
+        for rep in range(4):
+            note(f"cycled split rows graph replay {rep}")
+            out.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            check(w, out.cpu().numpy(), None)
+            w2 = ws[1]
+            out2, raw2 = run(lib, w2, raw=True, tensors=tens[1])   # eager queued call between replays
+            check(w2, out2, raw2)
+    finally:
+        lib.topk_set_dispatch_override(0, 0)
+    assert lib.topk_debug_fault_word() == 0
+
+
 def test_graph_replay(lib):
     """Calls captured in a HIP graph and replayed give the eager result every time."""
     import torch
