@@ -484,7 +484,10 @@ __device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* r
   for (int j = 0; j < 4 * V; ++j) key[j] = slot_key<NT>(key[j], j, cbase, L, tid);
 }
 
-template <int E, bool COOP>
+// SHORT (split kernel, rows cycled over slots): rows that fit one
+// workgroup run in one workgroup of the slot (below).  A separate
+// instantiation, so the one-pass split kernel keeps its split-only code.
+template <int E, bool COOP, bool SHORT>
 __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
   __shared__ uint32_t sh_hist[kBinsWide];
   __shared__ int32_t sh_raw[kMaxK + 64];   // + one trash word per lane
@@ -511,12 +514,20 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
     const int64_t L = sl < 0 ? 0 : ((int64_t)sl > W ? W : (int64_t)sl);
     const int n = L < (int64_t)k ? (int)L : k;
+    // Rows that need no cross-workgroup merge -- every position selected
+    // (L <= k), or, with SHORT, the row fits one workgroup's registers
+    // (L <= C) -- run in one workgroup of the slot, the it-th row's in
+    // workgroup it % G, so a run of them spreads over the slot; the slot's
+    // other workgroups go on to its next row (whose first barrier, if it is
+    // split, waits for this one).
+    const int owner = SHORT ? it % G : 0;
     if (L <= (int64_t)k) {  // every valid position is selected (uniform over the row's workgroups)
-      if (g == 0) write_row_output<kThreads>(a, row, L, n, true, sh_raw, tid);
-      if (g == 0 && tid == 0) record_selection(a, row, 0u, 32, (uint32_t)n, (uint32_t)n, 0u);
+      if (g == owner) write_row_output<kThreads>(a, row, L, n, true, sh_raw, tid);
+      if (g == owner && tid == 0) record_selection(a, row, 0u, 32, (uint32_t)n, (uint32_t)n, 0u);
       continue;
     }
-    constexpr bool split = COOP;   // the host launches the split kernel only with G > 1
+    const bool split = COOP && (!SHORT || L > C);   // the host launches the split kernel only with G > 1
+    if (SHORT && !split && g != owner) continue;
     // Consecutive split rows of a slot alternate regions.  A region is reused
     // two split rows later, after every workgroup of the slot has passed the
     // in-between row's first barrier -- which the finisher that clears it
@@ -530,7 +541,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 
     // ---- load this workgroup's share of the row into registers (one HBM read)
     const float* rowp = a.scores + row * W;
-    const uint32_t c0 = (uint32_t)g * (uint32_t)C;
+    const uint32_t c0 = split ? (uint32_t)g * (uint32_t)C : 0u;
     const uint32_t pbase = c0 + (uint32_t)tid * 4u;
     uint32_t key[E];
     load_keys<kThreads, E / 4>(key, rowp, c0, (uint32_t)L, a.vec != 0, tid);
@@ -1422,20 +1433,32 @@ hipError_t launch_e(bool coop, const KernelArgs& args, hipStream_t stream) {
   const dim3 block(kThreads);
   if (coop) {
     const dim3 grid((unsigned)args.slots * (unsigned)args.wgs_per_row);
-    hipLaunchKernelGGL((rows_kernel<E, true>), grid, block, 0, stream, args);
+    if (args.slots < args.batch)
+      hipLaunchKernelGGL((rows_kernel<E, true, true>), grid, block, 0, stream, args);
+    else
+      hipLaunchKernelGGL((rows_kernel<E, true, false>), grid, block, 0, stream, args);
   } else {
     const dim3 grid((unsigned)args.slots);
-    hipLaunchKernelGGL((rows_kernel<E, false>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((rows_kernel<E, false, false>), grid, block, 0, stream, args);
   }
   return hipGetLastError();
 }
 
 template <int E>
 hipError_t occupancy_e(bool coop, int* blocks) {
-  if (coop)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, reinterpret_cast<const void*>(&rows_kernel<E, true>),
-                                                        kThreads, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, reinterpret_cast<const void*>(&rows_kernel<E, false>),
+  if (coop) {
+    // the grid is sized once for both split instantiations: the smaller
+    // residency holds for either
+    int one_pass = 0, cycled = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &one_pass, reinterpret_cast<const void*>(&rows_kernel<E, true, false>), kThreads, 0);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&cycled, reinterpret_cast<const void*>(&rows_kernel<E, true, true>),
+                                                       kThreads, 0);
+    *blocks = one_pass < cycled ? one_pass : cycled;
+    return e;
+  }
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, reinterpret_cast<const void*>(&rows_kernel<E, false, false>),
                                                       kThreads, 0);
 }
 
