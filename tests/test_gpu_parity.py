@@ -140,6 +140,36 @@ def test_batch_zero_and_width_zero(lib):
     assert (out.cpu() == -1).all() and (raw.cpu() == -1).all()
 
 
+@pytest.mark.parametrize("ept,wgs", [(0, 1), (32, 0), (8, 0)])   # streaming, resident, split
+def test_empty_page_table(lib, ept, wgs):
+    """pages_per_row = 0 (the ABI then allows a null page table): every
+    transformed slot is -1, while the raw positions are the usual exact set."""
+    import ctypes
+    import torch
+    W = 20000
+    seq = [W, 5000, 100, 0]
+    w = workloads.custom(808, len(seq), W, 512, 64, seq_lens=seq, kind="normal")
+    s, sl, _ = upload(w)
+    out = torch.full((w.batch, w.k), -7, dtype=torch.int32, device=s.device)
+    raw = torch.full((w.batch, w.k), -7, dtype=torch.int32, device=s.device)
+    lib.topk_set_dispatch_override(ept, wgs)
+    try:
+        st = lib.load().topk_transform(ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(sl.data_ptr()), None,
+                                       w.k, w.page_size, ctypes.c_void_p(out.data_ptr()),
+                                       ctypes.c_void_p(raw.data_ptr()),
+                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), w.batch, W, 0)
+        assert st == 0, lib.topk_last_error()
+        torch.cuda.synchronize()
+    finally:
+        lib.topk_set_dispatch_override(0, 0)
+    assert (out.cpu().numpy() == -1).all()
+    # the raw positions against the oracle, with a table that maps every page to itself
+    got_raw = raw.cpu().numpy()
+    ident = np.broadcast_to(np.arange(-(-W // w.page_size), dtype=np.int32), (w.batch, -(-W // w.page_size))).copy()
+    check(workloads.Workload(w.name, w.description, w.scores, w.seq_lens, ident, w.k, w.page_size, True, w.seed),
+          got_raw, got_raw)
+
+
 def test_repeated_split_rows_stress(lib):
     """The cross-workgroup path, many times with fresh seeds (race check)."""
     for rep in range(40):
