@@ -24,14 +24,22 @@
 //     global candidate list and the last workgroup to leave the row finishes
 //     the remaining digits on the candidates in LDS -- one barrier per row
 //     instead of one per digit.
-//   * Selected positions go to a staging list (LDS, or global when the row is
-//     split); after a barrier one pass gathers the page-table entries and
-//     writes out_idx / out_raw coalesced, -1 padded.
+//   * Selected positions go to a staging list in LDS; after a barrier one
+//     pass gathers the page-table entries and writes out_idx / out_raw, -1
+//     padded.  A split row's workgroups each write the slots their own keys
+//     took (one batched gather per workgroup), and the finisher only the
+//     slots it fills from the candidates.
+//   * When more rows than slots fit resident, rows cycle over the slots; in
+//     that launch a row that fits one workgroup runs in one workgroup of its
+//     slot, with no cross-workgroup merge.
 //   * Large batches stream instead (stream_rows_kernel): one workgroup per
 //     row, a gate set from a sample of the row, the keys at or above it
 //     appended to an LDS candidate list while the rest of the row streams
-//     past in two register-held chunks; the radix digits then run on the
-//     list.  Rows past the grid come from a ticket queue.
+//     past in register-held chunks (two or three in flight); the radix
+//     digits then run on the list.  Rows past the grid come from a ticket
+//     queue.
+//   * A row's scores are read once, with non-temporal loads; only the
+//     fallback re-stream and the sorted finish read a row again.
 //   * The deterministic entry point adds a second launch (sorted_rows_kernel)
 //     that puts each row's selection in the plain definition's order.
 
