@@ -88,11 +88,12 @@ typedef enum topk_status_t {
  * pages_per_row gets -1 in out_idx (its raw position is still written).
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer past
- * the call.  Rows long enough to be split across workgroups use an internal
- * per-(device, stream) workspace that the library allocates on first need,
- * keeps zeroed between calls, and frees in topk_release_workspaces().  The
- * first call that needs a larger workspace synchronises `stream` (so do not
- * make that first call under stream capture).
+ * the call.  Rows split across workgroups, and batches with more rows than
+ * the streaming kernel's grid, use an internal per-(device, stream) workspace
+ * that the library allocates on first need, keeps in its initial state
+ * between calls, and frees in topk_release_workspaces().  The first call
+ * that needs a larger workspace synchronises `stream` (so do not make that
+ * first call under stream capture).
  *
  * Completion is asynchronous: outputs are valid once `stream` reaches the call.
  * Returns TOPK_SUCCESS, or an error status; on error nothing was queued.
@@ -114,8 +115,10 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
  * launch and device state.  out_idx[b, j] is the transform of out_raw[b, j];
  * slots [n_b, k) are -1.
  *
- * Cost: the row is selected as by topk_transform, then read once more from
- * memory, and the n_b chosen pairs are sorted in LDS (a bitonic network).
+ * Cost: the row is selected as by topk_transform; then the selected
+ * positions' scores are gathered (when ties at the threshold value are cut,
+ * the row is read once more to take the lowest tied positions), and the n_b
+ * chosen pairs are sorted in LDS (a bitonic network).
  * Besides the workspace, one 16-byte record per row is kept per (device,
  * stream) between the two launches; it is allocated on first use (call once
  * outside graph capture), grown on demand, and freed by

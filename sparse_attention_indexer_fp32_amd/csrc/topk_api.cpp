@@ -9,7 +9,9 @@
 // length (SGLang PR #26788 commit notes: one block per row at large batch,
 // several cooperating blocks per row for long rows at small batch), with the
 // thresholds measured on MI355X (256 CUs): streaming from half a row per CU
-// up, register-resident rows for a few short ones, split rows otherwise.
+// up, register-resident rows for a few short ones, split rows otherwise --
+// cycled over the resident slots when they do not all fit at once and that
+// is estimated faster than streaming them.
 
 #include <hip/hip_runtime_api.h>
 
