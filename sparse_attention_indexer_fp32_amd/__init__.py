@@ -134,11 +134,16 @@ def _call(fn, scores, seq_lens, page_table, k, page_size, out, out_raw, want_raw
         raise ValueError("out_raw must be a contiguous int32 tensor of shape (B, k)")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    with torch.cuda.device(dev):
-        st = fn(scores.data_ptr(), seq_lens.data_ptr(), page_table.data_ptr(), int(k),
-                                int(page_size), out.data_ptr(),
-                                out_raw.data_ptr() if out_raw is not None else None,
-                                ctypes.c_void_p(stream.cuda_stream), int(B), int(W), int(page_table.shape[1]))
+    args = (scores.data_ptr(), seq_lens.data_ptr(), page_table.data_ptr(), int(k), int(page_size), out.data_ptr(),
+            out_raw.data_ptr() if out_raw is not None else None, ctypes.c_void_p(stream.cuda_stream), int(B), int(W),
+            int(page_table.shape[1]))
+    # The library works on the current device: switch only when the tensors
+    # live on another one (the switch costs a device get/set round trip).
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        st = fn(*args)
+    else:
+        with torch.cuda.device(dev):
+            st = fn(*args)
     _check(st)
     return out, out_raw
 
