@@ -238,10 +238,17 @@ __device__ void list_hist(const float* sc, int count, uint32_t* hist, int lane, 
 // of those equal to T, need entries in all, and sets gate = T + 1.  Otherwise,
 // when the 11-bit bin holding the need-th key leaves at most `room` entries at
 // or above its lower edge, it keeps those and sets gate = that edge.  Returns
-// the new count.  The list's earlier stores of this wave are made visible to
-// its loads first.
-__device__ __attribute__((noinline)) int compact_list(float* sc, int32_t* ps, int count, uint32_t need, int room, bool exact_only,
-                            uint32_t* hist, int lane, uint32_t* gate) {
+// the new count and gate by value: a gate passed by address would keep the
+// caller's gate in scratch memory, and every gate test would then reload it
+// and wait on the load counter, i.e. on the key stages still in flight.  The
+// list's earlier stores of this wave are made visible to its loads first.
+struct Trimmed {
+  int count;
+  uint32_t gate;
+};
+
+__device__ __attribute__((noinline)) Trimmed compact_list(float* sc, int32_t* ps, int count, uint32_t need, int room,
+                                                          bool exact_only, uint32_t* hist, int lane) {
   __threadfence();
   uint32_t above = 0, in_bin = 0;
   list_hist(sc, count, hist, lane, 21, 0x7FF, 32, 0);
@@ -299,8 +306,7 @@ __device__ __attribute__((noinline)) int compact_list(float* sc, int32_t* ps, in
       out += __builtin_popcountll(km);
     }
   }
-  *gate = new_gate;
-  return out;
+  return Trimmed{out, new_gate};
 }
 
 }  // namespace
@@ -470,9 +476,12 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
         }
         count[i] += staged[i];
         staged[i] = 0;
-        if (count[i] > a.cap - kStage && count[i] > a.k)
-          count[i] = compact_list(list_score(i), list_pos(i), count[i], (uint32_t)a.k, a.cap / 2, false,
-                                  sh_hist[wave], lane, &gate[i]);
+        if (count[i] > a.cap - kStage && count[i] > a.k) {
+          const Trimmed t = compact_list(list_score(i), list_pos(i), count[i], (uint32_t)a.k, a.cap / 2, false,
+                                         sh_hist[wave], lane);
+          count[i] = t.count;
+          gate[i] = t.gate;
+        }
       }
     };
     // Two stages in flight in registers: the stage computed now, the next one
@@ -506,7 +515,7 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
       float* lsc = list_score(i);
       int32_t* lps = list_pos(i);
       if (count[i] > a.k)
-        count[i] = compact_list(lsc, lps, count[i], (uint32_t)a.k, 0, true, sh_hist[wave], lane, &gate[i]);
+        count[i] = compact_list(lsc, lps, count[i], (uint32_t)a.k, 0, true, sh_hist[wave], lane).count;
       if (count[i] == 0) continue;
       int off = 0;
       if (lane == 0) off = atomicAdd(&a.row_count[rix[i]], count[i]);
