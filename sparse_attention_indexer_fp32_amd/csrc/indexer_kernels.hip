@@ -209,7 +209,7 @@ __device__ __forceinline__ void clear_hist(uint32_t* hist, int bins, int lane) {
 // The list passes keep kListBatch loads per lane in flight: the list was just
 // written and its reads come from L2, so one load at a time would make a trim
 // a chain of memory latencies while the workgroup's other waves wait.
-constexpr int kListBatch = 8;
+constexpr int kListBatch = 16;
 
 __device__ void list_hist(const float* sc, int count, uint32_t* hist, int lane, int shift, uint32_t mask,
                           int match_shift, uint32_t match) {
@@ -236,8 +236,9 @@ __device__ void list_hist(const float* sc, int count, uint32_t* hist, int lane, 
 // Shrinks a list of `count` > need entries.  Exact mode keeps every entry
 // whose key is above the need-th largest key T and the first (in list order)
 // of those equal to T, need entries in all, and sets gate = T + 1.  Otherwise,
-// when the 11-bit bin holding the need-th key leaves at most `room` entries at
-// or above its lower edge, it keeps those and sets gate = that edge.  Returns
+// when the 11-bit (else the 22-bit) key prefix bin holding the need-th key
+// leaves at most `room` entries at or above its lower edge, it keeps those
+// and sets gate = that edge.  Returns
 // the new count and gate by value: a gate passed by address would keep the
 // caller's gate in scratch memory, and every gate test would then reload it
 // and wait on the load counter, i.e. on the key stages still in flight.  The
@@ -265,13 +266,19 @@ __device__ __attribute__((noinline)) Trimmed compact_list(float* sc, int32_t* ps
     list_hist(sc, count, hist, lane, 10, 0x7FF, 21, t1);
     const uint32_t t2 = (uint32_t)find_bin(hist, 2048, need - above, lane, &above2, &in2);
     const uint32_t p2 = (t1 << 11) | t2;
-    list_hist(sc, count, hist, lane, 0, 0x3FF, 10, p2);
-    const uint32_t t3 = (uint32_t)find_bin(hist, 1024, need - above - above2, lane, &above3, &in3);
-    const uint32_t T = (p2 << 10) | t3;
-    lo_key = T;
-    eq_key = T;
-    eq_need = need - above - above2 - above3;
-    new_gate = T == 0xFFFFFFFFu ? T : T + 1;
+    if (!exact_only && above + above2 + in2 <= (uint32_t)room) {
+      // the 22-bit bin's lower edge already leaves at most `room` entries
+      lo_key = p2 << 10;
+      new_gate = lo_key;
+    } else {
+      list_hist(sc, count, hist, lane, 0, 0x3FF, 10, p2);
+      const uint32_t t3 = (uint32_t)find_bin(hist, 1024, need - above - above2, lane, &above3, &in3);
+      const uint32_t T = (p2 << 10) | t3;
+      lo_key = T;
+      eq_key = T;
+      eq_need = need - above - above2 - above3;
+      new_gate = T == 0xFFFFFFFFu ? T : T + 1;
+    }
   }
   // In place and order-preserving.  A batch is loaded before any of it is
   // written, and the entries of element b of a batch go to indices below
@@ -316,7 +323,7 @@ constexpr int kStage = 2 * kTile;
 constexpr int kStageBytesBf16 = kStage * kDim * 2;   // 16 KB
 
 // One thread's share of a stage in flight: 32 fp8 bytes of position t / 4
-// (dims (t % 4) * 32 ..) and, for t % 4 == 0, that position's scale.
+// (dims (t % 4) * 32 ..) and that position's scale (staged by t % 4 == 0).
 struct Ring {
   uint4 r0, r1;
   float s;
@@ -392,18 +399,19 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
 
   if (span_lo < span_hi) {
     const int sn = tid >> 2, sc = tid & 3;
+    // The loads are issued unconditionally (a position past the key range
+    // reads position num_kv - 1 instead; num_kv >= 1 since the span is not
+    // empty): loads under a branch leave the compiler unsure how many are in
+    // flight, and its wait for a stage then drains the younger stage too.
+    // Scores of such positions are never used: every use checks the row's
+    // range, and a stage at or past span_hi is never computed.
     auto fetch = [&](Ring& R, int64_t base) {
-      const int64_t j = base + sn;
-      if (base < span_hi && j < a.num_kv) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.kv + j * kDim + sc * 32);
-        R.r0 = src[0];
-        R.r1 = src[1];
-        R.s = sc == 0 ? a.kv_scale[j] : 0.f;
-      } else {
-        R.r0 = uint4{0, 0, 0, 0};
-        R.r1 = uint4{0, 0, 0, 0};
-        R.s = 0.f;
-      }
+      int64_t j = base + sn;
+      j = j < a.num_kv ? j : a.num_kv - 1;
+      const uint4* src = reinterpret_cast<const uint4*>(a.kv + j * kDim + sc * 32);
+      R.r0 = src[0];
+      R.r1 = src[1];
+      R.s = a.kv_scale[j];
     };
     auto stage = [&](const Ring& R, int buf) {
       uint8_t* t = sh_tile[buf];
@@ -446,8 +454,7 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
             const int64_t c = j - rr[i].lo;
             if (valid && c < a.logits_stride) a.logits[rix[i] * a.logits_stride + c] = score[i];
           } else {
-            // staged in LDS; flush() writes them to the list once the next
-            // loads are issued, so no wait on their stores stalls the loop
+            // staged in LDS; flush() writes them to the list once per stage
             const uint32_t key = order_key(score[i]);
             const bool pass = valid && key >= gate[i];
             const uint64_t m = __ballot(pass);
@@ -462,7 +469,10 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
       }
     };
     // Appends the staged entries to the lists (at most kStage per row per
-    // stage), then trims any list that could not take another stage.  Either
+    // stage), then trims any list that could not take another stage.  It runs
+    // before the next stage's loads are issued: the load counter counts stores
+    // too, in issue order, so stores issued after those loads would make the
+    // wait for the stage before them wait for them as well.  Either
     // the list is shorter than its window (then it cannot overflow, and a trim
     // happens only above k entries) or its capacity is at least 4k and 4096,
     // so a trim leaves it at most half full.
@@ -485,7 +495,11 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
       }
     };
     // Two stages in flight in registers: the stage computed now, the next one
-    // already in LDS, and the two after it loading.
+    // already in LDS, and the two after it loading.  The loop has no exit in
+    // its middle (the second stage of a pair past the span is skipped, and
+    // its loads stay in bounds): the compiler merges the load counts of every
+    // path into the loop head, and an early exit path would make the wait
+    // for a stage drain the younger stage as well.
     Ring r0, r1;
     fetch(r0, span_lo);
     stage(r0, 0);
@@ -495,14 +509,13 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
     for (int64_t base = span_lo; base < span_hi; base += 2 * kStage) {
       compute(base, 0);
       stage(r1, 1);
+      if (kFused) flush();
       fetch(r1, base + 3 * kStage);
-      if (kFused) flush();
       __syncthreads();
-      if (base + kStage >= span_hi) break;
-      compute(base + kStage, 1);
+      if (base + kStage < span_hi) compute(base + kStage, 1);
       stage(r0, 0);
-      fetch(r0, base + 4 * kStage);
       if (kFused) flush();
+      fetch(r0, base + 4 * kStage);
       __syncthreads();
     }
   }
