@@ -120,6 +120,32 @@ def test_logits_every_fp8_code(lib):
     assert np.array_equal(got, np.maximum(v, 0) + 2 * np.maximum(-v, 0))
 
 
+def test_logits_narrower_than_rows(lib):
+    """An output narrower than some rows: each row's first min(length, width)
+    scores are written, within the bound, and nothing past them (a write past
+    a row's width would land in the next row's columns)."""
+    import torch
+    w = wl.make([(5, 3000)], 256, seed=7250)
+    w.ks = np.array([0, 100, 2000, -50, 2990], np.int32)
+    w.ke = np.array([3000, 2100, 9999, 700, 3000], np.int32)
+    _, L = _lengths(w)
+    width = 777   # below rows 0..2, above rows 3 and 4; not a multiple of 32
+    note(f"indexer_logits narrower output width={width}")
+    out = torch.full((w.num_q, width), float("nan"), dtype=torch.float32, device="cuda")
+    lib.indexer_logits(*_upload(w), width, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for r in range(w.num_q):
+        n = int(min(L[r], width))
+        pos = ix.key_range(int(w.ks[r]), int(w.ke[r]), w.num_kv)
+        exact = ix.indexer_scores_row(w.q[r], w.weights[r], w.kv, w.kv_scale, pos)[:n]
+        bound = ix.fp32_error_bound(w.q[r], w.weights[r], w.kv, w.kv_scale, pos)[:n]
+        g = got[r, :n].astype(np.float64)
+        assert np.all(np.isfinite(g)), f"row {r}: unwritten logits"
+        assert np.all(np.abs(g - exact) <= bound), f"row {r}: logits outside the bound"
+        assert np.all(np.isnan(got[r, n:])), f"row {r}: written past min(length, width)"
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_indexer_topk_vs_oracle(lib, name):
     import torch
