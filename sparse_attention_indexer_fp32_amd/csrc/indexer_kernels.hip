@@ -321,6 +321,9 @@ __device__ __attribute__((noinline)) Trimmed compact_list(float* sc, int32_t* ps
 // Key positions staged per barrier: two 32-position MFMA tiles.
 constexpr int kStage = 2 * kTile;
 constexpr int kStageBytesBf16 = kStage * kDim * 2;   // 16 KB
+// Appends held in LDS per (wave, row) before they go to the global list:
+// room for two stages' worth beyond the stage being computed.
+constexpr int kAppendCap = 3 * kStage;
 
 // One thread's share of a stage in flight: 32 fp8 bytes of position t / 4
 // (dims (t % 4) * 32 ..) and that position's scale (staged by t % 4 == 0).
@@ -335,8 +338,8 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
   __shared__ float sh_scale[2][kStage];
   __shared__ uint32_t sh_hist[kFused ? kWaves : 1][kFused ? kHistBins : 1];
   // a stage's appends, per wave and row, before they go to the global list
-  __shared__ float sh_app_score[kFused ? kWaves : 1][kRowsPerWave][kFused ? kStage : 1];
-  __shared__ int32_t sh_app_pos[kFused ? kWaves : 1][kRowsPerWave][kFused ? kStage : 1];
+  __shared__ float sh_app_score[kFused ? kWaves : 1][kRowsPerWave][kFused ? kAppendCap : 1];
+  __shared__ int32_t sh_app_pos[kFused ? kWaves : 1][kRowsPerWave][kFused ? kAppendCap : 1];
   __shared__ int64_t sh_span[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -454,7 +457,7 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
             const int64_t c = j - rr[i].lo;
             if (valid && c < a.logits_stride) a.logits[rix[i] * a.logits_stride + c] = score[i];
           } else {
-            // staged in LDS; flush() writes them to the list once per stage
+            // staged in LDS; flush() writes them to the list
             const uint32_t key = order_key(score[i]);
             const bool pass = valid && key >= gate[i];
             const uint64_t m = __ballot(pass);
@@ -468,21 +471,25 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
         }
       }
     };
-    // Appends the staged entries to the lists (at most kStage per row per
-    // stage), then trims any list that could not take another stage.  It runs
-    // before the next stage's loads are issued: the load counter counts stores
-    // too, in issue order, so stores issued after those loads would make the
-    // wait for the stage before them wait for them as well.  Either
-    // the list is shorter than its window (then it cannot overflow, and a trim
-    // happens only above k entries) or its capacity is at least 4k and 4096,
-    // so a trim leaves it at most half full.
-    auto flush = [&]() {
+    // Runs after every stage (at most kStage appends per row).  A row's
+    // staged appends go to its list once they could not take another stage,
+    // or when the list with them could not (or `all`, at the end); then a
+    // list that could not take another stage is trimmed.  Between stages
+    // with few appends (after the first fill, a few per stage) nothing is
+    // written.  It runs before the next stage's loads are issued: the load
+    // counter counts stores too, in issue order, so stores issued after those
+    // loads would make the wait for the stage before them wait for them as
+    // well.  Either the list is shorter than its window (then it cannot
+    // overflow, and a trim happens only above k entries) or its capacity is
+    // at least 4k and 4096, so a trim leaves it at most half full.
+    auto flush = [&](bool all) {
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         if (staged[i] == 0) continue;   // wave-uniform
-        if (lane < staged[i]) {
-          list_score(i)[count[i] + lane] = sh_app_score[wave][i][lane];
-          list_pos(i)[count[i] + lane] = sh_app_pos[wave][i][lane];
+        if (!all && staged[i] <= kAppendCap - kStage && count[i] + staged[i] <= a.cap - kStage) continue;
+        for (int e = lane; e < staged[i]; e += 64) {
+          list_score(i)[count[i] + e] = sh_app_score[wave][i][e];
+          list_pos(i)[count[i] + e] = sh_app_pos[wave][i][e];
         }
         count[i] += staged[i];
         staged[i] = 0;
@@ -509,15 +516,16 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
     for (int64_t base = span_lo; base < span_hi; base += 2 * kStage) {
       compute(base, 0);
       stage(r1, 1);
-      if (kFused) flush();
+      if (kFused) flush(false);
       fetch(r1, base + 3 * kStage);
       __syncthreads();
       if (base + kStage < span_hi) compute(base + kStage, 1);
       stage(r0, 0);
-      if (kFused) flush();
+      if (kFused) flush(false);
       fetch(r0, base + 4 * kStage);
       __syncthreads();
     }
+    if (kFused) flush(true);
   }
 
   if (kFused) {
