@@ -23,11 +23,11 @@
 // within a few fp32 rounding errors of the exact value, at half the fp8 peak.
 //
 // Tiling.  A workgroup of 4 waves owns 8 query rows (2 per wave, their q held
-// in registers as bf16) and a window of key positions.  Key tiles of 32
-// positions are loaded once per workgroup (16 bytes per thread), widened to
-// bf16 into LDS (double-buffered, 16-byte chunks XOR-swizzled by position so
-// the 32 positions a half-wave reads fall in different banks), and read by
-// all four waves.  The epilogue (relu, head weights, the partner half-wave's
+// in registers as bf16) and a window of key positions.  Key stages of 64
+// positions (two 32-position tiles) are loaded once per workgroup (32 bytes
+// per thread, two stages ahead), widened to bf16 into LDS (double-buffered,
+// 16-byte chunks XOR-swizzled by position so the 32 positions a half-wave
+// reads fall in different banks), and read by all four waves.  The epilogue (relu, head weights, the partner half-wave's
 // 16 heads, the position's scale) runs on the accumulator registers.
 
 #include <hip/hip_runtime.h>
@@ -238,11 +238,11 @@ __device__ void list_hist(const float* sc, int count, uint32_t* hist, int lane, 
 // of those equal to T, need entries in all, and sets gate = T + 1.  Otherwise,
 // when the 11-bit (else the 22-bit) key prefix bin holding the need-th key
 // leaves at most `room` entries at or above its lower edge, it keeps those
-// and sets gate = that edge.  Returns
-// the new count and gate by value: a gate passed by address would keep the
-// caller's gate in scratch memory, and every gate test would then reload it
-// and wait on the load counter, i.e. on the key stages still in flight.  The
-// list's earlier stores of this wave are made visible to its loads first.
+// and sets gate = that edge.  Returns the new count and gate by value: a gate
+// passed by address would keep the caller's gate in scratch memory, and every
+// gate test would then reload it and wait on the load counter, i.e. on the
+// key stages still in flight.  The list's earlier stores of this wave are
+// made visible to its loads first.
 struct Trimmed {
   int count;
   uint32_t gate;
