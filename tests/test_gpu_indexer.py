@@ -168,6 +168,8 @@ def test_indexer_topk_vs_oracle(lib, name):
     ([(8, 40000)], 16, 4, 1 << 20),          # four distinct key rows: crowded bins, exact trims
     ([(3, 70000), (5, 9000)], 300, 64, 1 << 20),
     ([(3, 70000), (5, 9000)], 300, 64, 8192),
+    ([(8, 40000)], 1, None, 1 << 20),         # k = 1
+    ([(8, 40000)], 1, 4, 1 << 20),            # k = 1 among crowded ties
 ])
 def test_indexer_topk_trims(lib, requests, k, distinct, window):
     """Rows much longer than the candidate capacity, so the lists are trimmed
@@ -182,6 +184,30 @@ def test_indexer_topk_trims(lib, requests, k, distinct, window):
         w.kv = rows[rng.integers(0, distinct, w.num_kv)]
         w.kv_scale = np.ones(w.num_kv, np.float32)
     note(f"indexer_topk trims requests={requests} k={k} distinct={distinct} window={window}")
+    tensors = _upload(w)
+    out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    try:
+        lib.indexer_topk(*tensors, w.k, out=out)
+        torch.cuda.synchronize()
+    finally:
+        lib.indexer_set_window_override(0)
+    o = out.cpu().numpy()
+    _check_topk(w, o, range(w.num_q))
+    _check_exact_on_logits(w, o, _logits(lib, w, tensors))
+
+
+@pytest.mark.parametrize("k", [1, 512])
+def test_indexer_topk_narrow_scores(lib, k):
+    """Every key is the same vector, scaled by a distinct factor in [1, 1.1):
+    a row's scores share one or two 11-bit key bins but differ in the next
+    digits, so the trims cut at a 22-bit bin edge instead."""
+    import torch
+    lib.indexer_set_window_override(1 << 20)
+    w = wl.make([(8, 65536)], k, seed=7400 + k)
+    rng = np.random.default_rng(7400 + k)
+    w.kv = np.repeat(w.kv[:1], w.num_kv, axis=0)
+    w.kv_scale = rng.uniform(1.0, 1.1, w.num_kv).astype(np.float32)
+    note(f"indexer_topk narrow scores k={k}")
     tensors = _upload(w)
     out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
     try:
