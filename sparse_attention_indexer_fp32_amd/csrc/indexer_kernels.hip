@@ -211,6 +211,20 @@ __device__ __forceinline__ void clear_hist(uint32_t* hist, int bins, int lane) {
 // a chain of memory latencies while the workgroup's other waves wait.
 constexpr int kListBatch = 16;
 
+// Gate bins: per (wave, row), kGateBins counters over [lo, lo + kGateBins << shift)
+// of the order key, the last one also counting every key above.  A trim sets
+// lo = the new gate, fits shift so the bins reach the kept list's
+// (need/4)-th largest key, and counts the kept entries; the list writes count
+// the new ones.  The gate may then rise to the highest bin edge with `need`
+// list entries at or above it: every position it skips has `need` entries at
+// least as large.  shift = 32 marks the bins as unset (before a first trim).
+constexpr int kGateBins = 48;
+
+__device__ __forceinline__ uint32_t gate_bin(uint32_t key, uint32_t lo, uint32_t shift) {
+  const uint64_t b = (uint64_t)(key - lo) >> shift;
+  return b < (uint64_t)(kGateBins - 1) ? (uint32_t)b : (uint32_t)(kGateBins - 1);
+}
+
 __device__ void list_hist(const float* sc, int count, uint32_t* hist, int lane, int shift, uint32_t mask,
                           int match_shift, uint32_t match) {
   clear_hist(hist, (int)mask + 1 < 64 ? 64 : (int)mask + 1, lane);
@@ -243,17 +257,28 @@ __device__ void list_hist(const float* sc, int count, uint32_t* hist, int lane, 
 // gate test would then reload it and wait on the load counter, i.e. on the
 // key stages still in flight.  The list's earlier stores of this wave are
 // made visible to its loads first.
+// The gate returned is at least cur_gate (a valid gate stays valid: the
+// trim keeps every entry at or above it that the k-th largest key needs).
+// With gbins, the gate bins are refitted to the kept list (see kGateBins).
 struct Trimmed {
   int count;
   uint32_t gate;
+  uint32_t bins_lo, bins_shift;
 };
 
 __device__ __attribute__((noinline)) Trimmed compact_list(float* sc, int32_t* ps, int count, uint32_t need, int room,
-                                                          bool exact_only, uint32_t* hist, int lane) {
+                                                          bool exact_only, uint32_t* hist, int lane, uint32_t cur_gate,
+                                                          uint32_t* gbins) {
   __threadfence();
   uint32_t above = 0, in_bin = 0;
   list_hist(sc, count, hist, lane, 21, 0x7FF, 32, 0);
   const uint32_t t1 = (uint32_t)find_bin(hist, 2048, need, lane, &above, &in_bin);
+  uint64_t bins_top = 0;   // above the kept list's (need/4)-th largest key
+  if (gbins != nullptr) {
+    uint32_t aq = 0, iq = 0;
+    const uint32_t tq = (uint32_t)find_bin(hist, 2048, need / 4 > 0 ? need / 4 : 1, lane, &aq, &iq);
+    bins_top = ((uint64_t)tq + 1) << 21;
+  }
   uint32_t lo_key;   // keep keys >= lo_key (all) ...
   uint32_t eq_key = 0;   // ... except that only the first `eq_need` equal to eq_key are kept
   uint32_t eq_need = 0xFFFFFFFFu;
@@ -279,6 +304,17 @@ __device__ __attribute__((noinline)) Trimmed compact_list(float* sc, int32_t* ps
       eq_need = need - above - above2 - above3;
       new_gate = T == 0xFFFFFFFFu ? T : T + 1;
     }
+  }
+  if (new_gate < cur_gate) new_gate = cur_gate;
+  uint32_t bins_lo = 0, bins_shift = 32;
+  if (gbins != nullptr) {
+    bins_lo = new_gate;
+    const uint64_t span = bins_top > bins_lo ? bins_top - bins_lo : 1;
+    bins_shift = 0;
+    while (((uint64_t)kGateBins << bins_shift) < span) ++bins_shift;
+    if (lane < kGateBins) gbins[lane] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
   }
   // In place and order-preserving.  A batch is loaded before any of it is
   // written, and the entries of element b of a batch go to indices below
@@ -309,11 +345,12 @@ __device__ __attribute__((noinline)) Trimmed compact_list(float* sc, int32_t* ps
         const int o = out + wave_prefix(km, lane);
         sc[o] = sv[b];
         ps[o] = pv[b];
+        if (gbins != nullptr && key >= bins_lo) atomicAdd(&gbins[gate_bin(key, bins_lo, bins_shift)], 1u);
       }
       out += __builtin_popcountll(km);
     }
   }
-  return Trimmed{out, new_gate};
+  return Trimmed{out, new_gate, bins_lo, bins_shift};
 }
 
 }  // namespace
@@ -341,6 +378,9 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
   __shared__ float sh_app_score[kFused ? kWaves : 1][kRowsPerWave][kFused ? kAppendCap : 1];
   __shared__ int32_t sh_app_pos[kFused ? kWaves : 1][kRowsPerWave][kFused ? kAppendCap : 1];
   __shared__ int64_t sh_span[2];
+  // gate bins per (wave, row) and their (lo, shift); see kGateBins
+  __shared__ uint32_t sh_gbins[kFused ? kWaves : 1][kRowsPerWave][kFused ? kGateBins : 1];
+  __shared__ uint32_t sh_gpar[kFused ? kWaves : 1][kRowsPerWave][2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform, so the row indices, ranges and list pointers derived from it live in scalar registers
@@ -395,6 +435,10 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
       gate[i] = 0;
       count[i] = 0;
       staged[i] = 0;
+      if (lane == 0) {
+        sh_gpar[wave][i][0] = 0;
+        sh_gpar[wave][i][1] = 32;   // no bins before a first trim
+      }
     }
   }
   auto list_score = [&](int i) { return a.cand_score + (rix[i] * a.nwin + w) * (int64_t)a.cap; };
@@ -487,17 +531,42 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
       for (int i = 0; i < kRowsPerWave; ++i) {
         if (staged[i] == 0) continue;   // wave-uniform
         if (!all && staged[i] <= kAppendCap - kStage && count[i] + staged[i] <= a.cap - kStage) continue;
+        const uint32_t blo = __builtin_amdgcn_readfirstlane(sh_gpar[wave][i][0]);
+        const uint32_t bsh = __builtin_amdgcn_readfirstlane(sh_gpar[wave][i][1]);
         for (int e = lane; e < staged[i]; e += 64) {
-          list_score(i)[count[i] + e] = sh_app_score[wave][i][e];
+          const float v = sh_app_score[wave][i][e];
+          list_score(i)[count[i] + e] = v;
           list_pos(i)[count[i] + e] = sh_app_pos[wave][i][e];
+          const uint32_t key = order_key(v);
+          if (bsh < 32 && key >= blo) atomicAdd(&sh_gbins[wave][i][gate_bin(key, blo, bsh)], 1u);
         }
         count[i] += staged[i];
         staged[i] = 0;
+        if (bsh < 32) {
+          // the highest bin edge with k list entries at or above it
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          uint32_t c = lane < kGateBins ? sh_gbins[wave][i][lane] : 0u;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t up = __shfl_down(c, d);
+            if (lane + d < 64) c += up;
+          }
+          const uint64_t m = __ballot(lane < kGateBins && c >= (uint32_t)a.k);
+          if (m != 0) {
+            const uint64_t edge = (uint64_t)blo + ((uint64_t)(63 - __builtin_clzll(m)) << bsh);
+            if (edge <= 0xFFFFFFFFull && (uint32_t)edge > gate[i]) gate[i] = (uint32_t)edge;
+          }
+        }
         if (count[i] > a.cap - kStage && count[i] > a.k) {
           const Trimmed t = compact_list(list_score(i), list_pos(i), count[i], (uint32_t)a.k, a.cap / 2, false,
-                                         sh_hist[wave], lane);
+                                         sh_hist[wave], lane, gate[i], sh_gbins[wave][i]);
           count[i] = t.count;
           gate[i] = t.gate;
+          if (lane == 0) {
+            sh_gpar[wave][i][0] = t.bins_lo;
+            sh_gpar[wave][i][1] = t.bins_shift;
+          }
         }
       }
     };
@@ -536,7 +605,7 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
       float* lsc = list_score(i);
       int32_t* lps = list_pos(i);
       if (count[i] > a.k)
-        count[i] = compact_list(lsc, lps, count[i], (uint32_t)a.k, 0, true, sh_hist[wave], lane).count;
+        count[i] = compact_list(lsc, lps, count[i], (uint32_t)a.k, 0, true, sh_hist[wave], lane, 0u, nullptr).count;
       if (count[i] == 0) continue;
       int off = 0;
       if (lane == 0) off = atomicAdd(&a.row_count[rix[i]], count[i]);
