@@ -353,6 +353,34 @@ __device__ __attribute__((noinline)) Trimmed compact_list(float* sc, int32_t* ps
   return Trimmed{out, new_gate, bins_lo, bins_shift};
 }
 
+// Counts `n` newly written list entries (their scores in `app`) into a row's
+// gate bins (lo = par[0], shift = par[1], set), then returns the highest bin
+// edge with `need` list entries at or above it if it is above `gate`, else
+// `gate`.  Not inlined: it runs only on list writes after a first trim, and
+// inline it would crowd the scoring loop's registers.
+__device__ __attribute__((noinline)) uint32_t raise_gate(const float* app, int n, uint32_t* gbins, const uint32_t* par,
+                                                         uint32_t need, uint32_t gate, int lane) {
+  const uint32_t lo = par[0], shift = par[1];
+  for (int e = lane; e < n; e += 64) {
+    const uint32_t key = order_key(app[e]);
+    if (key >= lo) atomicAdd(&gbins[gate_bin(key, lo, shift)], 1u);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  uint32_t c = lane < kGateBins ? gbins[lane] : 0u;   // then: count of bins >= lane
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t up = __shfl_down(c, d);
+    if (lane + d < 64) c += up;
+  }
+  const uint64_t m = __ballot(lane < kGateBins && c >= need);
+  if (m != 0) {
+    const uint64_t edge = (uint64_t)lo + ((uint64_t)(63 - __builtin_clzll(m)) << shift);
+    if (edge <= 0xFFFFFFFFull && (uint32_t)edge > gate) return (uint32_t)edge;
+  }
+  return gate;
+}
+
 }  // namespace
 
 // Key positions staged per barrier: two 32-position MFMA tiles.
@@ -526,41 +554,25 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
     // well.  Either the list is shorter than its window (then it cannot
     // overflow, and a trim happens only above k entries) or its capacity is
     // at least 4k and 4096, so a trim leaves it at most half full.
-    auto flush = [&](bool all) {
+    auto flush = [&](bool all, int64_t next) {
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         if (staged[i] == 0) continue;   // wave-uniform
         if (!all && staged[i] <= kAppendCap - kStage && count[i] + staged[i] <= a.cap - kStage) continue;
-        const uint32_t blo = __builtin_amdgcn_readfirstlane(sh_gpar[wave][i][0]);
-        const uint32_t bsh = __builtin_amdgcn_readfirstlane(sh_gpar[wave][i][1]);
         for (int e = lane; e < staged[i]; e += 64) {
-          const float v = sh_app_score[wave][i][e];
-          list_score(i)[count[i] + e] = v;
+          list_score(i)[count[i] + e] = sh_app_score[wave][i][e];
           list_pos(i)[count[i] + e] = sh_app_pos[wave][i][e];
-          const uint32_t key = order_key(v);
-          if (bsh < 32 && key >= blo) atomicAdd(&sh_gbins[wave][i][gate_bin(key, blo, bsh)], 1u);
         }
+        if (__builtin_amdgcn_readfirstlane(sh_gpar[wave][i][1]) < 32)
+          gate[i] = raise_gate(sh_app_score[wave][i], staged[i], sh_gbins[wave][i], sh_gpar[wave][i], (uint32_t)a.k,
+                               gate[i], lane);
         count[i] += staged[i];
         staged[i] = 0;
-        if (bsh < 32) {
-          // the highest bin edge with k list entries at or above it
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          uint32_t c = lane < kGateBins ? sh_gbins[wave][i][lane] : 0u;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t up = __shfl_down(c, d);
-            if (lane + d < 64) c += up;
-          }
-          const uint64_t m = __ballot(lane < kGateBins && c >= (uint32_t)a.k);
-          if (m != 0) {
-            const uint64_t edge = (uint64_t)blo + ((uint64_t)(63 - __builtin_clzll(m)) << bsh);
-            if (edge <= 0xFFFFFFFFull && (uint32_t)edge > gate[i]) gate[i] = (uint32_t)edge;
-          }
-        }
         if (count[i] > a.cap - kStage && count[i] > a.k) {
+          // gate bins only pay where many positions remain after the trim
+          uint32_t* const gb = span_hi - next > 4 * (int64_t)a.cap ? sh_gbins[wave][i] : nullptr;
           const Trimmed t = compact_list(list_score(i), list_pos(i), count[i], (uint32_t)a.k, a.cap / 2, false,
-                                         sh_hist[wave], lane, gate[i], sh_gbins[wave][i]);
+                                         sh_hist[wave], lane, gate[i], gb);
           count[i] = t.count;
           gate[i] = t.gate;
           if (lane == 0) {
@@ -585,16 +597,16 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
     for (int64_t base = span_lo; base < span_hi; base += 2 * kStage) {
       compute(base, 0);
       stage(r1, 1);
-      if (kFused) flush(false);
+      if (kFused) flush(false, base + kStage);
       fetch(r1, base + 3 * kStage);
       __syncthreads();
       if (base + kStage < span_hi) compute(base + kStage, 1);
       stage(r0, 0);
-      if (kFused) flush(false);
+      if (kFused) flush(false, base + 2 * kStage);
       fetch(r0, base + 4 * kStage);
       __syncthreads();
     }
-    if (kFused) flush(true);
+    if (kFused) flush(true, span_hi);
   }
 
   if (kFused) {
