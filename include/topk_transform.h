@@ -41,7 +41,15 @@ typedef enum topk_status_t {
   /* The internal workspace could not be allocated. */
   TOPK_ERROR_OUT_OF_MEMORY = 3,
   /* A HIP call failed; topk_last_error() holds the HIP error text. */
-  TOPK_ERROR_LAUNCH = 4
+  TOPK_ERROR_LAUNCH = 4,
+  /* An earlier split-row launch queued on the same stream gave up one of its
+   * bounded cross-workgroup waits (its workgroups were not all resident at
+   * once, e.g. because another kernel held CUs), so that launch's outputs
+   * are invalid and must be recomputed.  Reported once, by the next call on
+   * that stream that sees it or by topk_check_faults; the reporting call
+   * queued nothing.  The launch that gave up put the workspace back in its
+   * initial state, so calls after the report run normally. */
+  TOPK_ERROR_DEVICE_FAULT = 5
 } topk_status_t;
 
 /*
@@ -92,8 +100,18 @@ typedef enum topk_status_t {
  * the streaming kernel's grid, use an internal per-(device, stream) workspace
  * that the library allocates on first need, keeps in its initial state
  * between calls, and frees in topk_release_workspaces().  The first call
- * that needs a larger workspace synchronises `stream` (so do not make that
- * first call under stream capture).
+ * that needs a larger workspace allocates and clears it synchronously (so do
+ * not make that first call under stream capture); the smaller one it replaces
+ * stays allocated until topk_release_workspaces(), so graphs captured before
+ * the growth stay valid.  The library also allocates, once per device, one
+ * page of pinned host memory through which split launches report waits that
+ * gave up (TOPK_ERROR_DEVICE_FAULT).
+ *
+ * Split rows rely on every workgroup of a row being resident at once: the
+ * grid is sized to the device's resident capacity and launched normally (no
+ * cooperative launch).  If that fails, a bounded wait gives up and the call's
+ * outputs are invalid; this is reported as TOPK_ERROR_DEVICE_FAULT, never
+ * silently.
  *
  * Completion is asynchronous: outputs are valid once `stream` reaches the call.
  * Returns TOPK_SUCCESS, or an error status; on error nothing was queued.
@@ -171,9 +189,18 @@ topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_p
  */
 topk_status_t topk_set_stream_shape(int32_t shape);
 
-/* Reads (and clears) the device-side fault word of `stream`'s workspace after
- * synchronising the stream: 0 when no cross-workgroup wait ever timed out. */
-topk_status_t topk_debug_fault_word(hipStream_t stream, uint32_t* word);
+/* Synchronises `stream`, then reports whether a split-row launch queued on
+ * it gave up a bounded cross-workgroup wait since the last report: returns
+ * TOPK_ERROR_DEVICE_FAULT once per such launch (then TOPK_SUCCESS), with the
+ * detail in topk_last_error().  The same report otherwise comes from the
+ * next call on the stream. */
+topk_status_t topk_check_faults(hipStream_t stream);
+
+/* Testing override, process-wide: the number of polls a split-row barrier
+ * wait makes before it gives up (0 restores the default, on the order of a
+ * second of waiting).  A tiny limit makes waits give up while every kernel
+ * still runs to its end, which tests the TOPK_ERROR_DEVICE_FAULT report. */
+topk_status_t topk_set_wait_limit(uint32_t polls);
 
 /* ABI version of this header (bumped on any signature change). */
 int32_t topk_abi_version(void);

@@ -19,11 +19,12 @@ from .build import LIB_PATH
 TOPK_MAX_K = 2048
 STREAM_SHAPES = 3   # compiled streaming-kernel shapes: topk_set_stream_shape accepts -1 and 0..STREAM_SHAPES-1
 STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUPPORTED",
-          3: "TOPK_ERROR_OUT_OF_MEMORY", 4: "TOPK_ERROR_LAUNCH"}
+          3: "TOPK_ERROR_OUT_OF_MEMORY", 4: "TOPK_ERROR_LAUNCH", 5: "TOPK_ERROR_DEVICE_FAULT"}
+TOPK_ERROR_DEVICE_FAULT = 5
 
 EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_status_string", "topk_last_error", "topk_last_launch",
             "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape",
-            "topk_debug_fault_word", "topk_abi_version", "indexer_logits", "indexer_topk",
+            "topk_check_faults", "topk_set_wait_limit", "topk_abi_version", "indexer_logits", "indexer_topk",
             "indexer_set_window_override")
 INDEXER_HEADS = 32
 INDEXER_HEAD_DIM = 128
@@ -65,8 +66,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topk_set_dispatch_override.restype = ctypes.c_int
     lib.topk_set_stream_shape.argtypes = [c_i32]
     lib.topk_set_stream_shape.restype = ctypes.c_int
-    lib.topk_debug_fault_word.argtypes = [c_vp, ctypes.POINTER(ctypes.c_uint32)]
-    lib.topk_debug_fault_word.restype = ctypes.c_int
+    lib.topk_check_faults.argtypes = [c_vp]
+    lib.topk_check_faults.restype = ctypes.c_int
+    lib.topk_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.topk_set_wait_limit.restype = ctypes.c_int
     lib.topk_abi_version.argtypes = []
     lib.topk_abi_version.restype = c_i32
     lib.indexer_logits.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64]
@@ -116,13 +119,13 @@ def _call(fn, scores, seq_lens, page_table, k, page_size, out, out_raw, want_raw
         raise ValueError("scores must be a contiguous 2-D float32 tensor")
     B, W = scores.shape
     dev = scores.device
-    if dev.type != "cuda":
-        raise ValueError("scores must be on a GPU")
-    if seq_lens.shape != (B,) or seq_lens.dtype != torch.int32 or seq_lens.device != dev:
-        raise ValueError("seq_lens must be an int32 tensor of shape (B,) on the scores' device")
+    if seq_lens.shape != (B,) or seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of shape (B,)")
     if (page_table.dim() != 2 or page_table.shape[0] != B or page_table.dtype != torch.int32
-            or not page_table.is_contiguous() or page_table.device != dev):
-        raise ValueError("page_table must be a contiguous int32 tensor of shape (B, P) on the scores' device")
+            or not page_table.is_contiguous()):
+        raise ValueError("page_table must be a contiguous int32 tensor of shape (B, P)")
+    if dev.type != "cuda" or seq_lens.device != dev or page_table.device != dev:
+        raise ValueError("scores, seq_lens and page_table must be on one GPU")
     if out is None:
         out = torch.empty((B, k), dtype=torch.int32, device=dev)
     elif (out.shape != (B, k) or out.dtype != torch.int32 or not out.is_contiguous() or out.device != dev):
@@ -172,13 +175,19 @@ def topk_set_stream_shape(shape: int = -1) -> None:
     _check(load().topk_set_stream_shape(int(shape)))
 
 
-def topk_debug_fault_word(stream=None) -> int:
+def topk_check_faults(stream=None) -> None:
+    """Synchronises `stream` (default: torch's current stream) and raises
+    TopkError(TOPK_ERROR_DEVICE_FAULT) once for each split-row launch on it
+    whose bounded cross-workgroup wait gave up since the last report."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream()
-    w = ctypes.c_uint32(0)
-    _check(load().topk_debug_fault_word(ctypes.c_void_p(stream.cuda_stream), ctypes.byref(w)))
-    return int(w.value)
+    _check(load().topk_check_faults(ctypes.c_void_p(stream.cuda_stream)))
+
+
+def topk_set_wait_limit(polls: int = 0) -> None:
+    """Testing override: polls of a split-row barrier wait before it gives up (0 = default)."""
+    _check(load().topk_set_wait_limit(int(polls)))
 
 
 def topk_abi_version() -> int:
@@ -188,8 +197,6 @@ def topk_abi_version() -> int:
 def _indexer_inputs(q, weights, kv, kv_scale, ks, ke):
     import torch
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("q must be on a GPU")
     H, D = INDEXER_HEADS, INDEXER_HEAD_DIM
     if q.dim() != 3 or tuple(q.shape[1:]) != (H, D) or q.dtype != torch.uint8 or not q.is_contiguous():
         raise ValueError("q must be a contiguous uint8 (fp8 E4M3 codes) tensor of shape (num_q, 32, 128)")
@@ -200,11 +207,14 @@ def _indexer_inputs(q, weights, kv, kv_scale, ks, ke):
     if kv.dim() != 2 or kv.shape[1] != D or kv.dtype != torch.uint8 or not kv.is_contiguous() or kv.device != dev:
         raise ValueError("kv must be a contiguous uint8 (fp8 E4M3 codes) tensor of shape (num_kv, 128) on q's device")
     nkv = kv.shape[0]
-    if kv_scale.shape != (nkv,) or kv_scale.dtype != torch.float32 or kv_scale.device != dev:
-        raise ValueError("kv_scale must be a float32 tensor of shape (num_kv,) on q's device")
+    if (kv_scale.shape != (nkv,) or kv_scale.dtype != torch.float32 or not kv_scale.is_contiguous()
+            or kv_scale.device != dev):
+        raise ValueError("kv_scale must be a contiguous float32 tensor of shape (num_kv,) on q's device")
     for name, t in (("ks", ks), ("ke", ke)):
-        if t.shape != (nq,) or t.dtype != torch.int32 or t.device != dev:
-            raise ValueError(f"{name} must be an int32 tensor of shape (num_q,) on q's device")
+        if t.shape != (nq,) or t.dtype != torch.int32 or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous int32 tensor of shape (num_q,) on q's device")
+    if dev.type != "cuda":
+        raise ValueError("the indexer inputs must be on a GPU")
     return dev, nq, nkv
 
 

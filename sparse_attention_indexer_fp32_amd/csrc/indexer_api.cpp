@@ -25,7 +25,7 @@ struct Buffers {
   size_t bytes = 0;
 };
 
-std::mutex g_mu;
+std::mutex& g_mu = topk::lib_mutex();   // the library's one lock
 std::map<int, int> g_cus;                                   // device -> CUs (gfx950 only)
 std::map<std::pair<int, hipStream_t>, Buffers> g_bufs;
 int64_t g_window_override = 0;                              // 0: automatic
@@ -124,13 +124,10 @@ topk_status_t check_common(const uint8_t* q, const float* weights, const uint8_t
 
 namespace indexer {
 
-bool has_buffers() {
-  std::lock_guard<std::mutex> lock(g_mu);
-  return !g_bufs.empty();
-}
+// Both are called with the library lock held (topk_release_workspaces).
+bool has_buffers() { return !g_bufs.empty(); }
 
 void release_buffers() {
-  std::lock_guard<std::mutex> lock(g_mu);
   for (auto& kv : g_bufs)
     if (kv.second.ptr) (void)hipFree(kv.second.ptr);
   g_bufs.clear();
@@ -186,50 +183,51 @@ topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t
   if (!out_idx) return fail(TOPK_ERROR_INVALID_VALUE, "out_idx must be non-null");
   indexer::ScanArgs a{};
   int64_t row_cap = 0;
-  {
-    std::lock_guard<std::mutex> lock(g_mu);
-    int dev = 0, cus = 0;
-    st = device_cus(&dev, &cus);
-    if (st != TOPK_SUCCESS) return st;
-    a.q = q;
-    a.weights = weights;
-    a.kv = kv;
-    a.kv_scale = kv_scale;
-    a.ks = ks;
-    a.ke = ke;
-    a.num_q = num_q;
-    a.num_kv = num_kv;
-    a.k = k;
-    plan_windows(num_q, num_kv, cus, &a.nwin, &a.window);
-    // a list never holds more than its window; a capacity below the window
-    // leaves room for k entries plus a tile after every trim
-    int64_t cap = 4 * (int64_t)k > 4096 ? 4 * (int64_t)k : 4096;
-    if (cap > a.window) cap = a.window;
-    a.cap = (int32_t)cap;
-    row_cap = (int64_t)a.nwin * k;
-    a.row_cap = row_cap;
-    const size_t lists = (size_t)num_q * a.nwin * (size_t)cap;
-    const size_t packed = (size_t)num_q * (size_t)row_cap;
-    const size_t bytes = lists * 8 + packed * 8 + (size_t)num_q * 4 + 256;
-    void* base = nullptr;
-    st = get_buffers(dev, stream, bytes, &base);
-    if (st != TOPK_SUCCESS) return st;
-    char* p = static_cast<char*>(base);
-    a.cand_score = reinterpret_cast<float*>(p);
-    p += lists * 4;
-    a.cand_pos = reinterpret_cast<int32_t*>(p);
-    p += lists * 4;
-    a.row_score = reinterpret_cast<float*>(p);
-    p += packed * 4;
-    a.row_pos = reinterpret_cast<int32_t*>(p);
-    p += packed * 4;
-    a.row_count = reinterpret_cast<int32_t*>(p);
-    hipError_t e = indexer::launch_scan(a, a.nwin, stream);
-    if (e != hipSuccess) return hip_fail(e, "indexer scan launch");
-  }
+  // The lock is held from the scan launch through the select's launch, so no
+  // other call can queue work on this stream's candidate buffers in between.
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0, cus = 0;
+  st = device_cus(&dev, &cus);
+  if (st != TOPK_SUCCESS) return st;
+  a.q = q;
+  a.weights = weights;
+  a.kv = kv;
+  a.kv_scale = kv_scale;
+  a.ks = ks;
+  a.ke = ke;
+  a.num_q = num_q;
+  a.num_kv = num_kv;
+  a.k = k;
+  plan_windows(num_q, num_kv, cus, &a.nwin, &a.window);
+  // a list never holds more than its window; a capacity below the window
+  // leaves room for k entries plus a tile after every trim
+  int64_t cap = 4 * (int64_t)k > 4096 ? 4 * (int64_t)k : 4096;
+  if (cap > a.window) cap = a.window;
+  a.cap = (int32_t)cap;
+  row_cap = (int64_t)a.nwin * k;
+  a.row_cap = row_cap;
+  const size_t lists = (size_t)num_q * a.nwin * (size_t)cap;
+  const size_t packed = (size_t)num_q * (size_t)row_cap;
+  const size_t bytes = lists * 8 + packed * 8 + (size_t)num_q * 4 + 256;
+  void* base = nullptr;
+  st = get_buffers(dev, stream, bytes, &base);
+  if (st != TOPK_SUCCESS) return st;
+  char* p = static_cast<char*>(base);
+  a.cand_score = reinterpret_cast<float*>(p);
+  p += lists * 4;
+  a.cand_pos = reinterpret_cast<int32_t*>(p);
+  p += lists * 4;
+  a.row_score = reinterpret_cast<float*>(p);
+  p += packed * 4;
+  a.row_pos = reinterpret_cast<int32_t*>(p);
+  p += packed * 4;
+  a.row_count = reinterpret_cast<int32_t*>(p);
+  hipError_t e = indexer::launch_scan(a, a.nwin, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer scan launch");
   // exact select over the packed candidates; the positions act as a page
   // table of page size 1, so out_idx receives them directly
-  st = topk_transform(a.row_score, a.row_count, a.row_pos, k, 1, out_idx, nullptr, stream, num_q, row_cap, row_cap);
+  st = topk::transform_locked(a.row_score, a.row_count, a.row_pos, k, 1, out_idx, nullptr, stream, num_q, row_cap,
+                              row_cap);
   if (st != TOPK_SUCCESS) return st;
   char buf[200];
   std::snprintf(buf, sizeof(buf), "indexer-topk grid=%lldx%d window=%lld cap=%d + select %s",

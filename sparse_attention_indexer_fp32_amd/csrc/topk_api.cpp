@@ -1,9 +1,9 @@
 // C-ABI layer of the fused top-k + page-table transform: argument checks,
 // device checks, the dispatcher that picks a kernel shape from the host-known
-// (batch, width, k) and the device's resident-workgroup capacity, and the
-// per-(device, stream) buffers: the workspace the split-row kernel
-// synchronises through (also the streaming kernel's row queue), and the sorted
-// mode's per-row records.
+// (batch, width, k) and the device's resident-workgroup capacity, the
+// per-(device, stream) buffers (the workspace the split-row kernel
+// synchronises through, also the streaming kernel's row queue; the sorted
+// mode's per-row records), and the report of split-row waits that gave up.
 //
 // Dispatch follows the pages' lesson that the path must depend on batch and
 // length (SGLang PR #26788 commit notes: one block per row at large batch,
@@ -22,6 +22,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "indexer_internal.h"
 #include "topk_internal.h"
@@ -32,28 +33,41 @@ namespace {
 thread_local std::string t_last_error;
 thread_local std::string t_last_launch;
 
+// Words of a device's host-visible fault page: one per workspace (word 0 is
+// reserved), set by a split launch whose bounded wait gave up.
+constexpr int kFaultWords = 1024;
+
 struct DeviceInfo {
   bool supported = false;
   int cus = 0;
-  bool coop = false;
   int occ[2][topk::kNumEpt] = {};   // [split][ept] resident workgroups per CU
   int stream_occ[topk::kNumStreamVariants] = {};   // streaming kernel shapes: resident workgroups per CU
   int sorted_occ = 0;               // sorted finish: resident workgroups per CU
+  uint32_t* fault_page = nullptr;   // pinned, device-mapped host memory (kFaultWords words)
+  uint32_t* fault_page_dev = nullptr;   // its device address
+  int fault_next = 1;               // next unassigned word of the page
   std::string arch;
 };
 
 struct Workspace {
   uint32_t* ptr = nullptr;
   int64_t slots = 0;
+  int fault_word = -1;              // this workspace's word of the device's fault page
 };
 
-std::mutex g_mu;
+// One lock for the whole library (the indexer entry points take it too, and
+// hold it across their launches and the select that reads their buffers).
+std::mutex& g_mu = topk::lib_mutex();
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 std::map<std::pair<int, hipStream_t>, Workspace> g_meta;   // sorted mode: records + raw positions ("slots" = words)
+// Buffers replaced by larger ones.  A graph captured before the growth still
+// names them, so they stay allocated until topk_release_workspaces.
+std::vector<void*> g_retired;
 int g_override_ept = 0;
 int g_override_wgs = 0;
 int g_stream_variant = -1;   // -1: the default streaming shape
+uint32_t g_spin_limit = topk::kDefaultSpinLimit;
 
 topk_status_t fail(topk_status_t st, const std::string& msg) {
   t_last_error = msg;
@@ -78,10 +92,6 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
   info.arch = prop.gcnArchName;
   info.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   info.cus = prop.multiProcessorCount;
-  int coop = 0;
-  e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-  info.coop = coop != 0;
   if (info.supported) {
     for (int c = 0; c < 2; ++c)
       for (int i = 0; i < topk::kNumEpt; ++i) {
@@ -94,26 +104,49 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
     }
     e = topk::sorted_occupancy(&info.sorted_occ);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    void* page = nullptr;
+    e = hipHostMalloc(&page, kFaultWords * sizeof(uint32_t), hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("fault page hipHostMalloc: ") + hipGetErrorString(e));
+    }
+    std::memset(page, 0, kFaultWords * sizeof(uint32_t));
+    void* page_dev = nullptr;
+    e = hipHostGetDevicePointer(&page_dev, page, 0);
+    if (e != hipSuccess) {
+      (void)hipHostFree(page);
+      return hip_fail(e, "hipHostGetDevicePointer");
+    }
+    info.fault_page = static_cast<uint32_t*>(page);
+    info.fault_page_dev = static_cast<uint32_t*>(page_dev);
   }
   *out = &g_devices.emplace(dev, info).first->second;
   return TOPK_SUCCESS;
 }
 
+// Caller holds g_mu.  Reports (once) a split launch on this workspace whose
+// bounded wait gave up since the last report: its outputs were invalid.  The
+// device sets the word when that launch ends; a report can therefore come one
+// call late, or from topk_check_faults after a synchronisation.
+topk_status_t take_fault(DeviceInfo& info, Workspace& w) {
+  if (w.fault_word < 0 || info.fault_page == nullptr) return TOPK_SUCCESS;
+  uint32_t* word = info.fault_page + w.fault_word;
+  if (__atomic_load_n(word, __ATOMIC_ACQUIRE) == 0u) return TOPK_SUCCESS;
+  __atomic_store_n(word, 0u, __ATOMIC_RELEASE);
+  return fail(TOPK_ERROR_DEVICE_FAULT,
+              "an earlier split-row launch on this stream gave up a cross-workgroup wait (its workgroups were not "
+              "all resident at once); that launch's outputs are invalid and must be recomputed; this call queued "
+              "nothing");
+}
+
 // Caller holds g_mu.
-topk_status_t get_workspace(int dev, hipStream_t stream, int64_t slots, uint32_t** ptr, int64_t* capacity) {
+topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, int64_t slots, Workspace** out) {
   Workspace& w = g_ws[std::make_pair(dev, stream)];
-  if (w.ptr && w.slots >= slots) {
-    *ptr = w.ptr;
-    *capacity = w.slots;
-    return TOPK_SUCCESS;
+  if (w.fault_word < 0) {
+    w.fault_word = info.fault_next < kFaultWords ? info.fault_next++ : kFaultWords - 1;
   }
-  if (w.ptr) {
-    hipError_t e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    (void)hipFree(w.ptr);
-    w.ptr = nullptr;
-    w.slots = 0;
-  }
+  *out = &w;
+  if (w.ptr && w.slots >= slots) return TOPK_SUCCESS;
   const size_t bytes = topk::workspace_words(slots) * sizeof(uint32_t);
   void* p = nullptr;
   if (std::getenv("TOPK_TEST_FAIL_ALLOC") == nullptr) {
@@ -131,10 +164,9 @@ topk_status_t get_workspace(int dev, hipStream_t stream, int64_t slots, uint32_t
     (void)hipFree(p);
     return hip_fail(e, "workspace hipMemset");
   }
+  if (w.ptr) g_retired.push_back(w.ptr);
   w.ptr = static_cast<uint32_t*>(p);
   w.slots = slots;
-  *ptr = w.ptr;
-  *capacity = w.slots;
   return TOPK_SUCCESS;
 }
 
@@ -148,19 +180,13 @@ topk_status_t get_meta(int dev, hipStream_t stream, int64_t words, uint32_t** pt
     *ptr = w.ptr;
     return TOPK_SUCCESS;
   }
-  if (w.ptr) {
-    hipError_t e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    (void)hipFree(w.ptr);
-    w.ptr = nullptr;
-    w.slots = 0;
-  }
   void* p = nullptr;
   hipError_t e = hipMalloc(&p, (size_t)words * sizeof(uint32_t));
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("selection record hipMalloc: ") + hipGetErrorString(e));
   }
+  if (w.ptr) g_retired.push_back(w.ptr);
   w.ptr = static_cast<uint32_t*>(p);
   w.slots = words;
   *ptr = w.ptr;
@@ -330,9 +356,11 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
   return TOPK_SUCCESS;
 }
 
-topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
-                            int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream, int32_t batch,
-                            int64_t width, int64_t pages_per_row, bool sorted) {
+// Caller holds g_mu.
+topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens, const int32_t* page_table,
+                                   int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
+                                   hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row,
+                                   bool sorted) {
   t_last_error.clear();
   if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERROR_INVALID_VALUE, "k must be in [1, 2048]");
   if (page_size < 1 || (page_size & (page_size - 1)) != 0)
@@ -353,11 +381,17 @@ topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const 
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
 
-  std::lock_guard<std::mutex> lock(g_mu);
   DeviceInfo* info = nullptr;
   topk_status_t st = device_info(dev, &info);
   if (st != TOPK_SUCCESS) return st;
   if (!info->supported) return fail(TOPK_ERROR_UNSUPPORTED, "device " + info->arch + " is not gfx950");
+  {
+    auto wit = g_ws.find(std::make_pair(dev, stream));
+    if (wit != g_ws.end()) {
+      st = take_fault(*info, wit->second);
+      if (st != TOPK_SUCCESS) return st;
+    }
+  }
 
   Plan plan;
   st = plan_launch(*info, batch, width, k, &plan);
@@ -383,6 +417,8 @@ topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const 
   a.vec = (width % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
   a.meta = nullptr;
   a.sel = nullptr;
+  a.spin_limit = g_spin_limit;
+  a.fault_host = nullptr;
   if (sorted) {
     // the selection launch always writes raw positions: the caller's out_raw,
     // else a scratch area after the records
@@ -395,10 +431,12 @@ topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const 
   if (plan.kind == Kind::kSplit || (plan.kind == Kind::kStream && batch > plan.slots)) {
     // split rows synchronise through per-slot regions; streamed rows beyond
     // the grid are handed out through a counter in the header
-    int64_t capacity = 0;
-    st = get_workspace(dev, stream, plan.kind == Kind::kSplit ? plan.slots : 0, &a.ws, &capacity);
+    Workspace* w = nullptr;
+    st = get_workspace(*info, dev, stream, plan.kind == Kind::kSplit ? plan.slots : 0, &w);
     if (st != TOPK_SUCCESS) return st;
-    a.ws_slots = (int32_t)capacity;
+    a.ws = w->ptr;
+    a.ws_slots = (int32_t)w->slots;
+    a.fault_host = info->fault_page_dev + w->fault_word;
   }
   if (plan.kind == Kind::kStream)
     e = topk::launch_stream_rows(plan.stream_variant, a, stream);
@@ -428,11 +466,29 @@ topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const 
   return TOPK_SUCCESS;
 }
 
+topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
+                            int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream, int32_t batch,
+                            int64_t width, int64_t pages_per_row, bool sorted) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  return run_transform_locked(scores, seq_lens, page_table, k, page_size, out_idx, out_raw, stream, batch, width,
+                              pages_per_row, sorted);
+}
+
 }  // namespace
 
 namespace topk {
 void set_last_error(const char* msg) { t_last_error = msg; }
 void set_last_launch(const char* msg) { t_last_launch = msg; }
+std::mutex& lib_mutex() {
+  static std::mutex m;
+  return m;
+}
+topk_status_t transform_locked(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
+                               int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream,
+                               int32_t batch, int64_t width, int64_t pages_per_row) {
+  return run_transform_locked(scores, seq_lens, page_table, k, page_size, out_idx, out_raw, stream, batch, width,
+                              pages_per_row, false);
+}
 }  // namespace topk
 
 extern "C" {
@@ -458,6 +514,7 @@ const char* topk_status_string(topk_status_t status) {
     case TOPK_ERROR_UNSUPPORTED: return "TOPK_ERROR_UNSUPPORTED";
     case TOPK_ERROR_OUT_OF_MEMORY: return "TOPK_ERROR_OUT_OF_MEMORY";
     case TOPK_ERROR_LAUNCH: return "TOPK_ERROR_LAUNCH";
+    case TOPK_ERROR_DEVICE_FAULT: return "TOPK_ERROR_DEVICE_FAULT";
   }
   return "TOPK_UNKNOWN_STATUS";
 }
@@ -468,15 +525,23 @@ const char* topk_last_launch(void) { return t_last_launch.c_str(); }
 
 topk_status_t topk_release_workspaces(void) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (g_ws.empty() && g_meta.empty() && !indexer::has_buffers()) return TOPK_SUCCESS;
+  if (g_ws.empty() && g_meta.empty() && g_retired.empty() && !indexer::has_buffers()) return TOPK_SUCCESS;
   hipError_t e = hipDeviceSynchronize();
   indexer::release_buffers();
-  for (auto& kv : g_ws)
+  // A released workspace's pending fault report goes with it (the streams'
+  // fault words stay assigned, so they are cleared here).
+  for (auto& kv : g_ws) {
     if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    auto dit = g_devices.find(kv.first.first);
+    if (dit != g_devices.end() && dit->second.fault_page != nullptr && kv.second.fault_word >= 0)
+      __atomic_store_n(dit->second.fault_page + kv.second.fault_word, 0u, __ATOMIC_RELEASE);
+  }
   g_ws.clear();
   for (auto& kv : g_meta)
     if (kv.second.ptr) (void)hipFree(kv.second.ptr);
   g_meta.clear();
+  for (void* p : g_retired) (void)hipFree(p);
+  g_retired.clear();
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   return TOPK_SUCCESS;
 }
@@ -499,25 +564,26 @@ topk_status_t topk_set_stream_shape(int32_t shape) {
   return TOPK_SUCCESS;
 }
 
-topk_status_t topk_debug_fault_word(hipStream_t stream, uint32_t* word) {
-  if (!word) return fail(TOPK_ERROR_INVALID_VALUE, "word must be non-null");
-  *word = 0;
+topk_status_t topk_check_faults(hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(g_mu);
+  t_last_error.clear();
   auto it = g_ws.find(std::make_pair(dev, stream));
-  if (it == g_ws.end() || !it->second.ptr) return TOPK_SUCCESS;
+  auto dit = g_devices.find(dev);
+  if (it == g_ws.end() || dit == g_devices.end()) return TOPK_SUCCESS;
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  e = hipMemcpy(word, it->second.ptr, sizeof(uint32_t), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
-  const uint32_t zero = 0;
-  e = hipMemcpy(it->second.ptr, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  return take_fault(dit->second, it->second);
+}
+
+topk_status_t topk_set_wait_limit(uint32_t polls) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_spin_limit = polls == 0u ? topk::kDefaultSpinLimit : polls;
   return TOPK_SUCCESS;
 }
 
-int32_t topk_abi_version(void) { return 1; }
+int32_t topk_abi_version(void) { return 2; }
 
 }  // extern "C"

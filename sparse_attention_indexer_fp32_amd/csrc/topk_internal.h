@@ -6,11 +6,24 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "topk_transform.h"
+
 namespace topk {
 
 // Per-host-thread status text shared by every entry point of the library.
 void set_last_error(const char* msg);
 void set_last_launch(const char* msg);
+
+// The library's one lock: every entry point that touches the per-device or
+// per-(device, stream) state holds it.
+std::mutex& lib_mutex();
+
+// topk_transform for a caller that already holds lib_mutex().
+topk_status_t transform_locked(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
+                               int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream,
+                               int32_t batch, int64_t width, int64_t pages_per_row);
 
 constexpr int kThreads = 1024;          // threads per workgroup (16 wave64s)
 constexpr int kWaves = kThreads / 64;
@@ -29,9 +42,13 @@ constexpr int kEptValues[kNumEpt] = {4, 8, 16, 32, 64};
 // cleared while the slot's other workgroups already accumulate the next row.
 // Every region is left zeroed by the workgroup that finishes its row.
 // ---------------------------------------------------------------------------
-constexpr size_t kHdrWords = 64;        // [0] = fault word (a bounded wait timed out)
+// Header words, each group on its own 128-byte line.
+constexpr size_t kHdrWords = 128;
+constexpr size_t kHdrFault = 0;         // nonzero while a split launch in which a bounded wait gave up runs
+constexpr size_t kHdrFaultCount = 1;    // split launches in which a wait gave up, ever (read by the host)
 constexpr size_t kHdrRowTicket = 32;    // streaming kernel: rows handed out beyond the first grid's
 constexpr size_t kHdrRowExit = 48;      // streaming kernel: workgroups out of rows
+constexpr size_t kHdrLaunchExit = 64;   // split kernel: workgroups out of the current launch (+ 2^16 per give-up)
 // Per-slot barrier block: an arrival counter per group of kBarGroup
 // workgroups, a counter of completed groups, and the generation, each on its
 // own 128-byte line (arrivals then contend per group, not per row, and the
@@ -78,7 +95,13 @@ struct KernelArgs {
   int32_t vec;                // rows are 16-byte aligned: use dwordx4 loads
   uint32_t* meta;             // (batch, kMetaWords): how each row's selection ended, for the sorted finish; or nullptr
   const int32_t* sel;         // sorted finish: (batch, k) raw positions the selection launch wrote
+  uint32_t spin_limit;        // split rows: polls of a barrier wait before it gives up
+  uint32_t* fault_host;       // split rows: host-visible copy of the workspace's fault count, or nullptr
 };
+
+// Polls of a split-row barrier wait before it gives up (with s_sleep 1 between
+// polls: on the order of a second).
+constexpr uint32_t kDefaultSpinLimit = 1u << 21;
 
 // ept_index selects kEptValues[ept_index]; coop selects the cross-workgroup
 // kernel (cooperative launch, grid = slots * wgs_per_row).

@@ -51,8 +51,6 @@
 namespace topk {
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 21;   // bounded wait: ~seconds, then flag a fault and go on
-
 enum Mode : int { kModeNone = 0, kModeTakeAll = 1, kModeTies = 2, kModeCands = 3 };
 
 // fp32 -> uint32 whose unsigned order is the value order (-0.0 just below +0.0).
@@ -218,18 +216,26 @@ __device__ __forceinline__ void find_threshold(const uint32_t* h, uint32_t need,
 __device__ __forceinline__ void wave_mem_drain() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Per-row barrier among the G workgroups of one slot.  The grid never exceeds
-// the device's resident-workgroup capacity, so all G are running.  Workgroup
-// g arrives on its group's counter; the last of a group resets that counter
-// and arrives on the top counter; the last group's closer resets the top and
-// publishes the next generation.  Every reset is drained before the arrival
-// (or publication) that follows it, so the counters are zero again before any
-// workgroup can leave, and the barrier resets itself across calls and graph
-// replays.  Each workgroup tracks the generation it waits for in `gen` (read
-// once per launch: no barrier of the slot can complete before this workgroup
-// has arrived, so the value is stable until then).  The wait is bounded: on
-// timeout the fault word is set, and waits that see it set give up, so the
-// kernel always drains.
-__device__ __forceinline__ void row_barrier(uint32_t* bar, int G, int g, uint32_t& gen, uint32_t* fault, int tid) {
+// the device's resident-workgroup capacity, so all G are normally running at
+// once (a kernel that holds CUs on another stream can break that: there is no
+// cooperative launch).  Workgroup g arrives on its group's counter; the last
+// of a group resets that counter and arrives on the top counter; the last
+// group's closer resets the top and publishes the next generation.  Every
+// reset is drained before the arrival (or publication) that follows it, so
+// the counters are zero again before any workgroup can leave, and the barrier
+// resets itself across calls and graph replays.  Each workgroup tracks the
+// generation it waits for in `gen` (read once per launch: no barrier of the
+// slot can complete before this workgroup has arrived, so the value is stable
+// until then).
+//
+// The wait is bounded by `spin_limit` polls.  A wait that gives up sets the
+// fault word and `gave_up`; every other wait that sees the fault word set gives
+// up too, so the kernel always drains.  The launch's outputs are then invalid:
+// its last workgroup out puts the workspace back in its initial state (fault
+// word included) and counts the fault for the host (launch_exit), so the next
+// launch starts clean and waits its full limit.
+__device__ __forceinline__ void row_barrier(uint32_t* bar, int G, int g, uint32_t& gen, uint32_t* fault,
+                                            uint32_t spin_limit, uint32_t& gave_up, int tid) {
   wave_mem_drain();
   __syncthreads();
   if (tid == 0) {
@@ -252,17 +258,55 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, int G, int g, uint32_
     } else {
       uint32_t spins = 0;
       while ((int32_t)(g_load(bar + kBarGen) - gen) < 0) {
-        __builtin_amdgcn_s_sleep(1);
-        ++spins;
-        if (spins > kSpinLimit || ((spins & 1023u) == 0u && g_load(fault) != 0u)) {
+        if (spins >= spin_limit || ((spins & 1023u) == 1023u && g_load(fault) != 0u)) {
           g_store(fault, 1u);
+          gave_up = 1u;
           break;
         }
+        __builtin_amdgcn_s_sleep(1);
+        ++spins;
       }
     }
     wave_mem_drain();
   }
   __syncthreads();
+}
+
+// Arrivals on the launch-exit counter carry this much per wait given up.
+constexpr uint32_t kExitFaultUnit = 1u << 16;
+
+// End of a split-row launch, called by every workgroup once it has no more
+// rows.  Each workgroup counts itself out (plus kExitFaultUnit if one of its
+// waits gave up); its last workspace writes other than zeroes were drained at
+// its last row's exit, so the arrival needs no drain of its own.  The last
+// workgroup out resets the counter.  If any wait of the launch gave up, it
+// first zeroes every barrier block and region and the fault word -- a barrier
+// that gave up can leave stray arrivals and partial histograms behind -- and
+// counts the fault in the header and in the host-visible word.  Uniform;
+// contains barriers.
+__device__ __forceinline__ void launch_exit(const KernelArgs& a, uint32_t gave_up, uint32_t* sh_flag, int tid) {
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t mine = 1u + (gave_up != 0u ? kExitFaultUnit : 0u);
+    const uint32_t before = g_add_ret(a.ws + kHdrLaunchExit, mine);
+    const bool last = (before & (kExitFaultUnit - 1u)) == gridDim.x - 1u;
+    const uint32_t faults = (before >> 16) + (gave_up != 0u ? 1u : 0u);
+    *sh_flag = last ? (faults != 0u ? 2u : 1u) : 0u;
+  }
+  __syncthreads();
+  const uint32_t flag = uniform(*sh_flag);
+  if (flag == 0u) return;
+  if (flag == 2u) {
+    const size_t words = (size_t)a.ws_slots * kBarWords + (size_t)a.ws_slots * 2 * kRegionWords;
+    for (size_t i = (size_t)tid; i < words; i += kThreads) g_store(a.ws + kHdrWords + i, 0u);
+    if (tid == 0) {
+      g_store(a.ws + kHdrFault, 0u);
+      const uint32_t count = g_add_ret(a.ws + kHdrFaultCount, 1u) + 1u;
+      if (a.fault_host != nullptr)
+        __hip_atomic_store(a.fault_host, count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+  if (tid == 0) g_store(a.ws + kHdrLaunchExit, 0u);
 }
 
 // Gather + transform pass: slot j < n holds raw position r (trivial rows: r = j);
@@ -510,9 +554,10 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
   const int64_t C = (int64_t)kThreads * E;
   const int64_t W = a.width;
   const int k = a.k;
-  uint32_t* fault = a.ws;
+  uint32_t* fault = COOP ? a.ws + kHdrFault : nullptr;
   uint32_t* bar = COOP ? a.ws + kHdrWords + (size_t)slot * kBarWords : nullptr;
   uint32_t gen = (COOP && threadIdx.x == 0) ? g_load(bar + kBarGen) : 0u;   // see row_barrier
+  uint32_t gave_up = 0;   // thread 0: a barrier wait of this workgroup gave up
 
   int nsplit = 0;   // split rows this slot has finished: picks the workspace region parity
   for (int it = 0;; ++it) {
@@ -578,7 +623,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
           const uint32_t c = sh_hist[b];
           if (c && (uint32_t)b >= push_from) g_add(gh + b, c);
         }
-        row_barrier(bar, G, g, gen, fault, tid);
+        row_barrier(bar, G, g, gen, fault, a.spin_limit, gave_up, tid);
         for (int b = tid; b < nb; b += kThreads) sh_hist[b] = g_load(gh + b);
         __syncthreads();
       }
@@ -718,6 +763,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     if (tid < 64) g_store(region + kRegCtr + tid, 0u);
     __syncthreads();
   }
+  if (COOP) launch_exit(a, gave_up, &sh_var[15], opaque_tid());
 }
 
 // ---------------------------------------------------------------------------

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert topk.topk_abi_version() == 1
+    assert topk.topk_abi_version() == 2
     for code, name in topk.STATUS.items():
         assert topk.topk_status_string(code) == name
     assert topk.topk_status_string(99) == "TOPK_UNKNOWN_STATUS"
@@ -72,12 +72,20 @@ def test_dispatch_override_validation(lib):
 
 
 def test_stream_shape_validation(lib):
-    """Two compiled streaming shapes (0 and 1); -1 restores automatic choice."""
+    """Every compiled streaming shape (0 .. STREAM_SHAPES - 1) is accepted; -1
+    restores the automatic choice."""
     for shape in range(-1, topk.STREAM_SHAPES):
         assert lib.topk_set_stream_shape(shape) == 0
     assert lib.topk_set_stream_shape(topk.STREAM_SHAPES) == 1
     assert lib.topk_set_stream_shape(-2) == 1
     assert lib.topk_set_stream_shape(-1) == 0
+
+
+def test_wait_limit_setter(lib):
+    """The testing override of the split rows' wait limit takes any count; 0
+    restores the default."""
+    assert lib.topk_set_wait_limit(1) == 0
+    assert lib.topk_set_wait_limit(0) == 0
 
 
 def test_python_binding_rejects_bad_tensors():
@@ -88,6 +96,27 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         topk.topk_transform(s.double(), torch.zeros(2, dtype=torch.int32), torch.zeros((2, 1), dtype=torch.int32),
                             4, 8)
+
+
+def test_python_binding_rejects_strided_1d_inputs():
+    """A strided 1-D view (a column of a 2-D tensor) would be read as dense
+    int32 through its data pointer: the binding refuses it before any call."""
+    import torch
+    lens2d = torch.zeros((2, 3), dtype=torch.int32)
+    with pytest.raises(ValueError, match="seq_lens"):
+        topk._call(None, torch.zeros((2, 8)), lens2d[:, 0], torch.zeros((2, 1), dtype=torch.int32), 4, 8, None,
+                   None, False, None)
+    q = torch.zeros((2, 32, 128), dtype=torch.uint8)
+    w = torch.zeros((2, 32), dtype=torch.float32)
+    kv = torch.zeros((4, 128), dtype=torch.uint8)
+    sc = torch.zeros((4,), dtype=torch.float32)
+    ks = torch.zeros((2, 2), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        topk._indexer_inputs(q, w, kv, sc, ks[:, 0], ks[:, 1])
+    with pytest.raises(ValueError):
+        topk._indexer_inputs(q, w, kv, torch.zeros((4, 2), dtype=torch.float32)[:, 0], ks[:, 0].contiguous(),
+                             ks[:, 1].contiguous())
+
 
 
 @pytest.mark.parametrize("k,num_q,num_kv,expect", [

@@ -80,3 +80,73 @@ def test_sorted_graph_replay(lib, name, batch, width, k):
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), exp_out), f"replay {rep}"
         assert np.array_equal(raw.cpu().numpy(), exp_raw), f"replay {rep}"
+
+
+def test_wait_give_up_reported_once_and_not_sticky(lib):
+    """A wait limit of one poll makes the split rows' barrier waits give up
+    while every kernel still runs to its end (nothing on the device waits
+    unbounded).  The faulted call's outputs are invalid, and the library says
+    so: the next call on the stream returns TOPK_ERROR_DEVICE_FAULT once and
+    queues nothing, or topk_check_faults raises it after a synchronisation.
+    The faulted launch put the workspace back in its initial state, so calls
+    at the normal limit are exact again, with no fault reported."""
+    import torch
+    w = workloads.custom(61, 2, 1 << 20, 2048, 64, kind="normal", table="perm")
+    s, sl, pt = upload(w)
+    out = torch.empty((w.batch, w.k), dtype=torch.int32, device=s.device)
+    raw = torch.empty_like(out)
+    lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=raw)
+    torch.cuda.synchronize()
+    note(f"give-up: {lib.topk_last_launch()}")
+    assert lib.topk_last_launch().startswith("split-row")
+    check(w, out.cpu().numpy(), raw.cpu().numpy())
+    lib.topk_check_faults()
+    try:
+        lib.topk_set_wait_limit(1)
+        note("give-up: one-poll waits, reported by topk_check_faults")
+        lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=raw)
+        with pytest.raises(lib.TopkError) as e:
+            lib.topk_check_faults()
+        assert e.value.status == lib.TOPK_ERROR_DEVICE_FAULT and "invalid" in str(e.value)
+        lib.topk_check_faults()   # reported once
+        note("give-up: one-poll waits, reported by the next call")
+        lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=raw)
+        torch.cuda.synchronize()
+        out.fill_(-7)
+        with pytest.raises(lib.TopkError) as e:
+            lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=raw)
+        assert e.value.status == lib.TOPK_ERROR_DEVICE_FAULT
+        torch.cuda.synchronize()
+        assert bool((out == -7).all()), "the call that reported the fault queued work"
+    finally:
+        lib.topk_set_wait_limit(0)
+    for rep in range(3):
+        note(f"give-up: normal limit again, rep {rep}")
+        out.fill_(-7)
+        raw.fill_(-7)
+        lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=raw)
+        torch.cuda.synchronize()
+        check(w, out.cpu().numpy(), raw.cpu().numpy())
+    lib.topk_check_faults()
+
+
+def test_forced_workspace_allocation_failure(lib, monkeypatch):
+    """TOPK_TEST_FAIL_ALLOC makes the next workspace allocation fail: the call
+    returns TOPK_ERROR_OUT_OF_MEMORY with a message and queues nothing; once
+    the variable is gone, the same call on the same stream runs exactly."""
+    import torch
+    w = workloads.custom(62, 3, 300000, 1024, 64, kind="normal")
+    s, sl, pt = upload(w)
+    stream = torch.cuda.Stream()   # a stream with no workspace yet
+    out = torch.full((w.batch, w.k), -7, dtype=torch.int32, device=s.device)
+    monkeypatch.setenv("TOPK_TEST_FAIL_ALLOC", "1")
+    note("forced allocation failure")
+    with pytest.raises(lib.TopkError) as e:
+        lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out, stream=stream)
+    assert e.value.status == 3 and "TOPK_TEST_FAIL_ALLOC" in str(e.value)
+    stream.synchronize()
+    assert bool((out == -7).all())
+    monkeypatch.delenv("TOPK_TEST_FAIL_ALLOC")
+    o, r = lib.topk_transform(s, sl, pt, w.k, w.page_size, want_raw=True, stream=stream)
+    stream.synchronize()
+    check(w, o.cpu().numpy(), r.cpu().numpy())
