@@ -146,6 +146,42 @@ topk_status_t topk_transform_sorted(const float* scores, const int32_t* seq_lens
                                     int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
                                     hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row);
 
+/*
+ * topk_transform_noalloc -- topk_transform for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, layouts, result and errors as topk_transform;
+ * it calls no allocating routine.  Its workspace is the library's static
+ * device scratch (16 MiB per device, held from the library's first call on
+ * the device until the process ends) instead of a per-(device, stream)
+ * buffer.  The first call on a device that needs the scratch queues a zero
+ * fill of it on `stream` before its own kernel.
+ *
+ * Limit: shapes whose split-row plan needs more than 127 row slots of
+ * workspace return TOPK_ERROR_UNSUPPORTED with a message (no current plan
+ * does: split rows are chosen only for fewer than half a row per CU).
+ *
+ * Every call on one device shares that device's scratch, and each call's
+ * kernels leave it in its initial state; calls whose kernels overlap on one
+ * device (queued on different streams without ordering between them) race
+ * on it and give wrong results.  Split-row waits that give up are reported
+ * as for topk_transform (TOPK_ERROR_DEVICE_FAULT at the next call of this
+ * entry point, or from topk_check_faults); the next-call report needs the
+ * pinned page topk_init() allocates.
+ */
+topk_status_t topk_transform_noalloc(const float* scores, const int32_t* seq_lens, const int32_t* page_table,
+                                     int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
+                                     hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row);
+
+/*
+ * Sets up the current device for the library: device properties and kernel
+ * residency, the static scratch's device address, and the pinned host page of
+ * fault words.  Every entry point does this on its first call on a device
+ * (topk_transform_noalloc without the page); calling it first, outside graph
+ * capture, lets topk_transform_noalloc report faults at its next call too.
+ * Returns TOPK_ERROR_UNSUPPORTED on a device that is not gfx950.
+ */
+topk_status_t topk_init(void);
+
 /* Static text for a status code (never NULL). */
 const char* topk_status_string(topk_status_t status);
 
@@ -190,10 +226,10 @@ topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_p
 topk_status_t topk_set_stream_shape(int32_t shape);
 
 /* Synchronises `stream`, then reports whether a split-row launch queued on
- * it gave up a bounded cross-workgroup wait since the last report: returns
- * TOPK_ERROR_DEVICE_FAULT once per such launch (then TOPK_SUCCESS), with the
- * detail in topk_last_error().  The same report otherwise comes from the
- * next call on the stream. */
+ * it (or, on this device, through topk_transform_noalloc) gave up a bounded
+ * cross-workgroup wait since the last report: returns TOPK_ERROR_DEVICE_FAULT
+ * once per such report (then TOPK_SUCCESS), with the detail in
+ * topk_last_error().  The same report otherwise comes from the next call. */
 topk_status_t topk_check_faults(hipStream_t stream);
 
 /* Testing override, process-wide: the number of polls a split-row barrier

@@ -22,7 +22,7 @@ STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUP
           3: "TOPK_ERROR_OUT_OF_MEMORY", 4: "TOPK_ERROR_LAUNCH", 5: "TOPK_ERROR_DEVICE_FAULT"}
 TOPK_ERROR_DEVICE_FAULT = 5
 
-EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_status_string", "topk_last_error", "topk_last_launch",
+EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_transform_noalloc", "topk_init", "topk_status_string", "topk_last_error", "topk_last_launch",
             "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape",
             "topk_check_faults", "topk_set_wait_limit", "topk_abi_version", "indexer_logits", "indexer_topk",
             "indexer_set_window_override")
@@ -51,9 +51,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         pass
     lib = ctypes.CDLL(path)
     c_i32, c_i64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
-    for fn in (lib.topk_transform, lib.topk_transform_sorted):
+    for fn in (lib.topk_transform, lib.topk_transform_sorted, lib.topk_transform_noalloc):
         fn.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64]
         fn.restype = ctypes.c_int
+    lib.topk_init.argtypes = []
+    lib.topk_init.restype = ctypes.c_int
     lib.topk_status_string.argtypes = [ctypes.c_int]
     lib.topk_status_string.restype = ctypes.c_char_p
     lib.topk_last_error.argtypes = []
@@ -111,6 +113,23 @@ def topk_transform_sorted(scores, seq_lens, page_table, k: int, page_size: int, 
     taken at the threshold (the plain definition's order)."""
     return _call(load().topk_transform_sorted, scores, seq_lens, page_table, k, page_size, out, out_raw, want_raw,
                  stream)
+
+
+def topk_transform_noalloc(scores, seq_lens, page_table, k: int, page_size: int, out, out_raw=None,
+                           stream=None) -> Tuple[object, Optional[object]]:
+    """As topk_transform, through the entry point that allocates nothing: its
+    workspace is the library's static device scratch, and `out` (and
+    `out_raw`, if wanted) must be passed preallocated.  Calls that overlap on
+    one device race on the scratch."""
+    if out is None:
+        raise ValueError("topk_transform_noalloc needs a preallocated out")
+    return _call(load().topk_transform_noalloc, scores, seq_lens, page_table, k, page_size, out, out_raw, False,
+                 stream)
+
+
+def topk_init() -> None:
+    """Sets up the current device (also the pinned page of fault words)."""
+    _check(load().topk_init())
 
 
 def _call(fn, scores, seq_lens, page_table, k, page_size, out, out_raw, want_raw, stream):

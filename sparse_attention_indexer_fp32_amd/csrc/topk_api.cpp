@@ -33,8 +33,9 @@ namespace {
 thread_local std::string t_last_error;
 thread_local std::string t_last_launch;
 
-// Words of a device's host-visible fault page: one per workspace (word 0 is
-// reserved), set by a split launch whose bounded wait gave up.
+// Words of a device's host-visible fault page: word 0 for the static scratch,
+// then one per workspace.  A split launch whose bounded wait gave up stores its
+// workspace's new fault count there.
 constexpr int kFaultWords = 1024;
 
 struct DeviceInfo {
@@ -43,9 +44,12 @@ struct DeviceInfo {
   int occ[2][topk::kNumEpt] = {};   // [split][ept] resident workgroups per CU
   int stream_occ[topk::kNumStreamVariants] = {};   // streaming kernel shapes: resident workgroups per CU
   int sorted_occ = 0;               // sorted finish: resident workgroups per CU
-  uint32_t* fault_page = nullptr;   // pinned, device-mapped host memory (kFaultWords words)
+  uint32_t* fault_page = nullptr;   // pinned, device-mapped host memory (kFaultWords words), or null
   uint32_t* fault_page_dev = nullptr;   // its device address
   int fault_next = 1;               // next unassigned word of the page
+  uint32_t* scratch = nullptr;      // device address of the static scratch
+  bool scratch_zeroed = false;      // the scratch's zero fill has been queued
+  uint32_t scratch_reported = 0;    // the scratch's fault count last reported
   std::string arch;
 };
 
@@ -53,6 +57,7 @@ struct Workspace {
   uint32_t* ptr = nullptr;
   int64_t slots = 0;
   int fault_word = -1;              // this workspace's word of the device's fault page
+  uint32_t reported = 0;            // its fault count last reported
 };
 
 // One lock for the whole library (the indexer entry points take it too, and
@@ -104,43 +109,57 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
     }
     e = topk::sorted_occupancy(&info.sorted_occ);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-    void* page = nullptr;
-    e = hipHostMalloc(&page, kFaultWords * sizeof(uint32_t), hipHostMallocMapped | hipHostMallocCoherent);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("fault page hipHostMalloc: ") + hipGetErrorString(e));
-    }
-    std::memset(page, 0, kFaultWords * sizeof(uint32_t));
-    void* page_dev = nullptr;
-    e = hipHostGetDevicePointer(&page_dev, page, 0);
-    if (e != hipSuccess) {
-      (void)hipHostFree(page);
-      return hip_fail(e, "hipHostGetDevicePointer");
-    }
-    info.fault_page = static_cast<uint32_t*>(page);
-    info.fault_page_dev = static_cast<uint32_t*>(page_dev);
+    // set-up of the static scratch: its address on this (the current) device
+    e = topk::scratch_address(&info.scratch);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
   }
   *out = &g_devices.emplace(dev, info).first->second;
   return TOPK_SUCCESS;
 }
 
-// Caller holds g_mu.  Reports (once) a split launch on this workspace whose
-// bounded wait gave up since the last report: its outputs were invalid.  The
-// device sets the word when that launch ends; a report can therefore come one
-// call late, or from topk_check_faults after a synchronisation.
-topk_status_t take_fault(DeviceInfo& info, Workspace& w) {
-  if (w.fault_word < 0 || info.fault_page == nullptr) return TOPK_SUCCESS;
-  uint32_t* word = info.fault_page + w.fault_word;
-  if (__atomic_load_n(word, __ATOMIC_ACQUIRE) == 0u) return TOPK_SUCCESS;
-  __atomic_store_n(word, 0u, __ATOMIC_RELEASE);
+// Caller holds g_mu.  The device's page of host-visible fault words.
+topk_status_t ensure_fault_page(DeviceInfo& info) {
+  if (info.fault_page != nullptr) return TOPK_SUCCESS;
+  void* page = nullptr;
+  hipError_t e = hipHostMalloc(&page, kFaultWords * sizeof(uint32_t), hipHostMallocMapped | hipHostMallocCoherent);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("fault page hipHostMalloc: ") + hipGetErrorString(e));
+  }
+  std::memset(page, 0, kFaultWords * sizeof(uint32_t));
+  void* page_dev = nullptr;
+  e = hipHostGetDevicePointer(&page_dev, page, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(page);
+    return hip_fail(e, "hipHostGetDevicePointer");
+  }
+  info.fault_page = static_cast<uint32_t*>(page);
+  info.fault_page_dev = static_cast<uint32_t*>(page_dev);
+  return TOPK_SUCCESS;
+}
+
+// Caller holds g_mu.  `count` is a workspace's fault count (split launches on
+// it whose bounded wait gave up); reports once each time it moves.  The device
+// stores the count when such a launch ends, so a report can come one call
+// late, or from topk_check_faults after a synchronisation.
+topk_status_t take_fault(uint32_t count, uint32_t* reported) {
+  if (count == 0u || count == *reported) return TOPK_SUCCESS;
+  *reported = count;
   return fail(TOPK_ERROR_DEVICE_FAULT,
               "an earlier split-row launch on this stream gave up a cross-workgroup wait (its workgroups were not "
               "all resident at once); that launch's outputs are invalid and must be recomputed; this call queued "
               "nothing");
 }
 
+uint32_t page_word(const DeviceInfo& info, int word) {
+  if (info.fault_page == nullptr || word < 0) return 0u;
+  return __atomic_load_n(info.fault_page + word, __ATOMIC_ACQUIRE);
+}
+
 // Caller holds g_mu.
 topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, int64_t slots, Workspace** out) {
+  topk_status_t st = ensure_fault_page(info);
+  if (st != TOPK_SUCCESS) return st;
   Workspace& w = g_ws[std::make_pair(dev, stream)];
   if (w.fault_word < 0) {
     w.fault_word = info.fault_next < kFaultWords ? info.fault_next++ : kFaultWords - 1;
@@ -160,6 +179,10 @@ topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, int64
   }
   hipError_t e = hipMemsetAsync(p, 0, bytes, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  // a new buffer continues the stream's fault count, so reports stay one per fault
+  if (e == hipSuccess && w.reported != 0u)
+    e = hipMemcpy(static_cast<uint32_t*>(p) + topk::kHdrFaultCount, &w.reported, sizeof(uint32_t),
+                  hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(p);
     return hip_fail(e, "workspace hipMemset");
@@ -356,11 +379,12 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
   return TOPK_SUCCESS;
 }
 
-// Caller holds g_mu.
+// Caller holds g_mu.  With `noalloc` (never with `sorted`) the workspace is
+// the device's static scratch and nothing is allocated.
 topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens, const int32_t* page_table,
                                    int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
                                    hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row,
-                                   bool sorted) {
+                                   bool sorted, bool noalloc = false) {
   t_last_error.clear();
   if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERROR_INVALID_VALUE, "k must be in [1, 2048]");
   if (page_size < 1 || (page_size & (page_size - 1)) != 0)
@@ -385,10 +409,13 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   topk_status_t st = device_info(dev, &info);
   if (st != TOPK_SUCCESS) return st;
   if (!info->supported) return fail(TOPK_ERROR_UNSUPPORTED, "device " + info->arch + " is not gfx950");
-  {
+  if (noalloc) {
+    st = take_fault(page_word(*info, 0), &info->scratch_reported);
+    if (st != TOPK_SUCCESS) return st;
+  } else {
     auto wit = g_ws.find(std::make_pair(dev, stream));
     if (wit != g_ws.end()) {
-      st = take_fault(*info, wit->second);
+      st = take_fault(page_word(*info, wit->second.fault_word), &wit->second.reported);
       if (st != TOPK_SUCCESS) return st;
     }
   }
@@ -431,12 +458,32 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   if (plan.kind == Kind::kSplit || (plan.kind == Kind::kStream && batch > plan.slots)) {
     // split rows synchronise through per-slot regions; streamed rows beyond
     // the grid are handed out through a counter in the header
-    Workspace* w = nullptr;
-    st = get_workspace(*info, dev, stream, plan.kind == Kind::kSplit ? plan.slots : 0, &w);
-    if (st != TOPK_SUCCESS) return st;
-    a.ws = w->ptr;
-    a.ws_slots = (int32_t)w->slots;
-    a.fault_host = info->fault_page_dev + w->fault_word;
+    const size_t words = plan.kind == Kind::kSplit ? topk::workspace_words(plan.slots) : topk::kHdrWords;
+    if (noalloc) {
+      if (words > topk::kScratchWords) {
+        char msg[200];
+        std::snprintf(msg, sizeof(msg),
+                      "this shape needs %zu words of workspace; the static scratch of the no-allocation entry "
+                      "point holds %zu (16 MiB)",
+                      words, topk::kScratchWords);
+        return fail(TOPK_ERROR_UNSUPPORTED, msg);
+      }
+      if (!info->scratch_zeroed) {
+        e = topk::clear_words(info->scratch, topk::kScratchWords, stream);
+        if (e != hipSuccess) return hip_fail(e, "scratch zero fill");
+        info->scratch_zeroed = true;
+      }
+      a.ws = info->scratch;
+      a.ws_slots = (int32_t)topk::kScratchSlots;
+      a.fault_host = info->fault_page_dev;   // word 0, or none before a page exists
+    } else {
+      Workspace* w = nullptr;
+      st = get_workspace(*info, dev, stream, plan.kind == Kind::kSplit ? plan.slots : 0, &w);
+      if (st != TOPK_SUCCESS) return st;
+      a.ws = w->ptr;
+      a.ws_slots = (int32_t)w->slots;
+      a.fault_host = info->fault_page_dev + w->fault_word;
+    }
   }
   if (plan.kind == Kind::kStream)
     e = topk::launch_stream_rows(plan.stream_variant, a, stream);
@@ -457,11 +504,11 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     if (e != hipSuccess) return hip_fail(e, "sorted finish launch");
   }
   char buf[200];
-  std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s",
+  std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s",
                 kind_name(plan.kind), plan.kind == Kind::kStream ? 0 : topk::kEptValues[plan.ept_idx],
                 (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G),
                 plan.kind == Kind::kStream ? topk::stream_variant_threads(plan.stream_variant) : topk::kThreads, a.vec,
-                sorted ? " + sorted-finish" : "");
+                sorted ? " + sorted-finish" : "", noalloc ? " (static scratch)" : "");
   t_last_launch = buf;
   return TOPK_SUCCESS;
 }
@@ -507,6 +554,27 @@ topk_status_t topk_transform_sorted(const float* scores, const int32_t* seq_lens
                        pages_per_row, true);
 }
 
+topk_status_t topk_transform_noalloc(const float* scores, const int32_t* seq_lens, const int32_t* page_table,
+                                     int32_t k, int32_t page_size, int32_t* out_idx, int32_t* out_raw,
+                                     hipStream_t stream, int32_t batch, int64_t width, int64_t pages_per_row) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  return run_transform_locked(scores, seq_lens, page_table, k, page_size, out_idx, out_raw, stream, batch, width,
+                              pages_per_row, false, true);
+}
+
+topk_status_t topk_init(void) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  t_last_error.clear();
+  DeviceInfo* info = nullptr;
+  topk_status_t st = device_info(dev, &info);
+  if (st != TOPK_SUCCESS) return st;
+  if (!info->supported) return fail(TOPK_ERROR_UNSUPPORTED, "device " + info->arch + " is not gfx950");
+  return ensure_fault_page(*info);
+}
+
 const char* topk_status_string(topk_status_t status) {
   switch (status) {
     case TOPK_SUCCESS: return "TOPK_SUCCESS";
@@ -528,14 +596,10 @@ topk_status_t topk_release_workspaces(void) {
   if (g_ws.empty() && g_meta.empty() && g_retired.empty() && !indexer::has_buffers()) return TOPK_SUCCESS;
   hipError_t e = hipDeviceSynchronize();
   indexer::release_buffers();
-  // A released workspace's pending fault report goes with it (the streams'
-  // fault words stay assigned, so they are cleared here).
-  for (auto& kv : g_ws) {
+  // A released workspace's pending fault report goes with it: a stream's next
+  // workspace gets a fresh fault word.
+  for (auto& kv : g_ws)
     if (kv.second.ptr) (void)hipFree(kv.second.ptr);
-    auto dit = g_devices.find(kv.first.first);
-    if (dit != g_devices.end() && dit->second.fault_page != nullptr && kv.second.fault_word >= 0)
-      __atomic_store_n(dit->second.fault_page + kv.second.fault_word, 0u, __ATOMIC_RELEASE);
-  }
   g_ws.clear();
   for (auto& kv : g_meta)
     if (kv.second.ptr) (void)hipFree(kv.second.ptr);
@@ -570,12 +634,25 @@ topk_status_t topk_check_faults(hipStream_t stream) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(g_mu);
   t_last_error.clear();
-  auto it = g_ws.find(std::make_pair(dev, stream));
   auto dit = g_devices.find(dev);
-  if (it == g_ws.end() || dit == g_devices.end()) return TOPK_SUCCESS;
+  if (dit == g_devices.end()) return TOPK_SUCCESS;
+  DeviceInfo& info = dit->second;
+  auto it = g_ws.find(std::make_pair(dev, stream));
+  if (it == g_ws.end() && !info.scratch_zeroed) return TOPK_SUCCESS;
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  return take_fault(dit->second, it->second);
+  if (it != g_ws.end()) {
+    topk_status_t st = take_fault(page_word(info, it->second.fault_word), &it->second.reported);
+    if (st != TOPK_SUCCESS) return st;
+  }
+  if (info.scratch_zeroed) {
+    // the scratch's count from the device itself (no page may exist yet)
+    uint32_t count = 0;
+    e = hipMemcpy(&count, info.scratch + topk::kHdrFaultCount, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+    return take_fault(count, &info.scratch_reported);
+  }
+  return TOPK_SUCCESS;
 }
 
 topk_status_t topk_set_wait_limit(uint32_t polls) {

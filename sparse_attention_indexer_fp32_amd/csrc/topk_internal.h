@@ -122,4 +122,16 @@ int stream_variant_threads(int variant);
 hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream);
 hipError_t sorted_occupancy(int* blocks_per_cu);
 
+// The library's static device scratch: the workspace of the entry point that
+// allocates nothing (topk_transform_noalloc).  One copy per device, 16 MiB,
+// which holds the header and up to kScratchSlots split-row slots.
+constexpr size_t kScratchWords = (size_t)4 << 20;
+constexpr int64_t kScratchSlots = (int64_t)((kScratchWords - kHdrWords) / (kBarWords + 2 * kRegionWords));
+// Its address on the current device (hipGetSymbolAddress: the array's
+// host-side name is not a device address).  Called once per device.
+hipError_t scratch_address(uint32_t** ptr);
+// Zero-fills `words` words at p with a kernel on `stream` (no memset node, so
+// it may be captured in a graph).
+hipError_t clear_words(uint32_t* p, size_t words, hipStream_t stream);
+
 }  // namespace topk

@@ -1516,7 +1516,29 @@ hipError_t occupancy_e(bool coop, int* blocks) {
                                                       kThreads, 0);
 }
 
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint32_t* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * 256u + threadIdx.x; i < words; i += (size_t)gridDim.x * 256u) p[i] = 0u;
+}
+
 }  // namespace
+
+// The workspace of the entry point that allocates nothing: split-row barrier
+// blocks and regions, and the streaming row queue, in the layout of an
+// allocated workspace of kScratchSlots slots.  Each device holds its own copy
+// for the life of the process.  It is zero-filled once before its first use;
+// every kernel leaves it as it found it (zeroes), or, after a wait gave up,
+// the launch's last workgroup zeroes it.  Host code must use the address
+// scratch_address() returns, never the array's name.
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+hipError_t scratch_address(uint32_t** ptr) {
+  return hipGetSymbolAddress(reinterpret_cast<void**>(ptr), HIP_SYMBOL(scratch));
+}
+
+hipError_t clear_words(uint32_t* p, size_t words, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, stream, p, words);
+  return hipGetLastError();
+}
 
 hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStream_t stream) {
   switch (ept_index) {
