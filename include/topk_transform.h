@@ -225,6 +225,25 @@ topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_p
  */
 topk_status_t topk_set_stream_shape(int32_t shape);
 
+/*
+ * Testing and tuning override of the split streaming kernel, process-wide
+ * (split streaming: G workgroups share a row, each streams a contiguous
+ * segment behind its own sampled gate, and the last one to finish selects
+ * from the merged lists):
+ *   shape        -1 = automatic (the dispatcher decides), else a compiled
+ *                shape forced for every call:
+ *                  0: 1024-thread workgroups, two per CU, an 8K-position
+ *                     sample, two 8K-position chunks in flight;
+ *                  1: 1024-thread workgroups, one per CU, a 16K-position
+ *                     sample, three 16K-position chunks in flight;
+ *   wgs_per_row  G, 1 <= G <= 1024, when shape >= 0.
+ * A forced call whose batch * G workgroups do not fit resident at once
+ * returns TOPK_ERROR_UNSUPPORTED.  Every shape and G are exact for every
+ * input; the choice only moves time.  Returns TOPK_ERROR_INVALID_VALUE for
+ * other values.
+ */
+topk_status_t topk_set_split_stream(int32_t shape, int32_t wgs_per_row);
+
 /* Synchronises `stream`, then reports whether a split-row launch queued on
  * it (or, on this device, through topk_transform_noalloc) gave up a bounded
  * cross-workgroup wait since the last report: returns TOPK_ERROR_DEVICE_FAULT

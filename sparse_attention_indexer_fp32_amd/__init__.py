@@ -18,12 +18,13 @@ from .build import LIB_PATH
 
 TOPK_MAX_K = 2048
 STREAM_SHAPES = 3   # compiled streaming-kernel shapes: topk_set_stream_shape accepts -1 and 0..STREAM_SHAPES-1
+SPLIT_STREAM_SHAPES = 2   # compiled split streaming shapes: topk_set_split_stream accepts -1 and 0..1
 STATUS = {0: "TOPK_SUCCESS", 1: "TOPK_ERROR_INVALID_VALUE", 2: "TOPK_ERROR_UNSUPPORTED",
           3: "TOPK_ERROR_OUT_OF_MEMORY", 4: "TOPK_ERROR_LAUNCH", 5: "TOPK_ERROR_DEVICE_FAULT"}
 TOPK_ERROR_DEVICE_FAULT = 5
 
 EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_transform_noalloc", "topk_init", "topk_status_string", "topk_last_error", "topk_last_launch",
-            "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape",
+            "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape", "topk_set_split_stream",
             "topk_check_faults", "topk_set_wait_limit", "topk_abi_version", "indexer_logits", "indexer_topk",
             "indexer_set_window_override")
 INDEXER_HEADS = 32
@@ -68,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topk_set_dispatch_override.restype = ctypes.c_int
     lib.topk_set_stream_shape.argtypes = [c_i32]
     lib.topk_set_stream_shape.restype = ctypes.c_int
+    lib.topk_set_split_stream.argtypes = [c_i32, c_i32]
+    lib.topk_set_split_stream.restype = ctypes.c_int
     lib.topk_check_faults.argtypes = [c_vp]
     lib.topk_check_faults.restype = ctypes.c_int
     lib.topk_set_wait_limit.argtypes = [ctypes.c_uint32]
@@ -188,6 +191,12 @@ def topk_release_workspaces() -> None:
 
 def topk_set_dispatch_override(elems_per_thread: int = 0, wgs_per_row: int = 0) -> None:
     _check(load().topk_set_dispatch_override(int(elems_per_thread), int(wgs_per_row)))
+
+
+def topk_set_split_stream(shape: int = -1, wgs_per_row: int = 0) -> None:
+    """Testing/tuning override: force the split streaming kernel's shape with
+    `wgs_per_row` workgroups per row (shape -1 restores automatic dispatch)."""
+    _check(load().topk_set_split_stream(int(shape), int(wgs_per_row)))
 
 
 def topk_set_stream_shape(shape: int = -1) -> None:

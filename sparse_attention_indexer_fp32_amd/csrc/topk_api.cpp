@@ -15,6 +15,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -44,6 +46,7 @@ struct DeviceInfo {
   int occ[2][topk::kNumEpt] = {};   // [split][ept] resident workgroups per CU
   int stream_occ[topk::kNumStreamVariants] = {};   // streaming kernel shapes: resident workgroups per CU
   int sorted_occ = 0;               // sorted finish: resident workgroups per CU
+  int ss_occ[topk::kNumSplitStreamVariants] = {};   // split streaming shapes: resident workgroups per CU
   uint32_t* fault_page = nullptr;   // pinned, device-mapped host memory (kFaultWords words), or null
   uint32_t* fault_page_dev = nullptr;   // its device address
   int fault_next = 1;               // next unassigned word of the page
@@ -55,7 +58,7 @@ struct DeviceInfo {
 
 struct Workspace {
   uint32_t* ptr = nullptr;
-  int64_t slots = 0;
+  size_t words = 0;
   int fault_word = -1;              // this workspace's word of the device's fault page
   uint32_t reported = 0;            // its fault count last reported
 };
@@ -65,13 +68,15 @@ struct Workspace {
 std::mutex& g_mu = topk::lib_mutex();
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-std::map<std::pair<int, hipStream_t>, Workspace> g_meta;   // sorted mode: records + raw positions ("slots" = words)
+std::map<std::pair<int, hipStream_t>, Workspace> g_meta;   // sorted mode: records + raw positions
 // Buffers replaced by larger ones.  A graph captured before the growth still
 // names them, so they stay allocated until topk_release_workspaces.
 std::vector<void*> g_retired;
 int g_override_ept = 0;
 int g_override_wgs = 0;
 int g_stream_variant = -1;   // -1: the default streaming shape
+int g_ss_variant = -1;       // split streaming override: -1 automatic, else the shape forced
+int g_ss_wgs = 0;            // ... with this many workgroups per row
 uint32_t g_spin_limit = topk::kDefaultSpinLimit;
 
 topk_status_t fail(topk_status_t st, const std::string& msg) {
@@ -109,6 +114,10 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
     }
     e = topk::sorted_occupancy(&info.sorted_occ);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    for (int v = 0; v < topk::kNumSplitStreamVariants; ++v) {
+      e = topk::split_stream_occupancy(v, &info.ss_occ[v]);
+      if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    }
     // set-up of the static scratch: its address on this (the current) device
     e = topk::scratch_address(&info.scratch);
     if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
@@ -157,7 +166,7 @@ uint32_t page_word(const DeviceInfo& info, int word) {
 }
 
 // Caller holds g_mu.
-topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, int64_t slots, Workspace** out) {
+topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, size_t words, Workspace** out) {
   topk_status_t st = ensure_fault_page(info);
   if (st != TOPK_SUCCESS) return st;
   Workspace& w = g_ws[std::make_pair(dev, stream)];
@@ -165,8 +174,8 @@ topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, int64
     w.fault_word = info.fault_next < kFaultWords ? info.fault_next++ : kFaultWords - 1;
   }
   *out = &w;
-  if (w.ptr && w.slots >= slots) return TOPK_SUCCESS;
-  const size_t bytes = topk::workspace_words(slots) * sizeof(uint32_t);
+  if (w.ptr && w.words >= words) return TOPK_SUCCESS;
+  const size_t bytes = words * sizeof(uint32_t);
   void* p = nullptr;
   if (std::getenv("TOPK_TEST_FAIL_ALLOC") == nullptr) {
     hipError_t e = hipMalloc(&p, bytes);
@@ -189,7 +198,7 @@ topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, int64
   }
   if (w.ptr) g_retired.push_back(w.ptr);
   w.ptr = static_cast<uint32_t*>(p);
-  w.slots = slots;
+  w.words = words;
   return TOPK_SUCCESS;
 }
 
@@ -199,7 +208,7 @@ topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, int64
 // reads it, so the buffer needs no clearing.
 topk_status_t get_meta(int dev, hipStream_t stream, int64_t words, uint32_t** ptr) {
   Workspace& w = g_meta[std::make_pair(dev, stream)];
-  if (w.ptr && w.slots >= words) {
+  if (w.ptr && w.words >= (size_t)words) {
     *ptr = w.ptr;
     return TOPK_SUCCESS;
   }
@@ -211,7 +220,7 @@ topk_status_t get_meta(int dev, hipStream_t stream, int64_t words, uint32_t** pt
   }
   if (w.ptr) g_retired.push_back(w.ptr);
   w.ptr = static_cast<uint32_t*>(p);
-  w.slots = words;
+  w.words = (size_t)words;
   *ptr = w.ptr;
   return TOPK_SUCCESS;
 }
@@ -224,7 +233,7 @@ int ept_index(int ept) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-enum class Kind { kResident, kSplit, kStream };
+enum class Kind { kResident, kSplit, kStream, kSplitStream };
 
 // Preferred upper bound on workgroups sharing one split row.
 constexpr int64_t kMaxSplitWgs = 128;
@@ -240,6 +249,7 @@ constexpr int kStreamDeep = 2;
 struct Plan {
   Kind kind = Kind::kStream;
   int stream_variant = kStreamWide;
+  int ss_variant = 0;
   int ept_idx = 0;
   int64_t G = 1;
   int64_t slots = 1;
@@ -250,6 +260,7 @@ const char* kind_name(Kind k) {
     case Kind::kResident: return "row-per-wg-resident";
     case Kind::kSplit: return "split-row";
     case Kind::kStream: return "row-per-wg-stream";
+    case Kind::kSplitStream: return "split-row-stream";
   }
   return "?";
 }
@@ -293,6 +304,35 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
     return idx;
   };
 
+  // split streaming: G workgroups per row, all resident at once
+  auto split_stream = [&](int variant, int64_t G) -> topk_status_t {
+    const int64_t cap = (int64_t)dev.ss_occ[variant] * dev.cus;
+    if (G < 1 || G > topk::kSsMaxParts || B * G > cap || B > (int64_t)topk::kSsMaxRows)
+      return fail(TOPK_ERROR_UNSUPPORTED,
+                  "split streaming takes at most 4 workgroups per row and 256 rows, all resident at once");
+    plan->kind = Kind::kSplitStream;
+    plan->ss_variant = variant;
+    plan->G = G;
+    plan->slots = B;
+    return TOPK_SUCCESS;
+  };
+  if (g_ss_variant >= 0) return split_stream(g_ss_variant, g_ss_wgs > 0 ? g_ss_wgs : 2);
+  // Split streaming rows, where measured to win.  G = CUs / B (2 to 4):
+  // about one workgroup per CU, each streaming a segment of the row.  Only
+  // where a row's merged candidates stay well inside the finisher's list:
+  // the sample (8K positions) sets each segment's gate at the rank
+  // m = mu + 7 sqrt(mu) + 6 of its n * S / L expected top keys, so a row
+  // passes about m * L / S keys; rows whose lists would crowd the list fall
+  // back to re-reading the row, which costs several times more (1M rows at
+  // k 2048: 279 against 76 us).
+  const int64_t ss_G = std::min<int64_t>(topk::kSsMaxParts, std::max<int64_t>(2, dev.cus / std::max<int64_t>(B, 1)));
+  auto split_stream_fits = [&]() {
+    const double S = 8192.0, L = (double)Wc, n = (double)std::min<int64_t>(k, Wc);
+    const double mu = n * std::min(S, L) / L;
+    const double passed = (mu + 7.0 * std::sqrt(mu) + 6.0) * L / S;
+    return g_stream_variant < 0 && B <= (int64_t)topk::kSsMaxRows && passed <= 4500.0 &&
+           (int64_t)dev.ss_occ[0] * dev.cus >= ss_G * B;
+  };
   if (g_override_ept || g_override_wgs) {
     if (g_override_wgs == 1 && g_override_ept == 0) {
       plan->kind = Kind::kStream;
@@ -306,7 +346,21 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
       plan->kind = G > 1 ? Kind::kSplit : Kind::kResident;
     }
   } else if (2 * B >= dev.cus || B >= stream_slots) {
+    // One row per two CUs, rows of 128K and more: two workgroups per row put
+    // every CU to work (measured on MI355X: 128 x 128K, k 512: 24.4 against
+    // 30.1 us; the tie-heavy 128 x 128K, k 1024: 27.4 against 34.1 us; 96 x
+    // 128K, k 1024: 24.9 us).
+    if (plan->stream_variant == kStreamDeep && split_stream_fits()) return split_stream(0, ss_G);
     plan->kind = Kind::kStream;
+  } else if (B >= 32 && Wc >= 32768 && Wc <= 262144 && split_stream_fits()) {
+    // Mid batches of rows up to 256K: G workgroups per row stream a segment
+    // each, with no barrier, where split rows would hold the row in
+    // registers behind one (measured on MI355X at k 2048: 64 ragged rows of
+    // 4K-64K 18.9 against 23.1 us; 64 x 256K 28.6 against 43.9 us; 48 x 96K
+    // 20.0 us; 32 x 128K 21.1 against 23.2 us; at k 512, 64 x 64K 15.4
+    // against 21.1 us and 32 x 256K 22.3 us).  Fewer rows stay split: 16 x
+    // 256K 22.8 us split against 26.0 us.
+    return split_stream(0, ss_G);
   } else if (Wc <= (int64_t)topk::kThreads * 16) {
     // few short rows: one workgroup each, the row in registers (1 x 16K, k 512:
     // 10.2 us against 12.6 us streamed)
@@ -350,7 +404,11 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
       }
     }
     if (chosen < 0) {
-      plan->kind = Kind::kStream;   // too many rows to hold resident: stream them
+      // too many rows to hold resident: stream them, G workgroups per row
+      // where that fits (100 x 256K at k 2048: 38.6 against 46.9 us streamed
+      // one per workgroup; 120 x 512K at k 512: 54.5 against 65.1 us)
+      if (plan->stream_variant == kStreamDeep && split_stream_fits()) return split_stream(0, ss_G);
+      plan->kind = Kind::kStream;
     } else {
       plan->ept_idx = chosen;
       plan->G = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[chosen]);
@@ -365,6 +423,8 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
       break;
     case Kind::kResident:
       plan->slots = B;
+      break;
+    case Kind::kSplitStream:
       break;
     case Kind::kSplit: {
       const int64_t cap = (int64_t)dev.occ[1][plan->ept_idx] * dev.cus;
@@ -455,10 +515,14 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     if (!out_raw) a.out_raw = reinterpret_cast<int32_t*>(a.meta + rec);
     a.sel = a.out_raw;
   }
-  if (plan.kind == Kind::kSplit || (plan.kind == Kind::kStream && batch > plan.slots)) {
-    // split rows synchronise through per-slot regions; streamed rows beyond
-    // the grid are handed out through a counter in the header
-    const size_t words = plan.kind == Kind::kSplit ? topk::workspace_words(plan.slots) : topk::kHdrWords;
+  if (plan.kind == Kind::kSplit || plan.kind == Kind::kSplitStream ||
+      (plan.kind == Kind::kStream && batch > plan.slots)) {
+    // split rows synchronise through per-slot regions, split streaming rows
+    // through per-row areas; streamed rows beyond the grid are handed out
+    // through a counter in the header
+    const size_t words = plan.kind == Kind::kSplit         ? topk::workspace_words(plan.slots)
+                         : plan.kind == Kind::kSplitStream ? topk::split_stream_words(batch)
+                                                           : topk::kHdrWords;
     if (noalloc) {
       if (words > topk::kScratchWords) {
         char msg[200];
@@ -478,15 +542,17 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
       a.fault_host = info->fault_page_dev;   // word 0, or none before a page exists
     } else {
       Workspace* w = nullptr;
-      st = get_workspace(*info, dev, stream, plan.kind == Kind::kSplit ? plan.slots : 0, &w);
+      st = get_workspace(*info, dev, stream, words, &w);
       if (st != TOPK_SUCCESS) return st;
       a.ws = w->ptr;
-      a.ws_slots = (int32_t)w->slots;
+      a.ws_slots = (int32_t)topk::workspace_slots(w->words);
       a.fault_host = info->fault_page_dev + w->fault_word;
     }
   }
   if (plan.kind == Kind::kStream)
     e = topk::launch_stream_rows(plan.stream_variant, a, stream);
+  else if (plan.kind == Kind::kSplitStream)
+    e = topk::launch_split_stream(plan.ss_variant, a, stream);
   else
     e = topk::launch_rows(plan.ept_idx, plan.kind == Kind::kSplit, a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
@@ -505,7 +571,8 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   }
   char buf[200];
   std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s",
-                kind_name(plan.kind), plan.kind == Kind::kStream ? 0 : topk::kEptValues[plan.ept_idx],
+                kind_name(plan.kind),
+                plan.kind == Kind::kStream || plan.kind == Kind::kSplitStream ? 0 : topk::kEptValues[plan.ept_idx],
                 (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G),
                 plan.kind == Kind::kStream ? topk::stream_variant_threads(plan.stream_variant) : topk::kThreads, a.vec,
                 sorted ? " + sorted-finish" : "", noalloc ? " (static scratch)" : "");
@@ -617,6 +684,17 @@ topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_p
   std::lock_guard<std::mutex> lock(g_mu);
   g_override_ept = elems_per_thread;
   g_override_wgs = wgs_per_row;
+  return TOPK_SUCCESS;
+}
+
+topk_status_t topk_set_split_stream(int32_t shape, int32_t wgs_per_row) {
+  if (shape < -1 || shape >= topk::kNumSplitStreamVariants)
+    return fail(TOPK_ERROR_INVALID_VALUE, "shape must be -1 (automatic) or a compiled split streaming shape index");
+  if (shape >= 0 && (wgs_per_row < 1 || wgs_per_row > 1024))
+    return fail(TOPK_ERROR_INVALID_VALUE, "wgs_per_row must be in [1, 1024]");
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_ss_variant = shape;
+  g_ss_wgs = shape >= 0 ? wgs_per_row : 0;
   return TOPK_SUCCESS;
 }
 

@@ -42,8 +42,11 @@ constexpr int kEptValues[kNumEpt] = {4, 8, 16, 32, 64};
 // cleared while the slot's other workgroups already accumulate the next row.
 // Every region is left zeroed by the workgroup that finishes its row.
 // ---------------------------------------------------------------------------
-// Header words, each group on its own 128-byte line.
-constexpr size_t kHdrWords = 128;
+// Header words, each group on its own 128-byte line; then the split streaming
+// kernel's per-row counters.
+constexpr size_t kSsMaxRows = 256;      // rows a split streaming launch may have
+constexpr size_t kSsCtr = 128;          // per-row counters: 4 words per row
+constexpr size_t kHdrWords = kSsCtr + 4 * kSsMaxRows;
 constexpr size_t kHdrFault = 0;         // nonzero while a split launch in which a bounded wait gave up runs
 constexpr size_t kHdrFaultCount = 1;    // split launches in which a wait gave up, ever (read by the host)
 constexpr size_t kHdrRowTicket = 32;    // streaming kernel: rows handed out beyond the first grid's
@@ -73,6 +76,26 @@ constexpr size_t kRegionWords = kRegCandPos + kCandCap;
 inline size_t workspace_words(int64_t slots) {
   return kHdrWords + (size_t)slots * kBarWords + (size_t)slots * 2 * kRegionWords;
 }
+// Split-row slots a workspace of `words` words is laid out for.
+inline int64_t workspace_slots(size_t words) {
+  return words > kHdrWords ? (int64_t)((words - kHdrWords) / (kBarWords + 2 * kRegionWords)) : 0;
+}
+
+// Split streaming rows: four counters per row in the header (zero at rest;
+// the row's finisher resets them), and an entry area per row after the
+// header (kSsRowWords each).  The entry areas overlap the split-row layout,
+// whose regions must be zero at rest; the finisher zeroes the entries it used.
+constexpr size_t kSsExit = 0;           // 64-bit: workgroups done with the row, and each part's entry count
+constexpr size_t kSsFloor = 2;          // the largest of the parts' gates (atomic max)
+constexpr size_t kSsFlag = 3;           // nonzero: a part's list lost keys
+constexpr int kSsMaxParts = 4;          // workgroups per row (parts) at most
+constexpr int kSsExitBits = 4;          // exit word: bits [0, 4) count the parts out,
+constexpr int kSsCountBits = 13;        // then 13 bits per part for its entry count
+constexpr size_t kSsCap = 8192;         // entries an area holds (kSsCap / G per part)
+constexpr size_t kSsKeys = 0;
+constexpr size_t kSsPos = kSsKeys + kSsCap;
+constexpr size_t kSsRowWords = kSsPos + kSsCap;
+inline size_t split_stream_words(int64_t batch) { return kHdrWords + (size_t)batch * kSsRowWords; }
 
 // Sorted mode: per-row selection record (prefix, shift, need, floor, cut).
 constexpr size_t kMetaWords = 8;
@@ -115,6 +138,12 @@ constexpr int kNumStreamVariants = 3;
 hipError_t launch_stream_rows(int variant, const KernelArgs& args, hipStream_t stream);
 hipError_t stream_occupancy(int variant, int* blocks_per_cu);
 int stream_variant_threads(int variant);
+
+// Split streaming kernel: G workgroups per row (wgs_per_row), grid = batch *
+// G, all resident at once.  `variant` selects a compiled shape.
+constexpr int kNumSplitStreamVariants = 2;
+hipError_t launch_split_stream(int variant, const KernelArgs& args, hipStream_t stream);
+hipError_t split_stream_occupancy(int variant, int* blocks_per_cu);
 
 // Sorted finish (deterministic mode): one workgroup per row, persistent over
 // rows (grid = slots); reads the per-row records a selection launch left in

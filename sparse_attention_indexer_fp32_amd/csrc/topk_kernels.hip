@@ -1227,6 +1227,310 @@ stream_rows_kernel(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Split streaming rows (split_stream_kernel): mid batches of long rows.
+//
+// With fewer rows than CUs, one workgroup per row leaves CUs idle.  Here G
+// workgroups share a row (grid = batch * G, every workgroup resident), and
+// workgroup g streams the contiguous segment g of the row exactly as the
+// streaming kernel streams a whole row: a gate from a sample of its segment
+// (ranked for the row's n, so it estimates the row's threshold), the keys at
+// or above it appended to an LDS list while the rest of the segment streams
+// past, the gate raised when the list fills.  Then, instead of a barrier:
+//   * each workgroup writes its list to its own share of the row's area in
+//     the workspace, raises the row's floor to its own gate (an atomic max)
+//     and flags a list that lost keys;
+//   * it counts itself out of the row on one 64-bit word that also sums every
+//     part's entry count (each in its own bit field); the last one out
+//     finishes the row, with every count in hand.
+// Every segment's keys at or above that segment's gate are in the area, so
+// the keys at or above the floor (the largest gate) are all there.  If at
+// least n of them are, the row's n largest are among them, and the finisher
+// selects from its LDS copy exactly as the streaming kernel's finish does.
+// Otherwise (fewer than n, or a list lost keys) it finishes the row from
+// memory (the streaming kernel's exact fallback).  No workgroup ever waits
+// for another, so nothing depends on co-residency.
+//
+// Per row: four counters in the header, and an area (kSsRowWords words after
+// the header) for the appended keys and positions.  The finisher resets the
+// counters and zeroes the entries it used, so the workspace is as it was when
+// the launch ends.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void g_max(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t g_add64_ret(uint64_t* p, uint64_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool REFINE>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
+split_stream_kernel(KernelArgs a) {
+  constexpr uint32_t kSampleSpan = (uint32_t)NT * 4u * SV;
+  constexpr uint32_t kChunkSpan = (uint32_t)NT * 4u * CV;
+  constexpr uint32_t kRefresh = CAP - CAP / 4;
+  constexpr int kLoadPer = (int)(kSsCap / NT);   // area entries per thread the finisher loads at once
+  static_assert(CAP >= kBinsNarrow, "the candidate list doubles as the gate's sub-histogram");
+  static_assert(kSsCap % NT == 0, "the finisher loads the area in whole rounds");
+  static_assert(CAP < (1 << kSsCountBits), "a part's entry count fits its field of the exit word");
+  __shared__ uint32_t sh_hist[kBinsWide];
+  __shared__ uint32_t sh_ckey[CAP + 1];
+  __shared__ int32_t sh_cpos[CAP + 1];
+  __shared__ uint32_t sh_scan[64];
+  static_assert(kBinsWide - kMaxK >= kBinsNarrow, "selected positions alias the histogram's upper half");
+  int32_t* const sh_raw = reinterpret_cast<int32_t*>(sh_hist + (kBinsWide - kMaxK));
+  __shared__ uint32_t sh_var[16];
+
+  const int G = a.wgs_per_row;
+  const int64_t row = (int64_t)(blockIdx.x / (uint32_t)G);
+  const uint32_t part = blockIdx.x - (uint32_t)row * (uint32_t)G;
+  if (row >= a.batch) return;
+  const int tid = opaque_tid();
+  const int64_t W = a.width;
+  const int k = a.k;
+  const bool vec = a.vec != 0;
+  const int32_t seq = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+  const int64_t L64 = seq < 0 ? 0 : ((int64_t)seq > W ? W : (int64_t)seq);
+  const uint32_t L = (uint32_t)L64;
+  const int n = L64 < (int64_t)k ? (int)L64 : k;
+  if (L64 <= (int64_t)k) {   // every valid position is selected; the row's area is not used
+    if (part == 0u) {
+      write_row_output<NT>(a, row, L64, n, true, sh_raw, tid);
+      if (tid == 0) record_selection(a, row, 0u, 32, (uint32_t)n, (uint32_t)n, 0u);
+    }
+    return;
+  }
+  // Segment [s0, s1): whole multiples of one float4 per thread, so every
+  // segment starts 16-byte aligned.
+  const uint32_t per = (L + (uint32_t)G - 1u) / (uint32_t)G;
+  const uint32_t seglen = (per + 4u * NT - 1u) / (4u * NT) * (4u * NT);
+  const uint32_t s0 = part * seglen < L ? part * seglen : L;
+  const uint32_t s1 = L - s0 > seglen ? s0 + seglen : L;
+  uint32_t* const ctr = a.ws + kSsCtr + 4 * (size_t)row;
+  uint32_t* const area = a.ws + kHdrWords + (size_t)row * kSsRowWords;
+  const float* rowp = a.scores + row * W;
+
+  for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
+  if (tid < 16) sh_var[tid] = 0;
+  __syncthreads();
+  uint32_t gate = 0u;
+  if (s0 < s1) {
+    // 1. sample: the first kSampleSpan positions of the segment
+    uint32_t sk[4 * SV];
+    load_raw<NT, SV>(sk, rowp, s0, s1, vec, tid);
+    const uint32_t seg = s1 - s0;
+    const uint32_t nch = seg > kSampleSpan ? (seg - kSampleSpan + kChunkSpan - 1) / kChunkSpan : 0u;
+#pragma unroll
+    for (int j = 0; j < 4 * SV; ++j) {
+      const uint32_t x = slot_key<NT>(sk[j], j, s0, s1, tid);
+      if (x) atomicAdd(&sh_hist[x >> 20], 1u);
+    }
+    __syncthreads();
+    // The first chunks are requested only now: every workgroup of the launch
+    // starts at once, and samples requested alone arrive sooner; these loads
+    // then stream in while the gate is worked out.
+    uint32_t ring[NBUF][4 * CV];
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b)
+      if ((uint32_t)b < nch) load_raw<NT, CV>(ring[b], rowp, s0 + kSampleSpan + (uint32_t)b * kChunkSpan, s1, vec, tid);
+    // ranked for the row: the sample holds on average n * S / L of the row's n largest
+    const uint32_t m = gate_rank((uint32_t)n, seg < kSampleSpan ? seg : kSampleSpan, L);
+    find_threshold<NT, kBinsWide>(sh_hist, m, sh_scan, sh_var, tid);
+    const uint32_t gbin = uniform(sh_var[0]), gneed = m - uniform(sh_var[1]);
+    gate = gbin << 20;
+    if (REFINE) {   // the gate refined inside its bin with the next 10 key bits
+      for (int b = tid; b < kBinsNarrow; b += NT) sh_ckey[b] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4 * SV; ++j) {
+        const uint32_t x = slot_key<NT>(sk[j], j, s0, s1, tid);
+        if (x != 0u && (x >> 20) == gbin) atomicAdd(&sh_ckey[(x >> 10) & 1023u], 1u);
+      }
+      __syncthreads();
+      find_threshold<NT, kBinsNarrow>(sh_ckey, gneed, sh_scan, sh_var, tid);
+      gate |= uniform(sh_var[0]) << 10;
+    }
+    if (gate == 0u) gate = 1u;
+    {
+      static_assert(SV % 2 == 0, "the sample is appended in two halves");
+      uint32_t lo[2 * SV], hi[2 * SV];
+#pragma unroll
+      for (int j = 0; j < 2 * SV; ++j) {
+        lo[j] = sk[j];
+        hi[j] = sk[2 * SV + j];
+      }
+      constexpr uint32_t half = (uint32_t)NT * 4u * (SV / 2);
+      gated_append<NT, CAP, 2 * SV, kGateChecked>(lo, s0, s1, gate, sh_ckey, sh_cpos, sh_var, tid);
+      gated_append<NT, CAP, 2 * SV, kGateChecked>(hi, s0 + half, s1, gate, sh_ckey, sh_cpos, sh_var, tid);
+    }
+    // 2. stream the rest of the segment through the ring
+    for (uint32_t i = 0; i < nch; i += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        const uint32_t idx = i + (uint32_t)b;
+        if (idx < nch) {
+          const uint32_t cbase = s0 + kSampleSpan + idx * kChunkSpan;
+          if (cbase + kChunkSpan > s1)
+            gated_append<NT, CAP, 4 * CV, kGateChecked>(ring[b], cbase, s1, gate, sh_ckey, sh_cpos, sh_var, tid);
+          else if (gate >= 0x80000000u)
+            gated_append<NT, CAP, 4 * CV, kGatePositive>(ring[b], cbase, s1, gate, sh_ckey, sh_cpos, sh_var, tid);
+          else
+            gated_append<NT, CAP, 4 * CV, kGateAny>(ring[b], cbase, s1, gate, sh_ckey, sh_cpos, sh_var, tid);
+          if (idx + NBUF < nch)
+            load_raw<NT, CV>(ring[b], rowp, s0 + kSampleSpan + (idx + NBUF) * kChunkSpan, s1, vec, tid);
+        }
+      }
+      __syncthreads();
+      if (uniform(sh_var[kVarCandCount]) > kRefresh)
+        gate = raise_gate<NT, CAP>(gate, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_scan, sh_var, tid);
+    }
+  }
+  __syncthreads();   // every wave's appends are in
+
+  // 3. publish the segment's list (keys >= gate, all of them unless it lost
+  // some) in the part's own share of the row's area, then count out on the
+  // row's exit word, which also carries every part's entry count.
+  const uint32_t partcap = (uint32_t)kSsCap / (uint32_t)G;
+  {
+    const uint32_t count = uniform(sh_var[kVarCandCount]);
+    const uint32_t ncur = count < (uint32_t)CAP ? count : (uint32_t)CAP;
+    const uint32_t nput = ncur < partcap ? ncur : partcap;
+    const bool lost = uniform(sh_var[kVarOverflow]) != 0u || count > (uint32_t)CAP || ncur > partcap;
+    for (uint32_t i = (uint32_t)tid; i < nput; i += NT) {
+      g_store(area + kSsKeys + part * partcap + i, sh_ckey[i]);
+      g_store(area + kSsPos + part * partcap + i, (uint32_t)sh_cpos[i]);
+    }
+    if (tid == 0) {
+      if (gate != 0u) g_max(ctr + kSsFloor, gate);
+      if (lost) g_store(ctr + kSsFlag, 1u);
+    }
+    wave_mem_drain();
+    __syncthreads();
+    if (tid == 0) {
+      const uint64_t mine = 1ull | ((uint64_t)nput << (kSsExitBits + kSsCountBits * part));
+      const uint64_t all = g_add64_ret(reinterpret_cast<uint64_t*>(ctr + kSsExit), mine) + mine;
+      const bool last = (uint32_t)(all & ((1ull << kSsExitBits) - 1ull)) == (uint32_t)G;
+      sh_var[4] = last ? 1u : 0u;
+#pragma unroll
+      for (int g = 0; g < kSsMaxParts; ++g)
+        sh_var[5 + g] = (uint32_t)(all >> (kSsExitBits + kSsCountBits * g)) & ((1u << kSsCountBits) - 1u);
+    }
+    __syncthreads();
+    if (uniform(sh_var[4]) == 0u) return;
+  }
+
+  // 4. the last workgroup out finishes the row.  Every other workgroup drained
+  // its appends and its floor before counting itself out; the exit word gave
+  // every part's count, so the floor, the flag and the entries are requested
+  // together.
+  uint32_t pc[kSsMaxParts], pstart[kSsMaxParts + 1];
+  pstart[0] = 0u;
+#pragma unroll
+  for (int g = 0; g < kSsMaxParts; ++g) {
+    pc[g] = g < G ? uniform(sh_var[5 + g]) : 0u;
+    pstart[g + 1] = pstart[g] + pc[g];
+  }
+  const uint32_t nload = pstart[kSsMaxParts];
+  uint32_t xk[kLoadPer], xp[kLoadPer];
+#pragma unroll
+  for (int r = 0; r < kLoadPer; ++r) {
+    const uint32_t i = (uint32_t)tid + (uint32_t)r * NT;
+    uint32_t g = 0;
+#pragma unroll
+    for (int q = 1; q < kSsMaxParts; ++q) g += i >= pstart[q] ? 1u : 0u;
+    const uint32_t at = g * partcap + (i - pstart[g]);
+    xk[r] = i < nload ? g_load(area + kSsKeys + at) : 0u;
+    xp[r] = i < nload ? g_load(area + kSsPos + at) : 0u;
+  }
+  const uint32_t floor0 = g_load(ctr + kSsFloor);   // >= 1: the row has a nonempty segment
+  const bool lost = g_load(ctr + kSsFlag) != 0u;
+  if (tid == 0) {
+    sh_var[kVarCandCount] = 0u;
+    sh_var[kVarOverflow] = 0u;
+  }
+  for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
+  __syncthreads();
+  {
+    // the area's keys >= floor into the LDS list: one ballot append per round
+    const int lane = tid & 63;
+#pragma unroll
+    for (int r = 0; r < kLoadPer; ++r) {
+      const bool pass = xk[r] >= floor0 && xk[r] != 0u;
+      const uint64_t msk = __ballot(pass);
+      if (msk == 0ull) continue;
+      uint32_t wbase = 0;
+      if (lane == 0) wbase = atomicAdd(&sh_var[kVarCandCount], (uint32_t)__popcll(msk));
+      wbase = __builtin_amdgcn_readfirstlane(wbase);
+      if (pass) {
+        uint32_t slot = wbase + lanes_below(msk);
+        slot = slot < (uint32_t)CAP ? slot : (uint32_t)CAP;
+        sh_ckey[slot] = xk[r];
+        sh_cpos[slot] = (int32_t)xp[r];
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t count = uniform(sh_var[kVarCandCount]);
+  const bool low_count = count < (uint32_t)n;
+  const bool overflow = lost || low_count || count > (uint32_t)CAP;
+  const uint32_t floor = low_count ? 1u : floor0;
+  if (!overflow) {
+    for (uint32_t i = (uint32_t)tid; i < count; i += NT) atomicAdd(&sh_hist[sh_ckey[i] >> 20], 1u);
+    __syncthreads();
+  } else {
+    restream_pass<NT, CAP, CV>(3, rowp, L, vec, floor, 0u, 20, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
+                               sh_var, tid);
+  }
+  find_threshold<NT, kBinsWide>(sh_hist, (uint32_t)n, sh_scan, sh_var, tid);
+  const uint32_t t0 = uniform(sh_var[0]), gt0 = uniform(sh_var[1]), cnt0 = uniform(sh_var[2]);
+  if (!overflow) {
+    uint32_t fprefix = t0, fneed = (uint32_t)n - gt0, fcnt = cnt0;
+    int fshift = 20;
+    select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
+                          sh_raw, sh_scan, sh_var, tid, true);
+    if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, floor);
+  } else {
+    for (int j = tid; j < k; j += NT) sh_raw[j] = -1;
+    __syncthreads();
+    uint32_t prefix = t0, need = (uint32_t)n - gt0, cnt = cnt0;
+    int shift = 20;
+    while (cnt > (uint32_t)CAP && cnt != need && shift > 0) {
+      for (int b = tid; b < kBinsNarrow; b += NT) sh_hist[b] = 0;
+      __syncthreads();
+      restream_pass<NT, CAP, CV>(0, rowp, L, vec, floor, prefix, shift, need, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
+                                 sh_raw, sh_var, tid);
+      find_threshold<NT, kBinsNarrow>(sh_hist, need, sh_scan, sh_var, tid);
+      const uint32_t bin = uniform(sh_var[0]), gt = uniform(sh_var[1]);
+      cnt = uniform(sh_var[2]);
+      need -= gt;
+      prefix = (prefix << 10) | bin;
+      shift -= 10;
+    }
+    if (tid == 0) {
+      sh_var[kVarGt] = 0;
+      sh_var[kVarEq] = 0;
+    }
+    __syncthreads();
+    const bool collect = cnt <= (uint32_t)CAP && cnt != need && shift > 0;
+    restream_pass<NT, CAP, CV>(collect ? 1 : 2, rowp, L, vec, floor, prefix, shift, need, (uint32_t)n, sh_hist, sh_ckey,
+                               sh_cpos, sh_raw, sh_var, tid);
+    if (collect)
+      select_candidates<NT>((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist, sh_ckey,
+                            sh_cpos, sh_raw, sh_scan, sh_var, tid);
+    if (tid == 0) record_selection(a, row, prefix, shift, need, cnt, floor);
+  }
+  __syncthreads();
+  write_row_output<NT>(a, row, L64, n, false, sh_raw, tid);
+  // leave the row's area and counters zeroed
+#pragma unroll
+  for (int g = 0; g < kSsMaxParts; ++g)
+    for (uint32_t i = (uint32_t)tid; i < pc[g]; i += NT) {
+      g_store(area + kSsKeys + (uint32_t)g * partcap + i, 0u);
+      g_store(area + kSsPos + (uint32_t)g * partcap + i, 0u);
+    }
+  if (tid < 4) g_store(ctr + tid, 0u);
+}
+
+// ---------------------------------------------------------------------------
 // Sorted finish (deterministic mode).
 //
 // A selection launch recorded, per row, how its threshold ended
@@ -1479,6 +1783,37 @@ hipError_t occupancy_stream_variant(int variant, int* blocks) {
   }
 }
 
+// Split streaming shapes: (threads, sample float4 groups per thread, chunk
+// float4 groups per thread, chunks in flight, LDS candidates, waves per SIMD).
+#define TOPK_SPLIT_STREAM_VARIANTS(X) \
+  X(0, 1024, 2, 2, 2, 6144, 8, true)   \
+  X(1, 1024, 4, 4, 3, 6144, 4, true)
+
+hipError_t launch_split_stream_variant(int variant, const KernelArgs& args, hipStream_t stream) {
+  switch (variant) {
+#define TOPK_SS_LAUNCH_CASE(id, nt, sv, cv, nbuf, cap, waves, refine)                                            \
+  case id:                                                                                                  \
+    hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine>),                         \
+                       dim3((unsigned)args.batch * (unsigned)args.wgs_per_row), dim3(nt), 0, stream, args); \
+    return hipGetLastError();
+    TOPK_SPLIT_STREAM_VARIANTS(TOPK_SS_LAUNCH_CASE)
+#undef TOPK_SS_LAUNCH_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t occupancy_split_stream_variant(int variant, int* blocks) {
+  switch (variant) {
+#define TOPK_SS_OCC_CASE(id, nt, sv, cv, nbuf, cap, waves, refine)                                               \
+  case id:                                                                                              \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                                \
+        blocks, reinterpret_cast<const void*>(&split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine>), nt, 0);
+    TOPK_SPLIT_STREAM_VARIANTS(TOPK_SS_OCC_CASE)
+#undef TOPK_SS_OCC_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int E>
 hipError_t launch_e(bool coop, const KernelArgs& args, hipStream_t stream) {
   // Split rows need every workgroup of a row resident at once; the host sizes
@@ -1556,6 +1891,14 @@ hipError_t launch_stream_rows(int variant, const KernelArgs& args, hipStream_t s
 }
 
 hipError_t stream_occupancy(int variant, int* blocks_per_cu) { return occupancy_stream_variant(variant, blocks_per_cu); }
+
+hipError_t launch_split_stream(int variant, const KernelArgs& args, hipStream_t stream) {
+  return launch_split_stream_variant(variant, args, stream);
+}
+
+hipError_t split_stream_occupancy(int variant, int* blocks_per_cu) {
+  return occupancy_split_stream_variant(variant, blocks_per_cu);
+}
 
 hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream) {
   hipLaunchKernelGGL(sorted_rows_kernel, dim3((unsigned)args.slots), dim3(kThreads), 0, stream, args);

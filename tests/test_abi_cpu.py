@@ -81,6 +81,15 @@ def test_stream_shape_validation(lib):
     assert lib.topk_set_stream_shape(-1) == 0
 
 
+def test_split_stream_override_validation(lib):
+    for shape in range(topk.SPLIT_STREAM_SHAPES):
+        assert lib.topk_set_split_stream(shape, 2) == 0
+    assert lib.topk_set_split_stream(topk.SPLIT_STREAM_SHAPES, 2) == 1
+    assert lib.topk_set_split_stream(0, 0) == 1
+    assert lib.topk_set_split_stream(-2, 0) == 1
+    assert lib.topk_set_split_stream(-1, 0) == 0
+
+
 def test_wait_limit_setter(lib):
     """The testing override of the split rows' wait limit takes any count; 0
     restores the default."""

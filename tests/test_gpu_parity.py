@@ -384,3 +384,96 @@ def test_stream_rows_within_sample_repeated(lib, shape):
         finally:
             lib.topk_set_stream_shape(-1)
             lib.topk_set_dispatch_override(0, 0)
+
+
+# ---- split streaming rows: G workgroups per row, the last one out finishes it
+
+SS_FORCED = [(0, 1), (0, 2), (0, 4), (1, 2), (1, 3)]
+
+
+@pytest.mark.parametrize("shape,G", SS_FORCED)
+@pytest.mark.parametrize("kind", ["normal", "ties", "int", "const", "asc", "desc", "neginf", "zeros"])
+def test_split_stream_forced(lib, shape, G, kind):
+    """Every split streaming shape at several G, on an unaligned width (scalar
+    loads, ragged segments) with short, empty, exactly-k and full rows.  The
+    adversarial kinds drive it through the per-segment gate raise, lists that
+    lose keys, and the finisher's low-count and overflow fallbacks (the row
+    finished from memory)."""
+    W = 90001
+    seq = [W, W - 1, W // 3, 2049, 17000, 0, 513, 2048, -4, W + 9]
+    for k in (1, 700, 2048):
+        w = workloads.custom(500 + 10 * shape + G + k, len(seq), W, k, 16, seq_lens=seq, kind=kind, table="perm")
+        note(f"split stream shape={shape} G={G} kind={kind} k={k}")
+        lib.topk_set_split_stream(shape, G)
+        try:
+            out, raw = run(lib, w, raw=True)
+            assert lib.topk_last_launch().startswith("split-row-stream"), lib.topk_last_launch()
+        finally:
+            lib.topk_set_split_stream(-1, 0)
+        check(w, out, raw)
+
+
+@pytest.mark.parametrize("shape,G", [(0, 4), (1, 2)])
+def test_split_stream_aligned_repeated(lib, shape, G):
+    """dwordx4 loads (aligned width), a permuted table, no raw output, and
+    repeated calls with different lengths: each call leaves the rows' areas
+    zeroed for the next."""
+    W = 131072
+    rng = np.random.Generator(np.random.PCG64(510 + shape))
+    for rep in range(4):
+        seq = rng.integers(1000, W + 1, size=24).tolist()
+        w = workloads.custom(520 + rep, len(seq), W, 1024, 64, seq_lens=seq, kind="normal" if rep % 2 else "ties",
+                             table="perm")
+        note(f"split stream aligned shape={shape} G={G} rep={rep}")
+        lib.topk_set_split_stream(shape, G)
+        try:
+            out, raw = run(lib, w, raw=rep % 2 == 0)
+        finally:
+            lib.topk_set_split_stream(-1, 0)
+        check(w, out, raw)
+
+
+def test_split_stream_graph_replay(lib):
+    """Split streaming rows in a replayed graph, with eager calls between the
+    replays: the row areas reset themselves on every launch."""
+    import torch
+    w = workloads.custom(530, 16, 200000, 2048, 64, kind="normal", table="perm")
+    s, sl, pt = upload(w)
+    out = torch.empty((w.batch, w.k), dtype=torch.int32, device=s.device)
+    lib.topk_set_split_stream(0, 4)
+    try:
+        g = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)   # workspace allocated outside capture
+            stream.synchronize()
+            note(f"split stream graph: {lib.topk_last_launch()}")
+            check(w, out.cpu().numpy(), None)
+            with torch.cuda.graph(g, stream=stream):
+                lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)
+        for rep in range(4):
+            out.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            check(w, out.cpu().numpy(), None)
+            o2, r2 = lib.topk_transform(s, sl, pt, w.k, w.page_size, want_raw=True)
+            torch.cuda.synchronize()
+            check(w, o2.cpu().numpy(), r2.cpu().numpy())
+    finally:
+        lib.topk_set_split_stream(-1, 0)
+
+
+def test_split_stream_rejects_beyond_residency(lib):
+    """A forced G whose grid would not be resident at once is refused (the
+    finisher scheme needs no co-residency, but the grid is sized to it)."""
+    import torch
+    w = workloads.custom(540, 200, 8192, 64, 64, kind="normal")
+    s, sl, pt = upload(w)
+    lib.topk_set_split_stream(1, 64)
+    try:
+        with pytest.raises(topk.TopkError) as e:
+            lib.topk_transform(s, sl, pt, w.k, w.page_size)
+        assert e.value.status == 2
+    finally:
+        lib.topk_set_split_stream(-1, 0)
+    torch.cuda.synchronize()

@@ -37,7 +37,7 @@ def check_exact(w, out, raw, rows=None):
         assert bad.size == 0, f"{w.name}: raw differs from the oracle in {bad.size} rows (first {bad[:5].tolist()})"
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c3_b4", "c4b", "c5", "mixed"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c3_b4", "c3_b8", "c4b", "c5", "mixed"])
 def test_sorted_configs(lib, name):
     note(f"sorted config {name}")
     w = workloads.make(name)
@@ -61,9 +61,11 @@ def test_sorted_c4a_sampled(lib):
     check_exact(w, out, raw, rows=rows)
 
 
-# every selection path: each streaming shape, split rows, register-resident rows
+# every selection path: each streaming shape, split rows, register-resident rows,
+# split streaming rows (there wgs is G and shape the split streaming shape)
 SORTED_SHAPES = [("stream", 0, 1, 0), ("stream", 0, 1, 1), ("stream", 0, 1, 2), ("split", 4, 3, -1),
-                 ("split", 16, 0, -1), ("resident", 16, 1, -1), ("resident", 64, 1, -1)]
+                 ("split", 16, 0, -1), ("resident", 16, 1, -1), ("resident", 64, 1, -1), ("sstream", 0, 3, 0),
+                 ("sstream", 0, 2, 1)]
 
 
 @pytest.mark.parametrize("path,ept,wgs,shape", SORTED_SHAPES)
@@ -73,18 +75,22 @@ def test_sorted_every_path(lib, path, ept, wgs, shape, kind):
     overflow and low-count fallbacks, and the finish through its memory tie
     select (constant rows have more tied members than its LDS list); "zeros"
     orders -0 before +0, "wide" mixes subnormals and infinities."""
-    W = 3 * 4096 + 123 if path != "stream" else 50001
+    W = {"stream": 50001, "sstream": 90001}.get(path, 3 * 4096 + 123)
     seq = [W, W - 1, W // 3, 2049, 5000, 0, 513, -2]
     for k in (1, 700, 2048):
         w = workloads.custom(300 + ept + wgs + k, len(seq), W, k, 16, seq_lens=seq, kind=kind, table="perm")
         note(f"sorted path={path} ept={ept} wgs={wgs} shape={shape} kind={kind} k={k}")
-        lib.topk_set_dispatch_override(ept, wgs)
-        lib.topk_set_stream_shape(shape)
+        if path == "sstream":
+            lib.topk_set_split_stream(shape, wgs)
+        else:
+            lib.topk_set_dispatch_override(ept, wgs)
+            lib.topk_set_stream_shape(shape)
         try:
             out, raw = run_sorted(lib, w, raw=True)
         finally:
             lib.topk_set_dispatch_override(0, 0)
             lib.topk_set_stream_shape(-1)
+            lib.topk_set_split_stream(-1, 0)
         check_exact(w, out, raw)
 
 
