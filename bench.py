@@ -14,8 +14,14 @@ different copy of the inputs, with more than 1 GiB of distinct inputs in the
 rotation, so the 256 MiB Infinity Cache cannot serve them (the pages' own
 benchmark rotates every read tensor for the same reason).
 
-The CPU baseline is the oracle (numpy, one core) on a bounded sample of rows of
-the same workload.
+The CPU baseline is the oracle as it stands (numpy, one row at a time), over
+the host's cores: a pool of forked processes takes the headline workload's rows,
+timed before the GPU is touched.  The core count and the CPU model are reported.
+
+The latency workloads (batch 1 x 16K, the ragged decode batch, 1M-token rows at
+batch 1, 4 and 8, the mixed batch) are also timed as replays of a captured HIP
+graph of back-to-back calls over rotated inputs, which takes the Python
+binding's per-call cost out of the figure.
 
 "other_workloads" times every other workload the same way (cold inputs
 rotated over more than 1 GiB): batch 1 x 16K; the ragged decode batch of 64;
@@ -48,6 +54,7 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (the scoring kernels' contraction type)
 ROTATE_BYTES = 1.25 * (1 << 30)
 METRIC = "top-k+transform µs/call at b=1,L=1M,k=2048; effective HBM GB/s at b=2048,L=64K"
+GRAPH_TIMED = ("c1", "c2", "c3_b4", "c3_b8", "mixed")   # latency workloads also timed as graph replays
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "stream_rows_kernel__c4a_b2048_L64K_k512__hbm_counters.txt")
@@ -115,36 +122,109 @@ def time_calls(topk, w, sets, steps: int, warmup: int, raw: bool = False, sorted
     return start.elapsed_time(end) / steps, wall * 1e3 / steps
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle as it stands, timed on a bounded sample of the workload's rows."""
-    import numpy as np
+_CPU_W = None   # the workload the forked oracle workers read (inherited at fork)
+
+
+def _oracle_rows(rows):
     from oracle import topk_transform as oracle_topk
-    t = time.perf_counter()
-    oracle_topk(w.scores, w.seq_lens, w.page_table, w.k, w.page_size, rows=range(4))
-    per_row = (time.perf_counter() - t) / 4
-    rows = int(max(8, min(w.batch, budget_s / max(per_row, 1e-6))))
-    t = time.perf_counter()
-    oracle_topk(w.scores, w.seq_lens, w.page_table, w.k, w.page_size, rows=range(rows))
-    el = time.perf_counter() - t
-    L = np.clip(w.seq_lens[:rows].astype(np.int64), 0, w.width)
-    nbytes = int(4 * L.sum() + 4 * rows + 4 * rows * w.k)
-    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of {w.batch} rows of {w.name} (numpy sort per row, single thread); "
-                      f"{el:.1f} s, {rows / el:.1f} rows/s, {el / rows * 1e3:.2f} ms/row"}
+    w = _CPU_W
+    out, _, _ = oracle_topk(w.scores, w.seq_lens, w.page_table, w.k, w.page_size, rows=rows)
+    return int(out.shape[0])
 
 
-def counters_run(topk) -> int:
-    """Dispatches to profile with hardware counters: 4 calls of the headline
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, min_cpu_s: float = 12.0, max_passes: int = 4):
+    """The oracle as it stands, over the host's cores (a pool of forked
+    processes, rows handed out in chunks), on the whole workload, repeated
+    until about `min_cpu_s` of CPU work is done.  Must run before the GPU is
+    initialised: the workers are forks of this process."""
+    import multiprocessing as mp
+    import numpy as np
+    global _CPU_W
+    _CPU_W = w
+    nproc = len(os.sched_getaffinity(0))
+    cores = max(1, min(nproc, 16))   # a GPU box's CPU share is 16 cores
+    chunks = [list(range(i, min(i + 16, w.batch))) for i in range(0, w.batch, 16)]
+    ctx = mp.get_context("fork")
+    passes, el = 0, 0.0
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_rows, chunks[:cores])   # workers up, modules imported
+        while passes < max_passes and (passes == 0 or el * cores < min_cpu_s):
+            t = time.perf_counter()
+            done = sum(pool.map(_oracle_rows, chunks, chunksize=1))
+            el += time.perf_counter() - t
+            passes += 1
+    assert done == w.batch
+    L = np.clip(w.seq_lens.astype(np.int64), 0, w.width)
+    nbytes = passes * int(4 * L.sum() + 4 * w.batch + 4 * w.batch * w.k)
+    rows_s = passes * w.batch / el
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "nproc": nproc, "cpu_model": cpu_model(),
+            "sample": f"all {w.batch} rows of {w.name}, {passes} pass(es), a pool of {cores} forked processes over "
+                      f"chunks of 16 rows (numpy sort per row); {el:.1f} s wall, {rows_s:.1f} rows/s, "
+                      f"{el / passes * 1e3:.1f} ms per call"}
+
+
+def time_graph(topk, w, sets, raw: bool, max_calls: int = 512, replays: int = 20):
+    """us per call from replays of a captured graph of back-to-back calls
+    (the calls rotate over the input sets).  HIP events on the capture stream;
+    10 warm-up replays, then the median of `replays` replays."""
+    import numpy as np
+    import torch
+    dev = sets[0][0].device
+    n = min(len(sets), max_calls)
+    calls = max(n, 20)
+    stream = torch.cuda.Stream(dev)
+    out = torch.empty((w.batch, w.k), dtype=torch.int32, device=dev)
+    out_raw = torch.empty((w.batch, w.k), dtype=torch.int32, device=dev) if raw else None
+    with torch.cuda.stream(stream):
+        s, sl, pt = sets[0]
+        topk.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=out_raw)   # this stream's workspace
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(calls):
+                s, sl, pt = sets[i % n]
+                topk.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=out_raw)
+        for _ in range(10):
+            g.replay()
+        stream.synchronize()
+        times = []
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) / calls)
+    del g
+    in_mb = sum(x.nbytes for x in (w.scores, w.seq_lens, w.page_table)) * n / 2**20
+    return float(np.median(times)), f"graph of {calls} calls over {n} input sets ({in_mb:.0f} MiB)"
+
+
+def counters_run(topk, name: str = "c4a") -> int:
+    """Dispatches to profile with hardware counters: 4 calls of the named
     workload (cold inputs), then 2 copies of 256 MiB between fresh buffers."""
     import torch
     import workloads
-    w = workloads.c4a()
+    w = workloads.make(name)
     in_bytes = w.scores.nbytes + w.seq_lens.nbytes + w.page_table.nbytes
     sets = device_inputs(w, max(2, math.ceil(ROTATE_BYTES / in_bytes)))
     out = torch.empty((w.batch, w.k), dtype=torch.int32, device=sets[0][0].device)
+    out_raw = torch.empty((w.batch, w.k), dtype=torch.int32, device=sets[0][0].device) if w.want_raw else None
     for i in range(4):
         s, sl, pt = sets[i % len(sets)]
-        topk.topk_transform(s, sl, pt, w.k, w.page_size, out=out)
+        topk.topk_transform(s, sl, pt, w.k, w.page_size, out=out, out_raw=out_raw)
     torch.cuda.synchronize()
     del sets
     torch.cuda.empty_cache()
@@ -154,8 +234,8 @@ def counters_run(topk) -> int:
     for _ in range(2):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"counters_run": True, "kernel_calls": 4, "copy_bytes": n * 4,
-                      "algorithmic_bytes_per_call": algorithmic_bytes(w, raw=False),
+    print(json.dumps({"counters_run": True, "workload": w.name, "kernel_calls": 4, "copy_bytes": n * 4,
+                      "algorithmic_bytes_per_call": algorithmic_bytes(w, raw=w.want_raw),
                       "launch": topk.topk_last_launch()}), flush=True)
     return 0
 
@@ -247,9 +327,9 @@ def main() -> int:
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (c1, c2, c3 b=4/8, c4b, c5, mixed, sorted mode)")
     ap.add_argument("--no-indexer", action="store_true", help="skip the fused indexer scoring + top-k leg")
-    ap.add_argument("--counters", action="store_true",
-                    help="only run the headline kernel 4 times on rotated inputs, then 2 plain device copies of "
-                         "256 MiB (the calibration for HBM byte counters); for rocprofv3 --pmc passes")
+    ap.add_argument("--counters", nargs="?", const="c4a", default=None, metavar="WORKLOAD",
+                    help="only run a workload (default c4a) 4 times on rotated inputs, then 2 plain device copies "
+                         "of 256 MiB (the calibration for HBM byte counters); for rocprofv3 --pmc passes")
     ap.add_argument("--indexer-counters", action="store_true",
                     help="only run the indexer scoring kernels twice each on a 1024 x 65536 prefill; "
                          "for rocprofv3 --pmc passes")
@@ -260,20 +340,28 @@ def main() -> int:
         return 2
 
     import numpy as np
+    import workloads
+
+    # ---- the CPU baseline first: its workers are forks of this process, which
+    # has not touched the GPU yet
+    w = workloads.c4a()
+    cpu = None
+    if not (args.no_cpu or args.counters or args.indexer_counters):
+        cpu = cpu_baseline(w)
+        print(f"cpu_baseline {cpu}", file=sys.stderr, flush=True)
+
     import torch
 
     import sparse_attention_indexer_fp32_amd as topk
-    import workloads
 
     topk.load()
     props = torch.cuda.get_device_properties(0)
     if args.counters:
-        return counters_run(topk)
+        return counters_run(topk, args.counters)
     if args.indexer_counters:
         return indexer_counters_run(topk)
 
     # ---- headline: bandwidth workload (batch 2048 x 65536, k 512) -----------------
-    w = workloads.c4a()
     nbytes = algorithmic_bytes(w, raw=False)
     in_bytes = w.scores.nbytes + w.seq_lens.nbytes + w.page_table.nbytes
     copies = max(2, math.ceil(ROTATE_BYTES / in_bytes))
@@ -293,6 +381,7 @@ def main() -> int:
     ms3, _ = time_calls(topk, w3, sets3, max(args.steps, 100), args.warmup)
     launch3 = topk.topk_last_launch()
     hot3, _ = time_calls(topk, w3, sets3[:1], max(args.steps, 100), 2)
+    graph3, graph3_how = time_graph(topk, w3, sets3, raw=False)
     del sets3
     torch.cuda.empty_cache()
 
@@ -307,6 +396,10 @@ def main() -> int:
             extra[name] = {"us_per_call": round(msx * 1e3, 2), "GBps": round(bx / (msx * 1e-3) / 1e9, 1),
                            "frac_hbm": round(bx / (msx * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                            "rows_per_s": round(wx.batch / (msx * 1e-3), 1), "launch": topk.topk_last_launch()}
+            if name in GRAPH_TIMED:
+                gx, how = time_graph(topk, wx, sx, raw=wx.want_raw)
+                extra[name]["graph_us_per_call"] = round(gx * 1e3, 2)
+                extra[name]["graph"] = how
             print(f"{name:8s} {extra[name]}", file=sys.stderr, flush=True)
             del sx
             torch.cuda.empty_cache()
@@ -324,8 +417,6 @@ def main() -> int:
             torch.cuda.empty_cache()
 
     indexer = None if args.no_indexer else indexer_leg(topk, steps=5, warmup=2)
-
-    cpu = None if args.no_cpu else cpu_baseline(w)
 
     result = {
         "metric": METRIC,
@@ -348,6 +439,8 @@ def main() -> int:
         "hot_cache_GBps": round(nbytes / (hot_ms * 1e-3) / 1e9, 1),
         "wall_ms_per_step": round(wall_ms, 4),
         "latency_b1_L1M_k2048_us": round(ms3 * 1e3, 2),
+        "latency_b1_L1M_graph_us": round(graph3 * 1e3, 2),
+        "latency_b1_L1M_graph": graph3_how,
         "latency_b1_L1M_hot_us": round(hot3 * 1e3, 2),
         "latency_b1_roofline": {"bound": "hbm", "bytes": b3, "roofline_us": round(b3 / HBM_PEAK_GBPS / 1e3, 3),
                                 "frac": round(b3 / HBM_PEAK_GBPS / 1e3 / (ms3 * 1e3), 4), "launch": launch3},
