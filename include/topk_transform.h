@@ -236,9 +236,13 @@ topk_status_t topk_set_stream_shape(int32_t shape);
  *                     sample, two 8K-position chunks in flight;
  *                  1: 1024-thread workgroups, one per CU, a 16K-position
  *                     sample, three 16K-position chunks in flight;
- *   wgs_per_row  G, 1 <= G <= 1024, when shape >= 0.
- * A forced call whose batch * G workgroups do not fit resident at once
- * returns TOPK_ERROR_UNSUPPORTED.  Every shape and G are exact for every
+ *   wgs_per_row  G, 0 <= G <= 1024, when shape >= 0.  G = 0 selects the
+ *                length-aware form: each row gets between 1 and 4
+ *                workgroups, by its length against the batch's total
+ *                positions spread over the CUs, worked out on the device.
+ * A forced call whose batch * G workgroups do not fit resident at once (G
+ * given), or with G above 4 or more than 256 rows, returns
+ * TOPK_ERROR_UNSUPPORTED.  Every shape and G are exact for every
  * input; the choice only moves time.  Returns TOPK_ERROR_INVALID_VALUE for
  * other values.
  */

@@ -250,6 +250,7 @@ struct Plan {
   Kind kind = Kind::kStream;
   int stream_variant = kStreamWide;
   int ss_variant = 0;
+  bool ss_spread = false;   // split streaming: per-row parts from the lengths (G is their maximum)
   int ept_idx = 0;
   int64_t G = 1;
   int64_t slots = 1;
@@ -304,19 +305,23 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
     return idx;
   };
 
-  // split streaming: G workgroups per row, all resident at once
-  auto split_stream = [&](int variant, int64_t G) -> topk_status_t {
+  // split streaming: G workgroups per row, all resident at once; or, with
+  // `spread`, up to G per row from the rows' lengths (no residency needed:
+  // no workgroup of this kernel waits for another)
+  auto split_stream = [&](int variant, int64_t G, bool spread = false) -> topk_status_t {
     const int64_t cap = (int64_t)dev.ss_occ[variant] * dev.cus;
-    if (G < 1 || G > topk::kSsMaxParts || B * G > cap || B > (int64_t)topk::kSsMaxRows)
+    if (G < 1 || G > topk::kSsMaxParts || (!spread && B * G > cap) || B > (int64_t)topk::kSsMaxRows)
       return fail(TOPK_ERROR_UNSUPPORTED,
                   "split streaming takes at most 4 workgroups per row and 256 rows, all resident at once");
     plan->kind = Kind::kSplitStream;
     plan->ss_variant = variant;
+    plan->ss_spread = spread;
     plan->G = G;
     plan->slots = B;
     return TOPK_SUCCESS;
   };
-  if (g_ss_variant >= 0) return split_stream(g_ss_variant, g_ss_wgs > 0 ? g_ss_wgs : 2);
+  if (g_ss_variant >= 0)
+    return g_ss_wgs > 0 ? split_stream(g_ss_variant, g_ss_wgs) : split_stream(g_ss_variant, topk::kSsMaxParts, true);
   // Split streaming rows, where measured to win.  G = CUs / B (2 to 4):
   // about one workgroup per CU, each streaming a segment of the row.  Only
   // where a row's merged candidates stay well inside the finisher's list:
@@ -326,11 +331,11 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
   // back to re-reading the row, which costs several times more (1M rows at
   // k 2048: 279 against 76 us).
   const int64_t ss_G = std::min<int64_t>(topk::kSsMaxParts, std::max<int64_t>(2, dev.cus / std::max<int64_t>(B, 1)));
-  auto split_stream_fits = [&]() {
+  auto split_stream_fits = [&](double bound = 4500.0) {
     const double S = 8192.0, L = (double)Wc, n = (double)std::min<int64_t>(k, Wc);
     const double mu = n * std::min(S, L) / L;
     const double passed = (mu + 7.0 * std::sqrt(mu) + 6.0) * L / S;
-    return g_stream_variant < 0 && B <= (int64_t)topk::kSsMaxRows && passed <= 4500.0 &&
+    return g_stream_variant < 0 && B <= (int64_t)topk::kSsMaxRows && passed <= bound &&
            (int64_t)dev.ss_occ[0] * dev.cus >= ss_G * B;
   };
   if (g_override_ept || g_override_wgs) {
@@ -361,6 +366,14 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
     // against 21.1 us and 32 x 256K 22.3 us).  Fewer rows stay split: 16 x
     // 256K 22.8 us split against 26.0 us.
     return split_stream(0, ss_G);
+  } else if (B >= 32 && Wc > 262144 && split_stream_fits(6000.0)) {
+    // Mid batches of wider rows: the width says little about the lengths, so
+    // each row gets 1 to 4 workgroups by its own length, worked out on the
+    // device (measured on MI355X against split rows: 64 x 512K, k 512: 35.2
+    // against 67.6 us; 32 x 1M, k 512: 51.2 against 66.7 us; 64 x 512K, k
+    // 2048: 40.6 against 78.8 us; 48 rows of U[64K, 1M], k 1024: 53.2 against
+    // 94.6 us; 64 rows of U[32K, 512K], k 1024: 35.4 against 70.8 us).
+    return split_stream(0, topk::kSsMaxParts, true);
   } else if (Wc <= (int64_t)topk::kThreads * 16) {
     // few short rows: one workgroup each, the row in registers (1 x 16K, k 512:
     // 10.2 us against 12.6 us streamed)
@@ -506,6 +519,7 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   a.sel = nullptr;
   a.spin_limit = g_spin_limit;
   a.fault_host = nullptr;
+  a.spread = plan.kind == Kind::kSplitStream && plan.ss_spread ? info->cus : 0;
   if (sorted) {
     // the selection launch always writes raw positions: the caller's out_raw,
     // else a scratch area after the records
@@ -570,8 +584,8 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     if (e != hipSuccess) return hip_fail(e, "sorted finish launch");
   }
   char buf[200];
-  std::snprintf(buf, sizeof(buf), "%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s",
-                kind_name(plan.kind),
+  std::snprintf(buf, sizeof(buf), "%s%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s",
+                kind_name(plan.kind), plan.ss_spread ? " length-aware" : "",
                 plan.kind == Kind::kStream || plan.kind == Kind::kSplitStream ? 0 : topk::kEptValues[plan.ept_idx],
                 (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G),
                 plan.kind == Kind::kStream ? topk::stream_variant_threads(plan.stream_variant) : topk::kThreads, a.vec,
@@ -690,8 +704,8 @@ topk_status_t topk_set_dispatch_override(int32_t elems_per_thread, int32_t wgs_p
 topk_status_t topk_set_split_stream(int32_t shape, int32_t wgs_per_row) {
   if (shape < -1 || shape >= topk::kNumSplitStreamVariants)
     return fail(TOPK_ERROR_INVALID_VALUE, "shape must be -1 (automatic) or a compiled split streaming shape index");
-  if (shape >= 0 && (wgs_per_row < 1 || wgs_per_row > 1024))
-    return fail(TOPK_ERROR_INVALID_VALUE, "wgs_per_row must be in [1, 1024]");
+  if (shape >= 0 && (wgs_per_row < 0 || wgs_per_row > 1024))
+    return fail(TOPK_ERROR_INVALID_VALUE, "wgs_per_row must be in [0, 1024]");
   std::lock_guard<std::mutex> lock(g_mu);
   g_ss_variant = shape;
   g_ss_wgs = shape >= 0 ? wgs_per_row : 0;

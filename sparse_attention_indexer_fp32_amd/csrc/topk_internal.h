@@ -120,6 +120,8 @@ struct KernelArgs {
   const int32_t* sel;         // sorted finish: (batch, k) raw positions the selection launch wrote
   uint32_t spin_limit;        // split rows: polls of a barrier wait before it gives up
   uint32_t* fault_host;       // split rows: host-visible copy of the workspace's fault count, or nullptr
+  int32_t spread;             // split streaming: 0 = wgs_per_row parts per row; else per-row parts from
+                              // the lengths, at most wgs_per_row, the positions spread over this many shares
 };
 
 // Polls of a split-row barrier wait before it gives up (with s_sleep 1 between
@@ -139,8 +141,9 @@ hipError_t launch_stream_rows(int variant, const KernelArgs& args, hipStream_t s
 hipError_t stream_occupancy(int variant, int* blocks_per_cu);
 int stream_variant_threads(int variant);
 
-// Split streaming kernel: G workgroups per row (wgs_per_row), grid = batch *
-// G, all resident at once.  `variant` selects a compiled shape.
+// Split streaming kernel: G workgroups per row (wgs_per_row), or per-row
+// counts from the lengths (spread > 0); grid = batch * G.  `variant` selects
+// a compiled shape.
 constexpr int kNumSplitStreamVariants = 2;
 hipError_t launch_split_stream(int variant, const KernelArgs& args, hipStream_t stream);
 hipError_t split_stream_occupancy(int variant, int* blocks_per_cu);

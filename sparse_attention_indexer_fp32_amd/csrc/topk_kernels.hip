@@ -1280,15 +1280,56 @@ split_stream_kernel(KernelArgs a) {
   int32_t* const sh_raw = reinterpret_cast<int32_t*>(sh_hist + (kBinsWide - kMaxK));
   __shared__ uint32_t sh_var[16];
 
-  const int G = a.wgs_per_row;
-  const int64_t row = (int64_t)(blockIdx.x / (uint32_t)G);
-  const uint32_t part = blockIdx.x - (uint32_t)row * (uint32_t)G;
-  if (row >= a.batch) return;
-  const int tid = opaque_tid();
   const int64_t W = a.width;
   const int k = a.k;
   const bool vec = a.vec != 0;
-  const int32_t seq = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+  int G = a.wgs_per_row;
+  int64_t row;
+  uint32_t part;
+  int32_t seq;
+  if (a.spread == 0) {   // G parts for every row
+    row = (int64_t)(blockIdx.x / (uint32_t)G);
+    part = blockIdx.x - (uint32_t)row * (uint32_t)G;
+    if (row >= a.batch) return;
+    seq = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+  } else {
+    // Length-aware: every workgroup reads the batch's lengths (at most
+    // kSsMaxRows rows) and gives row r G_r = ceil(L_r / T) parts, between 1
+    // and G, with T the batch's positions over `spread` shares (about one
+    // workgroup per CU); rows of at most k positions get one.  Workgroups are
+    // numbered through the rows in order, parts within a row; those past the
+    // total exit.  The grid is batch * G.
+    const int t = opaque_tid();
+    int32_t sl = t < a.batch ? a.seq_lens[t] : 0;
+    const uint32_t Lt = sl <= 0 ? 0u : ((int64_t)sl > W ? (uint32_t)W : (uint32_t)sl);
+    uint32_t kilo_total;   // the batch's positions, in units of 1024 (fits 32 bits for 256 rows)
+    block_exclusive_scan<NT>(Lt >> 10, sh_scan, kilo_total, t);
+    const uint32_t share = (kilo_total + (uint32_t)a.spread - 1u) / (uint32_t)a.spread * 1024u;   // T
+    uint32_t gt = 0u;
+    if (t < a.batch) {
+      gt = 1u;
+      if (Lt > (uint32_t)k && share > 0u) {
+        const uint32_t want = (Lt + share - 1u) / share;
+        gt = want < 1u ? 1u : (want > (uint32_t)G ? (uint32_t)G : want);
+      }
+    }
+    uint32_t units;
+    const uint32_t first = block_exclusive_scan<NT>(gt, sh_scan, units, t);
+    if (t < a.batch && blockIdx.x >= first && blockIdx.x < first + gt) {
+      sh_var[0] = (uint32_t)t;
+      sh_var[1] = blockIdx.x - first;
+      sh_var[2] = gt;
+      sh_var[3] = (uint32_t)sl;
+    }
+    __syncthreads();
+    if (blockIdx.x >= units) return;
+    row = (int64_t)uniform(sh_var[0]);
+    part = uniform(sh_var[1]);
+    G = (int)uniform(sh_var[2]);
+    seq = (int32_t)uniform(sh_var[3]);
+    __syncthreads();   // sh_var is reused below
+  }
+  const int tid = opaque_tid();
   const int64_t L64 = seq < 0 ? 0 : ((int64_t)seq > W ? W : (int64_t)seq);
   const uint32_t L = (uint32_t)L64;
   const int n = L64 < (int64_t)k ? (int)L64 : k;

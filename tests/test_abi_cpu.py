@@ -85,7 +85,8 @@ def test_split_stream_override_validation(lib):
     for shape in range(topk.SPLIT_STREAM_SHAPES):
         assert lib.topk_set_split_stream(shape, 2) == 0
     assert lib.topk_set_split_stream(topk.SPLIT_STREAM_SHAPES, 2) == 1
-    assert lib.topk_set_split_stream(0, 0) == 1
+    assert lib.topk_set_split_stream(0, 0) == 0     # the length-aware form
+    assert lib.topk_set_split_stream(0, -1) == 1
     assert lib.topk_set_split_stream(-2, 0) == 1
     assert lib.topk_set_split_stream(-1, 0) == 0
 

@@ -388,7 +388,7 @@ def test_stream_rows_within_sample_repeated(lib, shape):
 
 # ---- split streaming rows: G workgroups per row, the last one out finishes it
 
-SS_FORCED = [(0, 1), (0, 2), (0, 4), (1, 2), (1, 3)]
+SS_FORCED = [(0, 1), (0, 2), (0, 4), (1, 2), (1, 3), (0, 0), (1, 0)]   # G 0: the length-aware form
 
 
 @pytest.mark.parametrize("shape,G", SS_FORCED)
@@ -477,3 +477,45 @@ def test_split_stream_rejects_beyond_residency(lib):
     finally:
         lib.topk_set_split_stream(-1, 0)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_split_stream_length_aware_ragged(lib, shape):
+    """The length-aware form on a ragged mid batch whose width is far above
+    most lengths: every row gets 1 to 4 workgroups by its length (worked out
+    on the device), trivial rows one; repeated calls with other lengths."""
+    W = 600000
+    rng = np.random.Generator(np.random.PCG64(550 + shape))
+    for rep in range(3):
+        seq = rng.integers(1000, W + 1, size=100).tolist()
+        seq[::17] = [0, 2048, 100, 2049, W, 1][: len(seq[::17])]
+        w = workloads.custom(560 + rep, len(seq), W, 512 if rep else 2048, 64, seq_lens=seq, kind="normal",
+                             table="perm")
+        note(f"split stream length-aware shape={shape} rep={rep}")
+        lib.topk_set_split_stream(shape, 0)
+        try:
+            out, raw = run(lib, w, raw=rep != 1)
+            assert "length-aware" in lib.topk_last_launch(), lib.topk_last_launch()
+        finally:
+            lib.topk_set_split_stream(-1, 0)
+        check(w, out, raw)
+
+
+@pytest.mark.parametrize("B,W,k,lo,expect", [
+    (40, 300000, 1024, 2000, "split-row-stream length-aware"),   # mid batch, wide rows: per-row parts
+    (48, 100000, 2048, 0, "split-row-stream ept=0 wgs_per_row=4"),   # mid batch, rows up to 256K: G = 4
+    (128, 131072, 512, 1000, "split-row-stream ept=0 wgs_per_row=2"),   # one row per two CUs: G = 2
+])
+def test_split_stream_automatic_choices(lib, B, W, k, lo, expect):
+    """The dispatcher's split streaming choices, exact on ragged rows (some
+    shorter than k, some empty)."""
+    rng = np.random.Generator(np.random.PCG64(B + k))
+    seq = rng.integers(lo, W + 1, size=B).tolist() if lo else [W] * B
+    if lo:
+        for i, v in zip(range(0, B, 9), (0, k, k - 1, 17)):
+            seq[i] = v
+    w = workloads.custom(570 + B, B, W, k, 64, seq_lens=seq, kind="normal", table="perm")
+    note(f"automatic split streaming B={B} W={W} k={k}")
+    out, raw = run(lib, w, raw=True)
+    assert lib.topk_last_launch().startswith(expect), lib.topk_last_launch()
+    check(w, out, raw)
