@@ -96,6 +96,13 @@ __device__ __forceinline__ void g_add(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t g_add_ret(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A row-queue ticket (one lane asks).  The address is made per-lane for the
+// compiler (it is the same word): an atomic on a wave-uniform address is
+// rewritten into one per wave whose result is read back at once, and that
+// read waits for every load the wave has in flight.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* queue) {
+  return g_add_ret(queue + ((uint32_t)opaque_tid() >> 16), 1u);
+}
 __device__ __forceinline__ uint32_t g_load(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -994,7 +1001,7 @@ __device__ __forceinline__ uint32_t gate_rank(uint32_t n, uint32_t S, uint32_t L
 // row is finished and staged in LDS for the output pass, taking the gather's
 // dependent global loads off the row's critical path.
 // ---------------------------------------------------------------------------
-template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool PTL>
+template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool PTL, bool VEC>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 stream_rows_kernel(KernelArgs a) {
   constexpr uint32_t kSampleSpan = (uint32_t)NT * 4u * SV;
@@ -1016,7 +1023,7 @@ stream_rows_kernel(KernelArgs a) {
 
   const int64_t W = a.width;
   const int k = a.k;
-  const bool vec = a.vec != 0;
+  constexpr bool vec = VEC;   // a compile-time load form: see the ring below
   // The host passes a workspace only when there are more rows than workgroups.
   uint32_t* const queue = a.ws != nullptr ? a.ws + kHdrRowTicket : nullptr;
   const uint32_t grid = gridDim.x;
@@ -1030,7 +1037,7 @@ stream_rows_kernel(KernelArgs a) {
     if (L64 <= (int64_t)k) {
       __syncthreads();   // every wave has read the previous row's ticket
       if (tid == 0) {
-        const uint32_t nx = queue != nullptr ? grid + g_add_ret(queue, 1u) : row + grid;
+        const uint32_t nx = queue != nullptr ? grid + take_ticket(queue) : row + grid;
         sh_next_row = nx;
         sh_next_len = nx < (uint32_t)a.batch ? a.seq_lens[nx] : 0;
         record_selection(a, row, 0u, 32, (uint32_t)n, (uint32_t)n, 0u);
@@ -1048,13 +1055,21 @@ stream_rows_kernel(KernelArgs a) {
 
     // 1. sample: full histogram of the first kSampleSpan positions (the
     // first NBUF streamed chunks' loads are issued before the sample is used)
+    //
+    // The ring's loads are issued unconditionally, also for chunks past the
+    // row (their descriptor covers nothing: no memory is read, they return
+    // zeros), and the load form is fixed at compile time.  Then every path
+    // issues the same loads in the same order, and the compiler's per-use
+    // waits can leave the later chunks in flight.  A branch around a load,
+    // or a vec / scalar choice made at run time, gives it a path with fewer
+    // loads outstanding, and its waits then hold each chunk's use until the
+    // chunks requested after it have arrived as well.
     uint32_t sk[4 * SV];   // the sample's raw scores
     load_raw<NT, SV>(sk, rowp, 0u, L, vec, tid);
     const uint32_t nch = L > kSampleSpan ? (L - kSampleSpan + kChunkSpan - 1) / kChunkSpan : 0u;
     uint32_t ring[NBUF][4 * CV];
 #pragma unroll
-    for (int b = 0; b < NBUF; ++b)
-      if ((uint32_t)b < nch) load_raw<NT, CV>(ring[b], rowp, kSampleSpan + (uint32_t)b * kChunkSpan, L, vec, tid);
+    for (int b = 0; b < NBUF; ++b) load_raw<NT, CV>(ring[b], rowp, kSampleSpan + (uint32_t)b * kChunkSpan, L, vec, tid);
 #pragma unroll
     for (int j = 0; j < 4 * SV; ++j) {
       const uint32_t x = slot_key<NT>(sk[j], j, 0u, L, tid);
@@ -1098,9 +1113,9 @@ stream_rows_kernel(KernelArgs a) {
     // is first needed when the stream ends)
     uint32_t next = row + grid;
     const uint32_t last_cycle = nch > 0u ? ((nch - 1u) / NBUF) * NBUF : 0u;
-    if (queue != nullptr && tid == 0 && nch == 0u) next = grid + g_add_ret(queue, 1u);
+    if (queue != nullptr && tid == 0 && nch == 0u) next = grid + take_ticket(queue);
     for (uint32_t i = 0; i < nch; i += NBUF) {
-      if (queue != nullptr && tid == 0 && i == last_cycle) next = grid + g_add_ret(queue, 1u);
+      if (queue != nullptr && tid == 0 && i == last_cycle) next = grid + take_ticket(queue);
 #pragma unroll
       for (int b = 0; b < NBUF; ++b) {
         const uint32_t idx = i + (uint32_t)b;
@@ -1112,9 +1127,8 @@ stream_rows_kernel(KernelArgs a) {
             gated_append<NT, CAP, 4 * CV, kGatePositive>(ring[b], cbase, L, gate, sh_ckey, sh_cpos, sh_var, tid);
           else
             gated_append<NT, CAP, 4 * CV, kGateAny>(ring[b], cbase, L, gate, sh_ckey, sh_cpos, sh_var, tid);
-          if (idx + NBUF < nch)
-            load_raw<NT, CV>(ring[b], rowp, kSampleSpan + (idx + NBUF) * kChunkSpan, L, vec, tid);
         }
+        load_raw<NT, CV>(ring[b], rowp, kSampleSpan + (idx + NBUF) * kChunkSpan, L, vec, tid);
       }
       __syncthreads();
       if (uniform(sh_var[kVarCandCount]) > kRefresh)
@@ -1262,7 +1276,7 @@ __device__ __forceinline__ uint64_t g_add64_ret(uint64_t* p, uint64_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool REFINE>
+template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool REFINE, bool VEC>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 split_stream_kernel(KernelArgs a) {
   constexpr uint32_t kSampleSpan = (uint32_t)NT * 4u * SV;
@@ -1282,7 +1296,7 @@ split_stream_kernel(KernelArgs a) {
 
   const int64_t W = a.width;
   const int k = a.k;
-  const bool vec = a.vec != 0;
+  constexpr bool vec = VEC;
   int G = a.wgs_per_row;
   int64_t row;
   uint32_t part;
@@ -1368,11 +1382,13 @@ split_stream_kernel(KernelArgs a) {
     __syncthreads();
     // The first chunks are requested only now: every workgroup of the launch
     // starts at once, and samples requested alone arrive sooner; these loads
-    // then stream in while the gate is worked out.
+    // then stream in while the gate is worked out.  As in the streaming
+    // kernel, every ring load is issued (past the segment they read nothing),
+    // so that each chunk's use waits for that chunk only.
     uint32_t ring[NBUF][4 * CV];
 #pragma unroll
     for (int b = 0; b < NBUF; ++b)
-      if ((uint32_t)b < nch) load_raw<NT, CV>(ring[b], rowp, s0 + kSampleSpan + (uint32_t)b * kChunkSpan, s1, vec, tid);
+      load_raw<NT, CV>(ring[b], rowp, s0 + kSampleSpan + (uint32_t)b * kChunkSpan, s1, vec, tid);
     // ranked for the row: the sample holds on average n * S / L of the row's n largest
     const uint32_t m = gate_rank((uint32_t)n, seg < kSampleSpan ? seg : kSampleSpan, L);
     find_threshold<NT, kBinsWide>(sh_hist, m, sh_scan, sh_var, tid);
@@ -1416,9 +1432,8 @@ split_stream_kernel(KernelArgs a) {
             gated_append<NT, CAP, 4 * CV, kGatePositive>(ring[b], cbase, s1, gate, sh_ckey, sh_cpos, sh_var, tid);
           else
             gated_append<NT, CAP, 4 * CV, kGateAny>(ring[b], cbase, s1, gate, sh_ckey, sh_cpos, sh_var, tid);
-          if (idx + NBUF < nch)
-            load_raw<NT, CV>(ring[b], rowp, s0 + kSampleSpan + (idx + NBUF) * kChunkSpan, s1, vec, tid);
         }
+        load_raw<NT, CV>(ring[b], rowp, s0 + kSampleSpan + (idx + NBUF) * kChunkSpan, s1, vec, tid);
       }
       __syncthreads();
       if (uniform(sh_var[kVarCandCount]) > kRefresh)
@@ -1791,6 +1806,16 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
   }
 }
 
+// Resident workgroups per CU of a kernel's two load forms (the launch picks
+// one by the rows' alignment; the host sizes grids for either).
+hipError_t occupancy_pair(const void* f_vec, const void* f_scalar, int nt, int* blocks) {
+  int b_vec = 0, b_scalar = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b_vec, f_vec, nt, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b_scalar, f_scalar, nt, 0);
+  *blocks = b_vec < b_scalar ? b_vec : b_scalar;
+  return e;
+}
+
 // Streaming-kernel shapes: (threads, sample float4 groups per thread, chunk
 // float4 groups per thread, chunks in flight, LDS candidates, waves per SIMD,
 // page-table row staged in LDS).
@@ -1803,8 +1828,12 @@ hipError_t launch_stream_variant(int variant, const KernelArgs& args, hipStream_
   switch (variant) {
 #define TOPK_LAUNCH_CASE(id, nt, sv, cv, nbuf, cap, waves, ptl)                                                      \
   case id:                                                                                              \
-    hipLaunchKernelGGL((stream_rows_kernel<nt, sv, cv, nbuf, cap, waves, ptl>), dim3((unsigned)args.slots), dim3(nt), 0, \
-                       stream, args);                                                                   \
+    if (args.vec)                                                                                       \
+      hipLaunchKernelGGL((stream_rows_kernel<nt, sv, cv, nbuf, cap, waves, ptl, true>), dim3((unsigned)args.slots), \
+                         dim3(nt), 0, stream, args);                                                    \
+    else                                                                                                \
+      hipLaunchKernelGGL((stream_rows_kernel<nt, sv, cv, nbuf, cap, waves, ptl, false>), dim3((unsigned)args.slots), \
+                         dim3(nt), 0, stream, args);                                                    \
     return hipGetLastError();
     TOPK_STREAM_VARIANTS(TOPK_LAUNCH_CASE)
 #undef TOPK_LAUNCH_CASE
@@ -1816,8 +1845,9 @@ hipError_t occupancy_stream_variant(int variant, int* blocks) {
   switch (variant) {
 #define TOPK_OCC_CASE(id, nt, sv, cv, nbuf, cap, waves, ptl)                                                         \
   case id:                                                                                              \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                                \
-        blocks, reinterpret_cast<const void*>(&stream_rows_kernel<nt, sv, cv, nbuf, cap, waves, ptl>), nt, 0);
+    return occupancy_pair(reinterpret_cast<const void*>(&stream_rows_kernel<nt, sv, cv, nbuf, cap, waves, ptl, true>), \
+                          reinterpret_cast<const void*>(&stream_rows_kernel<nt, sv, cv, nbuf, cap, waves, ptl, false>), \
+                          nt, blocks);
     TOPK_STREAM_VARIANTS(TOPK_OCC_CASE)
 #undef TOPK_OCC_CASE
     default: return hipErrorInvalidValue;
@@ -1834,8 +1864,12 @@ hipError_t launch_split_stream_variant(int variant, const KernelArgs& args, hipS
   switch (variant) {
 #define TOPK_SS_LAUNCH_CASE(id, nt, sv, cv, nbuf, cap, waves, refine)                                            \
   case id:                                                                                                  \
-    hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine>),                         \
-                       dim3((unsigned)args.batch * (unsigned)args.wgs_per_row), dim3(nt), 0, stream, args); \
+    if (args.vec)                                                                                           \
+      hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, true>),                 \
+                         dim3((unsigned)args.batch * (unsigned)args.wgs_per_row), dim3(nt), 0, stream, args); \
+    else                                                                                                    \
+      hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, false>),                \
+                         dim3((unsigned)args.batch * (unsigned)args.wgs_per_row), dim3(nt), 0, stream, args); \
     return hipGetLastError();
     TOPK_SPLIT_STREAM_VARIANTS(TOPK_SS_LAUNCH_CASE)
 #undef TOPK_SS_LAUNCH_CASE
@@ -1847,8 +1881,9 @@ hipError_t occupancy_split_stream_variant(int variant, int* blocks) {
   switch (variant) {
 #define TOPK_SS_OCC_CASE(id, nt, sv, cv, nbuf, cap, waves, refine)                                               \
   case id:                                                                                              \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                                \
-        blocks, reinterpret_cast<const void*>(&split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine>), nt, 0);
+    return occupancy_pair(reinterpret_cast<const void*>(&split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, true>), \
+                          reinterpret_cast<const void*>(&split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, false>), \
+                          nt, blocks);
     TOPK_SPLIT_STREAM_VARIANTS(TOPK_SS_OCC_CASE)
 #undef TOPK_SS_OCC_CASE
     default: return hipErrorInvalidValue;
