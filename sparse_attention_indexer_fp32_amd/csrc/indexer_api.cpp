@@ -204,7 +204,11 @@ topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t
   int64_t cap = 4 * (int64_t)k > 4096 ? 4 * (int64_t)k : 4096;
   if (cap > a.window) cap = a.window;
   a.cap = (int32_t)cap;
-  row_cap = (int64_t)a.nwin * k;
+  // With one window per row the select reads the lists in place (no final
+  // trim, no packed copy): every list entry is a candidate, and the list holds
+  // a top-k of its row.
+  a.inplace = a.nwin == 1 ? 1 : 0;
+  row_cap = a.inplace ? 0 : (int64_t)a.nwin * k;
   a.row_cap = row_cap;
   const size_t lists = (size_t)num_q * a.nwin * (size_t)cap;
   const size_t packed = (size_t)num_q * (size_t)row_cap;
@@ -224,15 +228,20 @@ topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t
   a.row_count = reinterpret_cast<int32_t*>(p);
   hipError_t e = indexer::launch_scan(a, a.nwin, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer scan launch");
-  // exact select over the packed candidates; the positions act as a page
-  // table of page size 1, so out_idx receives them directly
-  st = topk::transform_locked(a.row_score, a.row_count, a.row_pos, k, 1, out_idx, nullptr, stream, num_q, row_cap,
-                              row_cap);
+  // exact select over the candidates (the lists in place, or their packed
+  // copies); the positions act as a page table of page size 1, so out_idx
+  // receives them directly
+  if (a.inplace)
+    st = topk::transform_locked(a.cand_score, a.row_count, a.cand_pos, k, 1, out_idx, nullptr, stream, num_q, cap,
+                                cap);
+  else
+    st = topk::transform_locked(a.row_score, a.row_count, a.row_pos, k, 1, out_idx, nullptr, stream, num_q, row_cap,
+                                row_cap);
   if (st != TOPK_SUCCESS) return st;
   char buf[200];
-  std::snprintf(buf, sizeof(buf), "indexer-topk grid=%lldx%d window=%lld cap=%d + select %s",
+  std::snprintf(buf, sizeof(buf), "indexer-topk grid=%lldx%d window=%lld cap=%d%s + select %s",
                 (long long)ceil_div(num_q, indexer::rows_per_workgroup()), a.nwin, (long long)a.window, a.cap,
-                topk_last_launch());
+                a.inplace ? " in-place" : "", topk_last_launch());
   topk::set_last_launch(buf);
   return TOPK_SUCCESS;
 }

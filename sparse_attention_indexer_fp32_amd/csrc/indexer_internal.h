@@ -31,6 +31,10 @@ struct ScanArgs {
   int32_t* row_pos;
   int32_t* row_count;        // (num_q,)
   int64_t row_cap;
+  // One window per row: the select reads each row's list in place (row_count
+  // = the list's length, no final trim, no packed copy; row_score / row_pos
+  // unused).
+  int32_t inplace;
 };
 
 hipError_t launch_logits(const ScanArgs& a, int nwin, hipStream_t stream);

@@ -390,6 +390,26 @@ constexpr int kStageBytesBf16 = kStage * kDim * 2;   // 16 KB
 // room for two stages' worth beyond the stage being computed.
 constexpr int kAppendCap = 3 * kStage;
 
+// Calibrated start (fused scan).  Before its scan, a workgroup scores
+// kCalStages stages spread evenly over its span (every position appended),
+// and each row starts its scan behind the gate at rank m of that sample: the
+// sample holds on average mu = n S / L of the row's n best positions (S of its
+// L positions sampled), and m = mu + 7 sqrt(mu) + 6.  The scan then starts
+// from an empty list.  Every list entry is at or above the starting gate, so a
+// row that ends with at least n entries has a top-n in its list (a position
+// skipped below the starting gate is below all of them; one skipped after a
+// trim is covered by the trim's k entries); a row that ends with fewer is
+// scanned again from gate 0.  This is the page's prefix calibration of the
+// initial threshold, taken from samples of the whole window so that it does
+// not depend on where in the row the best positions lie, and made safe by the
+// end-of-scan count rather than by the sample's statistics.
+constexpr int kCalStages = 32;
+
+__device__ __forceinline__ int calibration_rank(int64_t n, int64_t sampled, int64_t avail) {
+  const float mu = (float)n * (float)sampled / (float)avail;
+  return (int)ceilf(mu + 7.0f * sqrtf(mu) + 6.0f);
+}
+
 // One thread's share of a stage in flight: 32 fp8 bytes of position t / 4
 // (dims (t % 4) * 32 ..) and that position's scale (staged by t % 4 == 0).
 struct Ring {
@@ -409,6 +429,7 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
   // gate bins per (wave, row) and their (lo, shift); see kGateBins
   __shared__ uint32_t sh_gbins[kFused ? kWaves : 1][kRowsPerWave][kFused ? kGateBins : 1];
   __shared__ uint32_t sh_gpar[kFused ? kWaves : 1][kRowsPerWave][2];
+  __shared__ uint32_t sh_redo;   // a calibrated row ended short: the span is scanned again
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform, so the row indices, ranges and list pointers derived from it live in scalar registers
@@ -435,6 +456,7 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
       const int64_t wlo = (int64_t)w * a.window, whi = wlo + a.window;
       sh_span[0] = lo > wlo ? lo : wlo;
       sh_span[1] = hi < whi ? hi : whi;
+      if (kFused) sh_redo = 0;
     }
   }
   __syncthreads();
@@ -453,16 +475,19 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
     load_row(a.q, a.weights, rix[i], rix[i] < a.num_q, lane, rows[i]);
   }
 
-  // fused scan state, wave-uniform: gate, list length, appends staged in LDS
+  // fused scan state, wave-uniform: gate, list length, appends staged in LDS,
+  // whether the row's starting gate came from the calibration sample
   uint32_t gate[kRowsPerWave];
   int count[kRowsPerWave];
   int staged[kRowsPerWave];
+  bool calibrated[kRowsPerWave];
   if (kFused) {
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       gate[i] = 0;
       count[i] = 0;
       staged[i] = 0;
+      calibrated[i] = false;
       if (lane == 0) {
         sh_gpar[wave][i][0] = 0;
         sh_gpar[wave][i][1] = 32;   // no bins before a first trim
@@ -582,38 +607,154 @@ __global__ void __launch_bounds__(kThreads, 2) logits_kernel(ScanArgs a) {
         }
       }
     };
+    // A row's positions in this window, and how many it selects.
+    auto row_avail = [&](int i) {
+      const int64_t lo = rr[i].lo > span_lo ? rr[i].lo : span_lo;
+      const int64_t hi = rr[i].hi < span_hi ? rr[i].hi : span_hi;
+      return hi > lo ? hi - lo : (int64_t)0;
+    };
+    auto row_n = [&](int i) {
+      const int64_t av = row_avail(i);
+      return av < (int64_t)a.k ? av : (int64_t)a.k;
+    };
+    // The calibration sample: the middle stage of each of kCalStages equal
+    // runs of the span's stages (stage counts fit 32 bits: positions are
+    // below 2^31), on spans of at least 4 kCalStages stages whose lists hold
+    // the sample without a trim.
+    const int nmain = (int)((span_hi - span_lo + kStage - 1) / kStage);
+    const bool sampled =
+        kFused && nmain >= 4 * kCalStages && a.cap >= kCalStages * kStage + kAppendCap + kStage;
+    const int stride = nmain / kCalStages;
+    auto sample_base = [&](int idx) { return span_lo + (int64_t)(idx * stride + stride / 2) * kStage; };
+    // End of the sample: every sampled position of a row is in its list (the
+    // gate was 0, and the capacity holds the sample without a trim).  The
+    // row's starting gate is the rank-m sampled key; the list is emptied.
+    auto calibrate = [&]() {
+      flush(true, span_hi);
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const int64_t av = row_avail(i);
+        uint32_t g0 = 0;
+        bool cal = false;
+        if (count[i] > 0 && av > 0) {
+          const int m = calibration_rank(row_n(i), count[i], av);
+          if (m < count[i]) {
+            const Trimmed t = compact_list(list_score(i), list_pos(i), count[i], (uint32_t)m, 0, true, sh_hist[wave],
+                                           lane, 0u, nullptr);
+            g0 = t.gate > 0u ? t.gate - 1u : 0u;   // the m-th largest sampled key
+            cal = true;
+          }
+        }
+        gate[i] = g0;
+        count[i] = 0;
+        calibrated[i] = cal;
+        if (lane == 0) {
+          sh_gpar[wave][i][0] = 0;
+          sh_gpar[wave][i][1] = 32;
+        }
+      }
+    };
+    // After a calibrated pass: a calibrated row with fewer than n entries may
+    // have skipped part of its top-n, so every such row is scanned again from
+    // gate 0 and the others keep their lists (their ranges are closed for the
+    // second pass).  Returns whether a second pass is needed.
+    auto verify = [&]() {
+      bool failed[kRowsPerWave];
+      bool any = false;
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        failed[i] = calibrated[i] && (int64_t)count[i] < row_n(i);
+        any |= failed[i];
+      }
+      if (any && lane == 0) atomicOr(&sh_redo, 1u);
+      __syncthreads();
+      const bool redo = __builtin_amdgcn_readfirstlane(sh_redo) != 0u;
+      if (redo) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          if (failed[i]) {
+            gate[i] = 0;
+            count[i] = 0;
+            calibrated[i] = false;
+            if (lane == 0) {
+              sh_gpar[wave][i][0] = 0;
+              sh_gpar[wave][i][1] = 32;
+            }
+          } else {
+            rr[i] = RowRange{0, 0};
+          }
+        }
+      }
+      return redo;
+    };
+    if (kFused && sampled) {
+      // the sample's stages, pipelined like the scan below (the stages
+      // fetched past the sample's end stay in bounds and are never computed)
+      Ring r0, r1;
+      fetch(r0, sample_base(0));
+      stage(r0, 0);
+      fetch(r1, sample_base(1));
+      fetch(r0, sample_base(2));
+      __syncthreads();
+      for (int idx = 0; idx < kCalStages; idx += 2) {
+        compute(sample_base(idx), 0);
+        stage(r1, 1);
+        flush(false, span_lo);
+        fetch(r1, sample_base(idx + 3));
+        __syncthreads();
+        compute(sample_base(idx + 1), 1);
+        stage(r0, 0);
+        flush(false, span_lo);
+        fetch(r0, sample_base(idx + 4));
+        __syncthreads();
+      }
+      calibrate();
+    }
     // Two stages in flight in registers: the stage computed now, the next one
     // already in LDS, and the two after it loading.  The loop has no exit in
     // its middle (the second stage of a pair past the span is skipped, and
     // its loads stay in bounds): the compiler merges the load counts of every
     // path into the loop head, and an early exit path would make the wait
-    // for a stage drain the younger stage as well.
-    Ring r0, r1;
-    fetch(r0, span_lo);
-    stage(r0, 0);
-    fetch(r1, span_lo + kStage);
-    fetch(r0, span_lo + 2 * kStage);
-    __syncthreads();
-    for (int64_t base = span_lo; base < span_hi; base += 2 * kStage) {
-      compute(base, 0);
-      stage(r1, 1);
-      if (kFused) flush(false, base + kStage);
-      fetch(r1, base + 3 * kStage);
-      __syncthreads();
-      if (base + kStage < span_hi) compute(base + kStage, 1);
+    // for a stage drain the younger stage as well.  A second pass runs only
+    // for rows whose calibrated first pass ended short (verify).
+    bool check = kFused && sampled;
+    for (;;) {
+      Ring r0, r1;
+      fetch(r0, span_lo);
       stage(r0, 0);
-      if (kFused) flush(false, base + 2 * kStage);
-      fetch(r0, base + 4 * kStage);
+      fetch(r1, span_lo + kStage);
+      fetch(r0, span_lo + 2 * kStage);
       __syncthreads();
+      for (int64_t base = span_lo; base < span_hi; base += 2 * kStage) {
+        compute(base, 0);
+        stage(r1, 1);
+        if (kFused) flush(false, base + kStage);
+        fetch(r1, base + 3 * kStage);
+        __syncthreads();
+        if (base + kStage < span_hi) compute(base + kStage, 1);
+        stage(r0, 0);
+        if (kFused) flush(false, base + 2 * kStage);
+        fetch(r0, base + 4 * kStage);
+        __syncthreads();
+      }
+      if (!kFused) break;
+      flush(true, span_hi);
+      if (!check || !verify()) break;
+      check = false;
     }
-    if (kFused) flush(true, span_hi);
   }
 
   if (kFused) {
-    // final trim to at most k entries, then hand the list to the row's area
+    // final trim to at most k entries, then hand the list to the row's area;
+    // or, with one window per row, only the list's length (the select reads
+    // the list where it is)
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       if (rix[i] >= a.num_q) continue;
+      if (a.inplace) {
+        if (lane == 0) a.row_count[rix[i]] = count[i];
+        continue;
+      }
       float* lsc = list_score(i);
       int32_t* lps = list_pos(i);
       if (count[i] > a.k)
@@ -660,9 +801,11 @@ hipError_t launch_logits(const ScanArgs& a, int nwin, hipStream_t stream) {
 
 hipError_t launch_scan(const ScanArgs& a, int nwin, hipStream_t stream) {
   const int64_t n = a.num_q;
-  hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.row_count, n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!a.inplace) {   // windows add their counts; in place, every row's count is written
+    hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.row_count, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)((a.num_q + kRowsPerWg - 1) / kRowsPerWg), (unsigned)nwin);
   hipLaunchKernelGGL(logits_kernel<true>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -220,6 +220,38 @@ def test_indexer_topk_narrow_scores(lib, k):
     _check_exact_on_logits(w, o, _logits(lib, w, tensors))
 
 
+@pytest.mark.parametrize("k", [64, 2048])
+def test_indexer_topk_calibration_overrated(lib, k):
+    """The fused scan starts each long row behind a gate set from a sample of
+    its window: the middle stage (64 positions) of each of 32 equal runs of
+    the window's stages.  Here exactly those positions have their scale raised
+    1000-fold, so the sample overrates every row: the starting gate lies above
+    all of the row's other scores, the first pass ends with fewer than k
+    entries, and the row is scanned again from gate 0.  The result must still
+    be exact."""
+    import torch
+    lib.indexer_set_window_override(1 << 20)   # one window: the span is [0, 65536), 1024 stages
+    w = wl.make([(8, 65536)], k, seed=7500 + k)
+    stages = 65536 // 64
+    stride = stages // 32
+    boosted = np.zeros(w.num_kv, bool)
+    for i in range(32):
+        st = i * stride + stride // 2
+        boosted[st * 64:(st + 1) * 64] = True
+    w.kv_scale = np.where(boosted, w.kv_scale * np.float32(1000.0), w.kv_scale).astype(np.float32)
+    note(f"indexer_topk calibration overrated k={k}")
+    tensors = _upload(w)
+    out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    try:
+        lib.indexer_topk(*tensors, w.k, out=out)
+        torch.cuda.synchronize()
+    finally:
+        lib.indexer_set_window_override(0)
+    o = out.cpu().numpy()
+    _check_topk(w, o, range(w.num_q))
+    _check_exact_on_logits(w, o, _logits(lib, w, tensors))
+
+
 def test_indexer_edge_ranges(lib):
     """Empty, inverted, clamped and shorter-than-k ranges; rows not a multiple of 8."""
     import torch
