@@ -66,8 +66,8 @@ constexpr size_t kRegHist0 = 0;
 constexpr size_t kRegHist1 = kRegHist0 + kBinsWide;
 constexpr size_t kRegHist2 = kRegHist1 + kBinsNarrow;
 constexpr size_t kRegCtr = kRegHist2 + kBinsNarrow;   // 64 words of counters
-constexpr size_t kCtrGreater = 0;       // slots taken by strictly-greater elements
-constexpr size_t kCtrEqual = 16;        // tie slots / candidates appended
+constexpr size_t kCtrSlots = 0;         // 64-bit: high word = slots taken by strictly-greater elements,
+                                        // low word = tie slots / candidates appended
 constexpr size_t kCtrExit = 32;         // workgroups done with the row
 constexpr size_t kRegCandKey = kRegCtr + 64;
 constexpr size_t kRegCandPos = kRegCandKey + kCandCap;

@@ -96,6 +96,9 @@ __device__ __forceinline__ void g_add(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t g_add_ret(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t g_add64_ret(uint64_t* p, uint64_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // A row-queue ticket (one lane asks).  The address is made per-lane for the
 // compiler (it is the same word): an atomic on a wave-uniform address is
 // rewritten into one per wave whose result is read back at once, and that
@@ -672,9 +675,14 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     uint32_t off_g = off >> 17, off_e = off & 0x1FFFFu;
     if (split) {
       if (tid == 0) {
+        // both offsets from one atomic (one round trip instead of two): the
+        // strictly-greater count in the high word, the threshold-bin count in
+        // the low word (a row's total is below 2^31, so it never carries)
         const uint32_t tg = tot >> 17, te = tot & 0x1FFFFu;
-        sh_var[4] = tg ? g_add_ret(region + kRegCtr + kCtrGreater, tg) : 0u;
-        sh_var[5] = te ? g_add_ret(region + kRegCtr + kCtrEqual, te) : 0u;
+        const uint64_t old = g_add64_ret(reinterpret_cast<uint64_t*>(region + kRegCtr + kCtrSlots),
+                                         ((uint64_t)tg << 32) | (uint64_t)te);
+        sh_var[4] = (uint32_t)(old >> 32);
+        sh_var[5] = (uint32_t)old;
         sh_var[7] = 0u;   // this workgroup's (slot, position) pairs staged below
       }
       __syncthreads();
@@ -1271,9 +1279,6 @@ stream_rows_kernel(KernelArgs a) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void g_max(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t g_add64_ret(uint64_t* p, uint64_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool REFINE, bool VEC>
