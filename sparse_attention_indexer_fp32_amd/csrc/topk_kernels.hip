@@ -99,6 +99,11 @@ __device__ __forceinline__ uint32_t g_add_ret(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint64_t g_add64_ret(uint64_t* p, uint64_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Wrapping increment: returns the old value and stores old + 1, or 0 once the
+// old value has reached `last` (one atomic; the counter resets itself).
+__device__ __forceinline__ uint32_t g_inc_wrap(uint32_t* p, uint32_t last) {
+  return __builtin_amdgcn_atomic_inc32(p, last, __ATOMIC_RELAXED, "agent");
+}
 // A row-queue ticket (one lane asks).  The address is made per-lane for the
 // compiler (it is the same word): an atomic on a wave-uniform address is
 // rewritten into one per wave whose result is read back at once, and that
@@ -229,11 +234,13 @@ __device__ __forceinline__ void wave_mem_drain() { __builtin_amdgcn_s_waitcnt(0)
 // the device's resident-workgroup capacity, so all G are normally running at
 // once (a kernel that holds CUs on another stream can break that: there is no
 // cooperative launch).  Workgroup g arrives on its group's counter; the last
-// of a group resets that counter and arrives on the top counter; the last
-// group's closer resets the top and publishes the next generation.  Every
-// reset is drained before the arrival (or publication) that follows it, so
-// the counters are zero again before any workgroup can leave, and the barrier
-// resets itself across calls and graph replays.  Each workgroup tracks the
+// of a group arrives on the top counter; the last group's closer publishes
+// the next generation.  Arrivals are wrapping increments, so the last one on
+// a counter also resets it to zero in the same atomic: every counter is zero
+// again before the publication (which follows the top counter's last
+// arrival, which follows each group's), and the barrier resets itself across
+// calls and graph replays with no reset stores to drain.  Each workgroup
+// drains its own writes before it arrives.  Each workgroup tracks the
 // generation it waits for in `gen` (read once per launch: no barrier of the
 // slot can complete before this workgroup has arrived, so the value is stable
 // until then).
@@ -253,18 +260,14 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, int G, int g, uint32_
     const int grp = g / kBarGroup;
     const int ngroups = (G + kBarGroup - 1) / kBarGroup;
     const uint32_t gsize = (uint32_t)(G - grp * kBarGroup < kBarGroup ? G - grp * kBarGroup : kBarGroup);
+    // Wrapping increments: a counter's last arrival sees gsize - 1 (ngroups
+    // - 1) and leaves it at 0 in the same atomic, so every counter is zero
+    // again before the generation that releases the workgroups is published.
     bool closer = false;
-    if (g_add_ret(bar + (size_t)grp * kBarLine, 1u) == gsize - 1u) {
-      g_store(bar + (size_t)grp * kBarLine, 0u);
-      wave_mem_drain();
-      if (g_add_ret(bar + kBarTop, 1u) == (uint32_t)ngroups - 1u) {
-        g_store(bar + kBarTop, 0u);
-        closer = true;
-      }
-    }
+    if (g_inc_wrap(bar + (size_t)grp * kBarLine, gsize - 1u) == gsize - 1u)
+      closer = g_inc_wrap(bar + kBarTop, (uint32_t)ngroups - 1u) == (uint32_t)ngroups - 1u;
     if (closer) {
-      wave_mem_drain();
-      g_store(bar + kBarGen, gen);
+      g_store(bar + kBarGen, gen);   // nothing this workgroup does next depends on its completion
     } else {
       uint32_t spins = 0;
       while ((int32_t)(g_load(bar + kBarGen) - gen) < 0) {
@@ -276,8 +279,8 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, int G, int g, uint32_
         __builtin_amdgcn_s_sleep(1);
         ++spins;
       }
+      wave_mem_drain();
     }
-    wave_mem_drain();
   }
   __syncthreads();
 }
