@@ -151,12 +151,12 @@ topk_status_t topk_transform_sorted(const float* scores, const int32_t* seq_lens
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, layouts, result and errors as topk_transform;
  * it calls no allocating routine.  Its workspace is the library's static
- * device scratch (16 MiB per device, held from the library's first call on
+ * device scratch (24 MiB per device, held from the library's first call on
  * the device until the process ends) instead of a per-(device, stream)
  * buffer.  The first call on a device that needs the scratch queues a zero
  * fill of it on `stream` before its own kernel.
  *
- * Limit: shapes whose split-row plan needs more than 127 row slots of
+ * Limit: shapes whose split-row plan needs more than 152 row slots of
  * workspace return TOPK_ERROR_UNSUPPORTED with a message (no current plan
  * does: split rows are chosen only for fewer than half a row per CU).
  *
@@ -261,7 +261,14 @@ topk_status_t topk_check_faults(hipStream_t stream);
  * still runs to its end, which tests the TOPK_ERROR_DEVICE_FAULT report. */
 topk_status_t topk_set_wait_limit(uint32_t polls);
 
-/* ABI version of this header (bumped on any signature change). */
+/* Test knob: the number of 32-bit words of the static scratch that
+ * topk_transform_noalloc may use (0, the default, = all of it; larger values
+ * are the same as 0).  A plan whose workspace needs more is refused with
+ * TOPK_ERROR_UNSUPPORTED, so a small value exercises that refusal with shapes
+ * that fit the real scratch.  Process-wide; takes effect from the next call. */
+topk_status_t topk_set_scratch_limit(uint64_t words);
+
+/* ABI version of this header (bumped on any signature or export change). */
 int32_t topk_abi_version(void);
 
 #ifdef __cplusplus

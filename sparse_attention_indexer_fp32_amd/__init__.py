@@ -25,7 +25,8 @@ TOPK_ERROR_DEVICE_FAULT = 5
 
 EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_transform_noalloc", "topk_init", "topk_status_string", "topk_last_error", "topk_last_launch",
             "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape", "topk_set_split_stream",
-            "topk_check_faults", "topk_set_wait_limit", "topk_abi_version", "indexer_logits", "indexer_topk",
+            "topk_check_faults", "topk_set_wait_limit", "topk_set_scratch_limit", "topk_abi_version",
+            "indexer_logits", "indexer_topk",
             "indexer_set_window_override")
 INDEXER_HEADS = 32
 INDEXER_HEAD_DIM = 128
@@ -75,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topk_check_faults.restype = ctypes.c_int
     lib.topk_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.topk_set_wait_limit.restype = ctypes.c_int
+    lib.topk_set_scratch_limit.argtypes = [ctypes.c_uint64]
+    lib.topk_set_scratch_limit.restype = ctypes.c_int
     lib.topk_abi_version.argtypes = []
     lib.topk_abi_version.restype = c_i32
     lib.indexer_logits.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64]
@@ -216,6 +219,11 @@ def topk_check_faults(stream=None) -> None:
 def topk_set_wait_limit(polls: int = 0) -> None:
     """Testing override: polls of a split-row barrier wait before it gives up (0 = default)."""
     _check(load().topk_set_wait_limit(int(polls)))
+
+
+def topk_set_scratch_limit(words: int = 0) -> None:
+    """Testing override: 32-bit words of the static scratch topk_transform_noalloc may use (0 = all)."""
+    _check(load().topk_set_scratch_limit(int(words)))
 
 
 def topk_abi_version() -> int:

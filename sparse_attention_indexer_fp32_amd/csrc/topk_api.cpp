@@ -78,6 +78,7 @@ int g_stream_variant = -1;   // -1: the default streaming shape
 int g_ss_variant = -1;       // split streaming override: -1 automatic, else the shape forced
 int g_ss_wgs = 0;            // ... with this many workgroups per row
 uint32_t g_spin_limit = topk::kDefaultSpinLimit;
+size_t g_scratch_limit = 0;  // words of the static scratch the no-allocation entry point may use; 0: all
 
 topk_status_t fail(topk_status_t st, const std::string& msg) {
   t_last_error = msg;
@@ -538,12 +539,14 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
                          : plan.kind == Kind::kSplitStream ? topk::split_stream_words(batch)
                                                            : topk::kHdrWords;
     if (noalloc) {
-      if (words > topk::kScratchWords) {
+      const size_t limit =
+          g_scratch_limit != 0 && g_scratch_limit < topk::kScratchWords ? g_scratch_limit : topk::kScratchWords;
+      if (words > limit) {
         char msg[200];
         std::snprintf(msg, sizeof(msg),
                       "this shape needs %zu words of workspace; the static scratch of the no-allocation entry "
-                      "point holds %zu (16 MiB)",
-                      words, topk::kScratchWords);
+                      "point holds %zu (%zu MiB)",
+                      words, limit, (topk::kScratchWords * 4) >> 20);
         return fail(TOPK_ERROR_UNSUPPORTED, msg);
       }
       if (!info->scratch_zeroed) {
@@ -753,6 +756,12 @@ topk_status_t topk_set_wait_limit(uint32_t polls) {
   return TOPK_SUCCESS;
 }
 
-int32_t topk_abi_version(void) { return 2; }
+topk_status_t topk_set_scratch_limit(uint64_t words) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_scratch_limit = (size_t)words;
+  return TOPK_SUCCESS;
+}
+
+int32_t topk_abi_version(void) { return 3; }
 
 }  // extern "C"

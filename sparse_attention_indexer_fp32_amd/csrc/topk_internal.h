@@ -71,7 +71,8 @@ constexpr size_t kCtrSlots = 0;         // 64-bit: high word = slots taken by st
 constexpr size_t kCtrExit = 32;         // workgroups done with the row
 constexpr size_t kRegCandKey = kRegCtr + 64;
 constexpr size_t kRegCandPos = kRegCandKey + kCandCap;
-constexpr size_t kRegionWords = kRegCandPos + kCandCap;
+constexpr size_t kRegCandOut = kRegCandPos + kCandCap;   // each candidate's output value (page-table transform)
+constexpr size_t kRegionWords = kRegCandOut + kCandCap;
 
 inline size_t workspace_words(int64_t slots) {
   return kHdrWords + (size_t)slots * kBarWords + (size_t)slots * 2 * kRegionWords;
@@ -155,9 +156,9 @@ hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream);
 hipError_t sorted_occupancy(int* blocks_per_cu);
 
 // The library's static device scratch: the workspace of the entry point that
-// allocates nothing (topk_transform_noalloc).  One copy per device, 16 MiB,
-// which holds the header and up to kScratchSlots split-row slots.
-constexpr size_t kScratchWords = (size_t)4 << 20;
+// allocates nothing (topk_transform_noalloc).  One copy per device, 24 MiB,
+// which holds the header and up to kScratchSlots (152) split-row slots.
+constexpr size_t kScratchWords = (size_t)6 << 20;
 constexpr int64_t kScratchSlots = (int64_t)((kScratchWords - kHdrWords) / (kBarWords + 2 * kRegionWords));
 // Its address on the current device (hipGetSymbolAddress: the array's
 // host-side name is not a device address).  Called once per device.

@@ -451,8 +451,9 @@ __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass
 // candidate with (key >> shift) == prefix is of it, cnt of them, `need` of
 // them were selected.
 // With `fill`, slots [0, n) of sh_raw are first set to -1 (nothing else
-// has written them yet).
-template <int NT>
+// has written them yet).  With INDEX the slots receive candidate indices
+// (into sh_ckey / sh_cpos) instead of positions.
+template <int NT, bool INDEX = false>
 __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, int& shift, uint32_t& cnt,
                                                   uint32_t& need, uint32_t gt_base, uint32_t n,
                                                   uint32_t* sh_hist, const uint32_t* sh_ckey,
@@ -486,10 +487,10 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, i
     const uint32_t x = sh_ckey[i] >> shift;
     if (x > prefix) {
       const uint32_t s = atomicAdd(&sh_var[8], 1u);
-      if (s < gt_end) sh_raw[s] = sh_cpos[i];
+      if (s < gt_end) sh_raw[s] = INDEX ? i : sh_cpos[i];
     } else if (x == prefix && sh_ckey[i] != 0u) {
       const uint32_t e = atomicAdd(&sh_var[9], 1u);
-      if (e < need) sh_raw[gt_end + e] = sh_cpos[i];
+      if (e < need) sh_raw[gt_end + e] = INDEX ? i : sh_cpos[i];
     }
   }
   __syncthreads();
@@ -554,12 +555,14 @@ __device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* r
 // instantiation, so the one-pass split kernel keeps its split-only code.
 template <int E, bool COOP, bool SHORT>
 __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
+  constexpr bool kOverlap = !SHORT;   // see the compaction below
   __shared__ uint32_t sh_hist[kBinsWide];
   __shared__ int32_t sh_raw[kMaxK + 64];   // + one trash word per lane
   __shared__ uint32_t sh_scan[64];   // block-scan wave totals, or the 64 coarse bins of find_threshold
   __shared__ uint32_t sh_var[16];
   __shared__ uint32_t sh_ckey[COOP ? kCandCap : 1];
   __shared__ int32_t sh_cpos[COOP ? kCandCap : 1];
+  __shared__ int32_t sh_cout[COOP && kOverlap ? kCandCap : 1];   // the candidates' output values
 
   const int G = COOP ? a.wgs_per_row : 1;
   const int slot = (int)blockIdx.x / G;
@@ -676,68 +679,169 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     uint32_t tot;
     const uint32_t off = block_exclusive_scan<kThreads>((cg << 17) | ce, sh_scan, tot, tid);
     uint32_t off_g = off >> 17, off_e = off & 0x1FFFFu;
-    if (split) {
-      if (tid == 0) {
-        // both offsets from one atomic (one round trip instead of two): the
-        // strictly-greater count in the high word, the threshold-bin count in
-        // the low word (a row's total is below 2^31, so it never carries)
-        const uint32_t tg = tot >> 17, te = tot & 0x1FFFFu;
-        const uint64_t old = g_add64_ret(reinterpret_cast<uint64_t*>(region + kRegCtr + kCtrSlots),
-                                         ((uint64_t)tg << 32) | (uint64_t)te);
-        sh_var[4] = (uint32_t)(old >> 32);
-        sh_var[5] = (uint32_t)old;
-        sh_var[7] = 0u;   // this workgroup's (slot, position) pairs staged below
-      }
-      __syncthreads();
-      off_g += uniform(sh_var[4]);
-      off_e += uniform(sh_var[5]);
-    }
-    // Selected keys are rare: a wave skips a register slot unless one of its
-    // lanes holds a key at or above the threshold prefix.  Inside, lanes that
-    // have nothing to store write a private trash word instead of branching.
-    const uint32_t trash = (uint32_t)kMaxK + (uint32_t)(tid & 63);
-    // Split rows stage each final (slot, position) pair in LDS (sh_ckey /
-    // sh_raw; a row has n <= kMaxK slots, so fewer pairs than either holds)
-    // and write them after the loop: a page-table gather per selected key
-    // inside the loop would make each register slot wait out a load.
-    auto stage_slot = [&](uint32_t slot, int32_t pos) {
-      const uint32_t li = atomicAdd(&sh_var[7], 1u);
-      sh_ckey[li] = slot;
-      sh_raw[li] = pos;
-    };
-    launder(key);   // recompute the compares here instead of keeping 2E masks from the counting loop
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const uint32_t x = key[j];
-      const uint32_t xp = x >> shift;
-      const bool isg = xp > prefix;
-      const bool ise = (xp == prefix) && (x != 0u);
-      if (__ballot(isg || ise) == 0ull) continue;
-      const uint32_t sg = off_g, se = off_e;
-      off_g += isg ? 1u : 0u;
-      off_e += ise ? 1u : 0u;
-      if (!split) {
-        const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : trash);
-        sh_raw[slot] = pos_of(j);
-      } else if (mode == kModeCands) {
-        if (isg && sg < n_gt) stage_slot(sg, pos_of(j));
-        if (ise && se < (uint32_t)kCandCap) {
-          g_store(region + kRegCandKey + se, x);
-          g_store(region + kRegCandPos + se, (uint32_t)pos_of(j));
+    // One-pass split rows (kOverlap) take their offsets while the selected
+    // keys are staged and gathered, and hand the finisher candidates with
+    // their output values.  Rows cycled over slots keep the staged-slot
+    // form (offsets first, then the gathers), measured faster there: the
+    // cycled batch's finish overlaps the slot's next row, and the overlapped
+    // form took it from 48.1 to 49.4 us.
+    if constexpr (kOverlap) {
+      // Split rows: the workgroup's slots come from one atomic on the row's
+      // counter (the strictly-greater count in the high word, the threshold-bin
+      // count in the low word; a row's total is below 2^31, so it never
+      // carries).  While it is in flight, the selected keys are staged in LDS
+      // at their ranks within the workgroup and the page-table entry of every
+      // staged key is gathered: the outputs (and the candidates' output values)
+      // are stored as soon as the offsets arrive, with no gather after them.
+      const uint32_t tg = tot >> 17, te = tot & 0x1FFFFu;
+      uint64_t base = 0;
+      if (split && tid == 0)
+        base = g_add64_ret(reinterpret_cast<uint64_t*>(region + kRegCtr + kCtrSlots), ((uint64_t)tg << 32) | (uint64_t)te);
+      // Selected keys are rare: a wave skips a register slot unless one of its
+      // lanes holds a key at or above the threshold prefix.  Inside, lanes that
+      // have nothing to store write a private trash word instead of branching.
+      // Split rows stage greater keys at ranks [0, tg) of sh_raw (tg <= n -
+      // need <= kMaxK) and threshold-bin keys at ranks [0, min(te, kCandCap))
+      // of sh_ckey / sh_cpos (a rank past that can be neither a candidate nor
+      // a tie slot).
+      const uint32_t trash = (uint32_t)kMaxK + (uint32_t)(tid & 63);
+      launder(key);   // recompute the compares here instead of keeping 2E masks from the counting loop
+  #pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const uint32_t x = key[j];
+        const uint32_t xp = x >> shift;
+        const bool isg = xp > prefix;
+        const bool ise = (xp == prefix) && (x != 0u);
+        if (__ballot(isg || ise) == 0ull) continue;
+        const uint32_t sg = off_g, se = off_e;
+        off_g += isg ? 1u : 0u;
+        off_e += ise ? 1u : 0u;
+        if (!split) {
+          const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : trash);
+          sh_raw[slot] = pos_of(j);
+        } else {
+          if (isg) sh_raw[sg] = pos_of(j);
+          if (ise && se < (uint32_t)kCandCap) {
+            sh_ckey[se] = x;
+            sh_cpos[se] = pos_of(j);
+          }
         }
-      } else {
-        const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : 0xFFFFFFFFu);
-        if (slot != 0xFFFFFFFFu) stage_slot(slot, pos_of(j));
+      }
+      if (split) {
+        __syncthreads();
+        const uint32_t te_staged = te < (uint32_t)kCandCap ? te : (uint32_t)kCandCap;
+        const int ps = a.log2_page;
+        const uint32_t pmask = (1u << ps) - 1u;
+        const int32_t* pt = a.page_table + row * a.pages_per_row;
+        auto transformed = [&](int32_t r, int32_t page) -> int32_t {
+          return (int64_t)(r >> ps) < a.pages_per_row ? (int32_t)(((uint32_t)page << ps) | ((uint32_t)r & pmask)) : -1;
+        };
+        // The page values go to LDS (the histogram and the finisher's output
+        // list are free now), so nothing is held in registers across the wait:
+        // greater keys' pages at sh_hist[i], threshold-bin keys' at sh_cout[i].
+        int32_t* const g_page = reinterpret_cast<int32_t*>(sh_hist);
+        for (uint32_t i = (uint32_t)tid; i < tg; i += kThreads) {
+          const int32_t r = sh_raw[i];
+          g_page[i] = (int64_t)(r >> ps) < a.pages_per_row ? pt[r >> ps] : 0;
+        }
+        for (uint32_t i = (uint32_t)tid; i < te_staged; i += kThreads) {
+          const int32_t r = sh_cpos[i];
+          sh_cout[i] = (int64_t)(r >> ps) < a.pages_per_row ? pt[r >> ps] : 0;
+        }
+        if (tid == 0) {
+          sh_var[4] = (uint32_t)(base >> 32);
+          sh_var[5] = (uint32_t)base;
+        }
+        __syncthreads();
+        const uint32_t base_g = uniform(sh_var[4]), base_e = uniform(sh_var[5]);
+        int32_t* o = a.out + row * (int64_t)k;
+        int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
+        for (uint32_t i = (uint32_t)tid; i < tg; i += kThreads) {
+          const uint32_t slot = base_g + i;
+          if (slot < n_gt) {
+            const int32_t r = sh_raw[i];
+            o[slot] = transformed(r, g_page[i]);
+            if (orw) orw[slot] = r;
+          }
+        }
+        for (uint32_t i = (uint32_t)tid; i < te_staged; i += kThreads) {
+          const uint32_t e = base_e + i;
+          const int32_t r = sh_cpos[i];
+          if (mode == kModeCands) {
+            if (e < (uint32_t)kCandCap) {
+              g_store(region + kRegCandKey + e, sh_ckey[i]);
+              g_store(region + kRegCandPos + e, (uint32_t)r);
+              g_store(region + kRegCandOut + e, (uint32_t)transformed(r, sh_cout[i]));
+            }
+          } else if (e < need) {
+            o[n_gt + e] = transformed(r, sh_cout[i]);
+            if (orw) orw[n_gt + e] = r;
+          }
+        }
+      }
+    } else {
+      if (split) {
+        if (tid == 0) {
+          // both offsets from one atomic (one round trip instead of two): the
+          // strictly-greater count in the high word, the threshold-bin count in
+          // the low word (a row's total is below 2^31, so it never carries)
+          const uint32_t tg = tot >> 17, te = tot & 0x1FFFFu;
+          const uint64_t old = g_add64_ret(reinterpret_cast<uint64_t*>(region + kRegCtr + kCtrSlots),
+                                           ((uint64_t)tg << 32) | (uint64_t)te);
+          sh_var[4] = (uint32_t)(old >> 32);
+          sh_var[5] = (uint32_t)old;
+          sh_var[7] = 0u;   // this workgroup's (slot, position) pairs staged below
+        }
+        __syncthreads();
+        off_g += uniform(sh_var[4]);
+        off_e += uniform(sh_var[5]);
+      }
+      // Selected keys are rare: a wave skips a register slot unless one of its
+      // lanes holds a key at or above the threshold prefix.  Inside, lanes that
+      // have nothing to store write a private trash word instead of branching.
+      const uint32_t trash = (uint32_t)kMaxK + (uint32_t)(tid & 63);
+      // Split rows stage each final (slot, position) pair in LDS (sh_ckey /
+      // sh_raw; a row has n <= kMaxK slots, so fewer pairs than either holds)
+      // and write them after the loop: a page-table gather per selected key
+      // inside the loop would make each register slot wait out a load.
+      auto stage_slot = [&](uint32_t slot, int32_t pos) {
+        const uint32_t li = atomicAdd(&sh_var[7], 1u);
+        sh_ckey[li] = slot;
+        sh_raw[li] = pos;
+      };
+      launder(key);   // recompute the compares here instead of keeping 2E masks from the counting loop
+  #pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const uint32_t x = key[j];
+        const uint32_t xp = x >> shift;
+        const bool isg = xp > prefix;
+        const bool ise = (xp == prefix) && (x != 0u);
+        if (__ballot(isg || ise) == 0ull) continue;
+        const uint32_t sg = off_g, se = off_e;
+        off_g += isg ? 1u : 0u;
+        off_e += ise ? 1u : 0u;
+        if (!split) {
+          const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : trash);
+          sh_raw[slot] = pos_of(j);
+        } else if (mode == kModeCands) {
+          if (isg && sg < n_gt) stage_slot(sg, pos_of(j));
+          if (ise && se < (uint32_t)kCandCap) {
+            g_store(region + kRegCandKey + se, x);
+            g_store(region + kRegCandPos + se, (uint32_t)pos_of(j));
+          }
+        } else {
+          const uint32_t slot = (isg && sg < n_gt) ? sg : ((ise && se < need) ? n_gt + se : 0xFFFFFFFFu);
+          if (slot != 0xFFFFFFFFu) stage_slot(slot, pos_of(j));
+        }
+      }
+      if (split) {
+        // The staged slots are final: write them through the page table, every
+        // gather in flight at once.
+        __syncthreads();
+        const uint32_t nsel = uniform(sh_var[7]);
+        for (uint32_t i = (uint32_t)tid; i < nsel; i += kThreads) write_slot(a, row, sh_ckey[i], sh_raw[i]);
       }
     }
-    if (split) {
-      // The staged slots are final: write them through the page table, every
-      // gather in flight at once.
-      __syncthreads();
-      const uint32_t nsel = uniform(sh_var[7]);
-      for (uint32_t i = (uint32_t)tid; i < nsel; i += kThreads) write_slot(a, row, sh_ckey[i], sh_raw[i]);
-    }
-
     if (!split) {
       __syncthreads();
       write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid);
@@ -759,17 +863,43 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     // A split row has L > k, so n = k: every slot below n_gt (all n of them
     // outside the candidates mode) was written by the workgroup whose key
     // took it; the candidates fill [n_gt, n).
-    if (mode == kModeCands) {
-      const int ncand = (int)(cnt < (uint32_t)kCandCap ? cnt : (uint32_t)kCandCap);
-      for (int i = tid; i < ncand; i += kThreads) {
-        sh_ckey[i] = g_load(region + kRegCandKey + i);
-        sh_cpos[i] = (int32_t)g_load(region + kRegCandPos + i);
+    if constexpr (kOverlap) {
+      if (mode == kModeCands) {
+        // Each candidate arrives with its output value (its workgroup did the
+        // page-table gather): the selected ones are written with no gather.
+        const int ncand = (int)(cnt < (uint32_t)kCandCap ? cnt : (uint32_t)kCandCap);
+        for (int i = tid; i < ncand; i += kThreads) {
+          sh_ckey[i] = g_load(region + kRegCandKey + i);
+          sh_cpos[i] = (int32_t)g_load(region + kRegCandPos + i);
+          sh_cout[i] = (int32_t)g_load(region + kRegCandOut + i);
+        }
+        __syncthreads();
+        select_candidates<kThreads, true>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
+                                          sh_raw, sh_scan, sh_var, tid);
+        __syncthreads();
+        // A split row has L > k: n = k, and the candidates fill [n_gt, k).
+        int32_t* o = a.out + row * (int64_t)k;
+        int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
+        for (int j = (int)n_gt + tid; j < k; j += kThreads) {
+          const int i = sh_raw[j];
+          const bool ok = i >= 0 && i < ncand;
+          o[j] = ok ? sh_cout[i] : -1;
+          if (orw) orw[j] = ok ? sh_cpos[i] : -1;
+        }
       }
-      __syncthreads();
-      select_candidates<kThreads>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
-                        sh_scan, sh_var, tid);
-      __syncthreads();
-      write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid, nullptr, (int)n_gt);
+    } else {
+      if (mode == kModeCands) {
+        const int ncand = (int)(cnt < (uint32_t)kCandCap ? cnt : (uint32_t)kCandCap);
+        for (int i = tid; i < ncand; i += kThreads) {
+          sh_ckey[i] = g_load(region + kRegCandKey + i);
+          sh_cpos[i] = (int32_t)g_load(region + kRegCandPos + i);
+        }
+        __syncthreads();
+        select_candidates<kThreads>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
+                          sh_scan, sh_var, tid);
+        __syncthreads();
+        write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid, nullptr, (int)n_gt);
+      }
     }
     if (tid == 0) record_selection(a, row, prefix, shift, need, cnt, 1u);
     // leave the region zeroed for the row this slot handles two iterations on

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert topk.topk_abi_version() == 2
+    assert topk.topk_abi_version() == 3
     for code, name in topk.STATUS.items():
         assert topk.topk_status_string(code) == name
     assert topk.topk_status_string(99) == "TOPK_UNKNOWN_STATUS"
@@ -96,6 +96,8 @@ def test_wait_limit_setter(lib):
     restores the default."""
     assert lib.topk_set_wait_limit(1) == 0
     assert lib.topk_set_wait_limit(0) == 0
+    assert lib.topk_set_scratch_limit(1 << 20) == 0
+    assert lib.topk_set_scratch_limit(0) == 0
 
 
 def test_python_binding_rejects_bad_tensors():

@@ -78,19 +78,25 @@ def test_noalloc_matches_topk_transform(lib, case):
 
 
 def test_noalloc_rejects_beyond_scratch(lib):
-    """A plan needing more split-row slots than the scratch holds is refused
-    with TOPK_ERROR_UNSUPPORTED and a message, and nothing is queued."""
+    """A plan needing more workspace than the scratch holds is refused with
+    TOPK_ERROR_UNSUPPORTED and a message, and nothing is queued.  No plan
+    needs more than the real scratch (split grids are capped at the resident
+    workgroups, at most 128 slots of 2 workgroups), so the scratch the entry
+    point may use is lowered to 1M words (4 MiB) for the call: 200 rows forced
+    onto 2 split workgroups each need far more."""
     import torch
     w = workloads.custom(75, 200, 8192, 64, 64, kind="normal")
     s, sl, pt = upload(w)
     out = torch.full((w.batch, w.k), -7, dtype=torch.int32, device=s.device)
-    lib.topk_set_dispatch_override(4, 2)   # 200 rows of 2 split workgroups: 200 slots
+    lib.topk_set_dispatch_override(4, 2)
+    lib.topk_set_scratch_limit(1 << 20)
     try:
         st = lib.load().topk_transform_noalloc(s.data_ptr(), sl.data_ptr(), pt.data_ptr(), w.k, w.page_size,
                                                out.data_ptr(), None,
                                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
                                                w.batch, w.width, pt.shape[1])
     finally:
+        lib.topk_set_scratch_limit(0)
         lib.topk_set_dispatch_override(0, 0)
     assert st == 2 and "scratch" in lib.topk_last_error(), (st, lib.topk_last_error())
     torch.cuda.synchronize()
