@@ -769,9 +769,14 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
           const int32_t r = sh_cpos[i];
           if (mode == kModeCands) {
             if (e < (uint32_t)kCandCap) {
-              g_store(region + kRegCandKey + e, sh_ckey[i]);
+              const uint32_t x = sh_ckey[i];
+              g_store(region + kRegCandKey + e, x);
               g_store(region + kRegCandPos + e, (uint32_t)r);
               g_store(region + kRegCandOut + e, (uint32_t)transformed(r, sh_cout[i]));
+              // the candidates' next digit, merged in the next pass's
+              // histogram (unused in this mode, zero at rest): the finisher
+              // starts from it instead of histogramming the candidates
+              g_add(region + (shift == 20 ? kRegHist1 : kRegHist2) + ((x >> (shift - 10)) & 1023u), 1u);
             }
           } else if (e < need) {
             o[n_gt + e] = transformed(r, sh_cout[i]);
@@ -867,13 +872,42 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
       if (mode == kModeCands) {
         // Each candidate arrives with its output value (its workgroup did the
         // page-table gather): the selected ones are written with no gather.
+        // The candidates' next digit arrives merged (the workgroups counted
+        // it), so the first refinement needs no pass over them.
         const int ncand = (int)(cnt < (uint32_t)kCandCap ? cnt : (uint32_t)kCandCap);
-        for (int i = tid; i < ncand; i += kThreads) {
-          sh_ckey[i] = g_load(region + kRegCandKey + i);
-          sh_cpos[i] = (int32_t)g_load(region + kRegCandPos + i);
-          sh_cout[i] = (int32_t)g_load(region + kRegCandOut + i);
+        static_assert(kThreads == kBinsNarrow, "one merged next-digit bin per thread");
+        const uint32_t sub = g_load(region + (shift == 20 ? kRegHist1 : kRegHist2) + tid);
+        // every candidate load in flight before the first is stored
+        constexpr int kPer = kCandCap / kThreads;
+        uint32_t ck[kPer], cp[kPer], co[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int i = tid + q * kThreads;
+          if (i < ncand) {
+            ck[q] = g_load(region + kRegCandKey + i);
+            cp[q] = g_load(region + kRegCandPos + i);
+            co[q] = g_load(region + kRegCandOut + i);
+          }
         }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int i = tid + q * kThreads;
+          if (i < ncand) {
+            sh_ckey[i] = ck[q];
+            sh_cpos[i] = (int32_t)cp[q];
+            sh_cout[i] = (int32_t)co[q];
+          }
+        }
+        sh_hist[tid] = sub;
         __syncthreads();
+        find_threshold<kThreads, kBinsNarrow>(sh_hist, need, sh_scan, sh_var, tid);
+        {
+          const uint32_t bin = uniform(sh_var[0]), gt = uniform(sh_var[1]);
+          cnt = uniform(sh_var[2]);
+          need -= gt;
+          prefix = (prefix << 10) | bin;
+          shift -= 10;
+        }
         select_candidates<kThreads, true>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
                                           sh_raw, sh_scan, sh_var, tid);
         __syncthreads();
