@@ -265,7 +265,7 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, int G, int g, uint32_
     // again before the generation that releases the workgroups is published.
     bool closer = false;
     if (g_inc_wrap(bar + (size_t)grp * kBarLine, gsize - 1u) == gsize - 1u)
-      closer = g_inc_wrap(bar + kBarTop, (uint32_t)ngroups - 1u) == (uint32_t)ngroups - 1u;
+      closer = ngroups == 1 || g_inc_wrap(bar + kBarTop, (uint32_t)ngroups - 1u) == (uint32_t)ngroups - 1u;
     if (closer) {
       g_store(bar + kBarGen, gen);   // nothing this workgroup does next depends on its completion
     } else {
