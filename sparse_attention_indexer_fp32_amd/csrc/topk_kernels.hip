@@ -953,7 +953,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 // ---------------------------------------------------------------------------
 
 // Stream-kernel LDS words (sh_var indices).
-enum : int { kVarCandCount = 10, kVarOverflow = 11, kVarGt = 12, kVarEq = 13 };
+enum : int { kVarCandCount = 10, kVarOverflow = 11, kVarGt = 12, kVarEq = 13, kVarAbove = 14 };
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -1313,6 +1313,7 @@ stream_rows_kernel(KernelArgs a) {
     // row that fits in the sample has no loop) before the count is read; the
     // histogram is cleared for the list under the same barrier.
     for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
+    if (tid == 0) sh_var[kVarAbove] = 0;
     __syncthreads();
     // The next row's length and this row's page table are requested now and
     // first used after the finish below.
@@ -1338,22 +1339,45 @@ stream_rows_kernel(KernelArgs a) {
     const bool low_count = count < (uint32_t)n;
     const bool overflow = low_count || uniform(sh_var[kVarOverflow]) != 0u || count > (uint32_t)CAP;
     const uint32_t floor = low_count ? 1u : gate;
+    // The list's keys are all at or above the gate, so their 22-bit prefixes
+    // are at or above the gate's, P: a histogram of the prefixes in a window
+    // of kBinsWide bins from P (the keys above the window counted apart)
+    // resolves the threshold to 22 bits in one pass, where the 12-bit digit
+    // needs a 10-bit refinement after it.  When n keys lie above the window
+    // (the threshold is above it), the 12-bit histogram is taken instead.
+    const uint32_t wbase = gate >> 10;
+    bool windowed = false;
+    uint32_t above = 0;
     if (!overflow) {
-      for (uint32_t i = (uint32_t)tid; i < count; i += NT) atomicAdd(&sh_hist[sh_ckey[i] >> 20], 1u);
+      for (uint32_t i = (uint32_t)tid; i < count; i += NT) {
+        const uint32_t d = (sh_ckey[i] >> 10) - wbase;
+        if (d < (uint32_t)kBinsWide) atomicAdd(&sh_hist[d], 1u);
+        else atomicAdd(&sh_var[kVarAbove], 1u);
+      }
       __syncthreads();
+      above = uniform(sh_var[kVarAbove]);
+      windowed = above < (uint32_t)n;
+      if (!windowed) {
+        above = 0;
+        for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
+        __syncthreads();
+        for (uint32_t i = (uint32_t)tid; i < count; i += NT) atomicAdd(&sh_hist[sh_ckey[i] >> 20], 1u);
+        __syncthreads();
+      }
     } else {
       for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
       __syncthreads();
       restream_pass<NT, CAP, CV>(3, rowp, L, vec, floor, 0u, 20, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
                                  sh_var, tid);
     }
-    find_threshold<NT, kBinsWide>(sh_hist, (uint32_t)n, sh_scan, sh_var, tid);
+    find_threshold<NT, kBinsWide>(sh_hist, (uint32_t)n - above, sh_scan, sh_var, tid);
     const uint32_t t0 = uniform(sh_var[0]), gt0 = uniform(sh_var[1]), cnt0 = uniform(sh_var[2]);
-    // From here the 12-bit histogram is done with: its upper half holds the
+    // From here the first histogram is done with: its upper half holds the
     // selected positions (-1 filled before they are written).
     if (!overflow) {
-      uint32_t fprefix = t0, fneed = (uint32_t)n - gt0, fcnt = cnt0;
-      int fshift = 20;
+      // windowed: the threshold's 22-bit prefix, with `above` keys over it
+      uint32_t fprefix = windowed ? wbase + t0 : t0, fneed = (uint32_t)n - above - gt0, fcnt = cnt0;
+      int fshift = windowed ? 10 : 20;
       select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
                             sh_raw, sh_scan, sh_var, tid, true);
       if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, gate);
@@ -1674,9 +1698,14 @@ split_stream_kernel(KernelArgs a) {
   if (tid == 0) {
     sh_var[kVarCandCount] = 0u;
     sh_var[kVarOverflow] = 0u;
+    sh_var[kVarAbove] = 0u;
   }
   for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
   __syncthreads();
+  // As the keys are appended, their 22-bit prefixes are counted in a window
+  // of kBinsWide bins from the floor's (keys above it counted apart), as in
+  // the streaming finish: the threshold comes out at 22 bits from one pass.
+  const uint32_t wbase = floor0 >> 10;
   {
     // the area's keys >= floor into the LDS list: one ballot append per round
     const int lane = tid & 63;
@@ -1685,14 +1714,17 @@ split_stream_kernel(KernelArgs a) {
       const bool pass = xk[r] >= floor0 && xk[r] != 0u;
       const uint64_t msk = __ballot(pass);
       if (msk == 0ull) continue;
-      uint32_t wbase = 0;
-      if (lane == 0) wbase = atomicAdd(&sh_var[kVarCandCount], (uint32_t)__popcll(msk));
-      wbase = __builtin_amdgcn_readfirstlane(wbase);
+      uint32_t lbase = 0;
+      if (lane == 0) lbase = atomicAdd(&sh_var[kVarCandCount], (uint32_t)__popcll(msk));
+      lbase = __builtin_amdgcn_readfirstlane(lbase);
       if (pass) {
-        uint32_t slot = wbase + lanes_below(msk);
+        uint32_t slot = lbase + lanes_below(msk);
         slot = slot < (uint32_t)CAP ? slot : (uint32_t)CAP;
         sh_ckey[slot] = xk[r];
         sh_cpos[slot] = (int32_t)xp[r];
+        const uint32_t d = (xk[r] >> 10) - wbase;
+        if (d < (uint32_t)kBinsWide) atomicAdd(&sh_hist[d], 1u);
+        else atomicAdd(&sh_var[kVarAbove], 1u);
       }
     }
   }
@@ -1701,18 +1733,26 @@ split_stream_kernel(KernelArgs a) {
   const bool low_count = count < (uint32_t)n;
   const bool overflow = lost || low_count || count > (uint32_t)CAP;
   const uint32_t floor = low_count ? 1u : floor0;
-  if (!overflow) {
-    for (uint32_t i = (uint32_t)tid; i < count; i += NT) atomicAdd(&sh_hist[sh_ckey[i] >> 20], 1u);
+  uint32_t above = overflow ? 0u : uniform(sh_var[kVarAbove]);
+  const bool windowed = !overflow && above < (uint32_t)n;
+  if (!windowed) {   // the 12-bit histogram instead: of the list, or of the row from memory
+    above = 0;
+    for (int b = tid; b < kBinsWide; b += NT) sh_hist[b] = 0;
     __syncthreads();
-  } else {
-    restream_pass<NT, CAP, CV>(3, rowp, L, vec, floor, 0u, 20, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
-                               sh_var, tid);
+    if (!overflow) {
+      for (uint32_t i = (uint32_t)tid; i < count; i += NT) atomicAdd(&sh_hist[sh_ckey[i] >> 20], 1u);
+      __syncthreads();
+    } else {
+      restream_pass<NT, CAP, CV>(3, rowp, L, vec, floor, 0u, 20, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
+                                 sh_var, tid);
+    }
   }
-  find_threshold<NT, kBinsWide>(sh_hist, (uint32_t)n, sh_scan, sh_var, tid);
+  find_threshold<NT, kBinsWide>(sh_hist, (uint32_t)n - above, sh_scan, sh_var, tid);
   const uint32_t t0 = uniform(sh_var[0]), gt0 = uniform(sh_var[1]), cnt0 = uniform(sh_var[2]);
   if (!overflow) {
-    uint32_t fprefix = t0, fneed = (uint32_t)n - gt0, fcnt = cnt0;
-    int fshift = 20;
+    // windowed: the threshold's 22-bit prefix, with `above` keys over it
+    uint32_t fprefix = windowed ? wbase + t0 : t0, fneed = (uint32_t)n - above - gt0, fcnt = cnt0;
+    int fshift = windowed ? 10 : 20;
     select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
                           sh_raw, sh_scan, sh_var, tid, true);
     if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, floor);
