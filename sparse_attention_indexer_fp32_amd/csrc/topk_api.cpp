@@ -45,7 +45,8 @@ struct DeviceInfo {
   int cus = 0;
   int occ[2][topk::kNumEpt] = {};   // [split][ept] resident workgroups per CU
   int stream_occ[topk::kNumStreamVariants] = {};   // streaming kernel shapes: resident workgroups per CU
-  int sorted_occ = 0;               // sorted finish: resident workgroups per CU
+  int sorted_occ_small = 0;         // sorted finish: resident workgroups per CU, k <= kSortSmallK
+  int sorted_occ = 0;               //                                            larger k
   int ss_occ[topk::kNumSplitStreamVariants] = {};   // split streaming shapes: resident workgroups per CU
   uint32_t* fault_page = nullptr;   // pinned, device-mapped host memory (kFaultWords words), or null
   uint32_t* fault_page_dev = nullptr;   // its device address
@@ -113,7 +114,8 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
       e = topk::stream_occupancy(v, &info.stream_occ[v]);
       if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     }
-    e = topk::sorted_occupancy(&info.sorted_occ);
+    e = topk::sorted_occupancy(topk::kSortSmallK, &info.sorted_occ_small);
+    if (e == hipSuccess) e = topk::sorted_occupancy(topk::kMaxK, &info.sorted_occ);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     for (int v = 0; v < topk::kNumSplitStreamVariants; ++v) {
       e = topk::split_stream_occupancy(v, &info.ss_occ[v]);
@@ -578,7 +580,7 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     // the finish reads every row's record once the selection launch is done (stream order)
     topk::KernelArgs f = a;
     f.out_raw = out_raw;   // the caller's (or none); f.sel holds the selection launch's positions
-    sorted_slots = (int64_t)info->sorted_occ * info->cus;
+    sorted_slots = (int64_t)(k <= topk::kSortSmallK ? info->sorted_occ_small : info->sorted_occ) * info->cus;
     if (sorted_slots > batch) sorted_slots = batch;
     if (sorted_slots < 1) sorted_slots = 1;
     f.slots = (int32_t)sorted_slots;

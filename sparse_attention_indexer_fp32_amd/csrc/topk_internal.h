@@ -31,6 +31,8 @@ constexpr int kMaxK = 2048;
 constexpr int kBinsWide = 4096;         // radix pass 0 digit: key bits 31..20
 constexpr int kBinsNarrow = 1024;       // passes 1 and 2: key bits 19..10, 9..0
 constexpr int kCandCap = 4096;          // threshold-bin candidates one workgroup finishes in LDS
+constexpr int kSortSmallK = 512;        // sorted finish: k up to this takes the small workgroup shape
+constexpr int kSortSmallThreads = 256;
 
 // Elements per thread the kernels are instantiated for (register-resident keys).
 constexpr int kNumEpt = 5;
@@ -151,9 +153,10 @@ hipError_t split_stream_occupancy(int variant, int* blocks_per_cu);
 
 // Sorted finish (deterministic mode): one workgroup per row, persistent over
 // rows (grid = slots); reads the per-row records a selection launch left in
-// `meta` and rewrites the row's outputs in canonical order.
+// `meta` and rewrites the row's outputs in canonical order.  The workgroup
+// shape depends on k (kSortSmallK); sorted_occupancy reports the one for k.
 hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream);
-hipError_t sorted_occupancy(int* blocks_per_cu);
+hipError_t sorted_occupancy(int k, int* blocks_per_cu);
 
 // The library's static device scratch: the workspace of the entry point that
 // allocates nothing (topk_transform_noalloc).  One copy per device, 24 MiB,

@@ -1820,7 +1820,6 @@ split_stream_kernel(KernelArgs a) {
 // members than the tie list holds, the same select runs over the row in
 // memory.  The n chosen (key, ~position) pairs are then bitonic-sorted in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kSortTieCap = 4096;
 constexpr int kSortCV = 4;   // float4 groups per thread per streamed chunk
 
 // One pass over the row for the memory fallback of the tie select: with
@@ -1828,17 +1827,18 @@ constexpr int kSortCV = 4;   // float4 groups per thread per streamed chunk
 // at dshift 20, else 10) of the bin members whose v >> (vshift) == vprefix
 // (vshift 32: all); with `collect` true, appends the members with
 // v >> vshift >= vprefix to sh_sort from slot `base` on.
+template <int NT, int CAP>
 __device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp, uint32_t L, bool vec,
                                                 uint32_t prefix, int shift, uint32_t floor, uint32_t vprefix,
                                                 int vshift, int dshift, uint32_t* sh_hist, uint64_t* sh_sort,
                                                 uint32_t base, uint32_t* sh_var, int tid) {
-  constexpr uint32_t span = (uint32_t)kThreads * 4u * kSortCV;
+  constexpr uint32_t span = (uint32_t)NT * 4u * kSortCV;
   for (uint32_t c = 0; c < L; c += span) {
     uint32_t raw[4 * kSortCV];
-    load_raw<kThreads, kSortCV, kLoadReuse>(raw, rowp, c, L, vec, tid);
+    load_raw<NT, kSortCV, kLoadReuse>(raw, rowp, c, L, vec, tid);
 #pragma unroll
     for (int j = 0; j < 4 * kSortCV; ++j) {
-      const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3);
+      const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (NT * 4) + (uint32_t)(j & 3);
       if (pos >= L) continue;
       const uint32_t x = order_key_bits(raw[j]);
       if (x < floor || ((uint64_t)x >> shift) != (uint64_t)prefix) continue;
@@ -1848,21 +1848,22 @@ __device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp,
         if (vshift >= 32 || vp == vprefix) atomicAdd(&sh_hist[(v >> dshift) & (dshift == 20 ? 4095u : 1023u)], 1u);
       } else if (vp >= vprefix) {
         const uint32_t s = base + atomicAdd(&sh_var[2], 1u);
-        if (s < (uint32_t)kMaxK) sh_sort[s] = ((uint64_t)x << 32) | (uint64_t)v;
+        if (s < (uint32_t)CAP) sh_sort[s] = ((uint64_t)x << 32) | (uint64_t)v;
       }
     }
   }
   __syncthreads();
 }
 
-__global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
-  __shared__ uint64_t sh_sort[kMaxK];        // (key << 32) | ~position of the selected
-  __shared__ uint32_t sh_tk[kSortTieCap];    // threshold-bin members: key
-  __shared__ uint32_t sh_tp[kSortTieCap];    //                        position
+template <int NT, int CAP, int TIES>
+__global__ void __launch_bounds__(NT) sorted_rows_kernel(KernelArgs a) {
+  __shared__ uint64_t sh_sort[CAP];    // (key << 32) | ~position of the selected
+  __shared__ uint32_t sh_tk[TIES];     // threshold-bin members: key
+  __shared__ uint32_t sh_tp[TIES];     //                        position
   __shared__ uint32_t sh_hist[kBinsWide];
   __shared__ uint32_t sh_scan[64];
   __shared__ uint32_t sh_var[16];
-  constexpr uint32_t span = (uint32_t)kThreads * 4u * kSortCV;
+  constexpr uint32_t span = (uint32_t)NT * 4u * kSortCV;
   const int64_t W = a.width;
   const int k = a.k;
   const bool vec = a.vec != 0;
@@ -1879,11 +1880,11 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
     const bool cut = uniform(m[4]) != 0u;
     const float* rowp = a.scores + row * W;
     if (tid < 16) sh_var[tid] = 0;
-    for (int i = tid; i < kMaxK; i += kThreads) sh_sort[i] = 0ull;   // unfilled slots read as no position
+    for (int i = tid; i < CAP; i += NT) sh_sort[i] = 0ull;   // unfilled slots read as no position
     __syncthreads();
     if (!cut) {
       const int32_t* sel = a.sel + row * (int64_t)k;
-      for (uint32_t j = (uint32_t)tid; j < n; j += kThreads) {
+      for (uint32_t j = (uint32_t)tid; j < n; j += NT) {
         const int32_t p = sel[j];
         if (p >= 0 && (uint32_t)p < L) {
           const uint32_t x = order_key_bits(__float_as_uint(rowp[p]));
@@ -1895,20 +1896,20 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
       // 1. keys above the bin -> sh_sort; the bin's members -> tie list
       for (uint32_t c = 0; c < L; c += span) {
         uint32_t raw[4 * kSortCV];
-        load_raw<kThreads, kSortCV, kLoadReuse>(raw, rowp, c, L, vec, tid);
+        load_raw<NT, kSortCV, kLoadReuse>(raw, rowp, c, L, vec, tid);
 #pragma unroll
         for (int j = 0; j < 4 * kSortCV; ++j) {
-          const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3);
+          const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (NT * 4) + (uint32_t)(j & 3);
           if (pos >= L) continue;
           const uint32_t x = order_key_bits(raw[j]);
           if (x < floor) continue;
           const uint64_t xp = (uint64_t)x >> shift;
           if (xp > (uint64_t)prefix) {
             const uint32_t s = atomicAdd(&sh_var[0], 1u);
-            if (s < (uint32_t)kMaxK) sh_sort[s] = ((uint64_t)x << 32) | (uint64_t)(~pos);
+            if (s < (uint32_t)CAP) sh_sort[s] = ((uint64_t)x << 32) | (uint64_t)(~pos);
           } else if (xp == (uint64_t)prefix) {
             const uint32_t t = atomicAdd(&sh_var[1], 1u);
-            if (t < (uint32_t)kSortTieCap) {
+            if (t < (uint32_t)TIES) {
               sh_tk[t] = x;
               sh_tp[t] = pos;
             }
@@ -1919,7 +1920,7 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
       const uint32_t ngt = uniform(sh_var[0]);
       const uint32_t nties = uniform(sh_var[1]);
       const uint32_t base = ngt < n ? ngt : n;
-      const bool in_lds = nties <= (uint32_t)kSortTieCap;
+      const bool in_lds = nties <= (uint32_t)TIES;
 
       // 2. which bin members: all, or the `need` lowest positions
       uint32_t vprefix = 0;
@@ -1929,22 +1930,22 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
         for (int level = 0; level < 3; ++level) {
           const int dshift = level == 0 ? 20 : (level == 1 ? 10 : 0);
           const int nb = level == 0 ? kBinsWide : kBinsNarrow;
-          for (int b = tid; b < nb; b += kThreads) sh_hist[b] = 0;
+          for (int b = tid; b < nb; b += NT) sh_hist[b] = 0;
           __syncthreads();
           if (in_lds) {
-            for (uint32_t i = (uint32_t)tid; i < nties; i += kThreads) {
+            for (uint32_t i = (uint32_t)tid; i < nties; i += NT) {
               const uint32_t v = ~sh_tp[i];
               if (vshift >= 32 || (v >> vshift) == vprefix)
                 atomicAdd(&sh_hist[(v >> dshift) & (level == 0 ? 4095u : 1023u)], 1u);
             }
             __syncthreads();
           } else {
-            sorted_tie_pass(false, rowp, L, vec, prefix, shift, floor, vprefix, vshift, dshift, sh_hist, sh_sort, 0u,
+            sorted_tie_pass<NT, CAP>(false, rowp, L, vec, prefix, shift, floor, vprefix, vshift, dshift, sh_hist, sh_sort, 0u,
                             sh_var, tid);
           }
           uint32_t bin, gtc, cnt;
-          if (level == 0) find_threshold<kThreads, kBinsWide>(sh_hist, vneed, sh_scan, sh_var, tid);
-          else find_threshold<kThreads, kBinsNarrow>(sh_hist, vneed, sh_scan, sh_var, tid);
+          if (level == 0) find_threshold<NT, kBinsWide>(sh_hist, vneed, sh_scan, sh_var, tid);
+          else find_threshold<NT, kBinsNarrow>(sh_hist, vneed, sh_scan, sh_var, tid);
           bin = uniform(sh_var[0]);
           gtc = uniform(sh_var[1]);
           cnt = uniform(sh_var[2]);
@@ -1959,16 +1960,16 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
       if (tid == 0) sh_var[2] = 0;
       __syncthreads();
       if (in_lds) {
-        for (uint32_t i = (uint32_t)tid; i < nties; i += kThreads) {
+        for (uint32_t i = (uint32_t)tid; i < nties; i += NT) {
           const uint32_t v = ~sh_tp[i];
           if (vshift >= 32 || (v >> vshift) >= vprefix) {
             const uint32_t s = base + atomicAdd(&sh_var[2], 1u);
-            if (s < (uint32_t)kMaxK) sh_sort[s] = ((uint64_t)sh_tk[i] << 32) | (uint64_t)v;
+            if (s < (uint32_t)CAP) sh_sort[s] = ((uint64_t)sh_tk[i] << 32) | (uint64_t)v;
           }
         }
         __syncthreads();
       } else {
-        sorted_tie_pass(true, rowp, L, vec, prefix, shift, floor, vprefix, vshift, 0, sh_hist, sh_sort, base, sh_var,
+        sorted_tie_pass<NT, CAP>(true, rowp, L, vec, prefix, shift, floor, vprefix, vshift, 0, sh_hist, sh_sort, base, sh_var,
                         tid);
       }
 
@@ -1979,7 +1980,7 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
     while (P < n) P <<= 1;
     for (uint32_t size = 2; size <= P; size <<= 1) {
       for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (uint32_t i = (uint32_t)tid; i < P / 2; i += kThreads) {
+        for (uint32_t i = (uint32_t)tid; i < P / 2; i += NT) {
           const uint32_t lo = 2 * i - (i & (stride - 1));
           const uint32_t hi = lo + stride;
           const bool desc = (lo & size) == 0;
@@ -2000,7 +2001,7 @@ __global__ void __launch_bounds__(kThreads) sorted_rows_kernel(KernelArgs a) {
       int32_t* o = a.out + row * (int64_t)k;
       int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
       const int32_t* pt = a.page_table + row * a.pages_per_row;
-      for (int j = tid; j < k; j += kThreads) {
+      for (int j = tid; j < k; j += NT) {
         int32_t r = -1, v = -1;
         if ((uint32_t)j < n) {
           const uint32_t p = ~(uint32_t)sh_sort[j];
@@ -2188,14 +2189,27 @@ hipError_t split_stream_occupancy(int variant, int* blocks_per_cu) {
   return occupancy_split_stream_variant(variant, blocks_per_cu);
 }
 
+// The sorted finish's two shapes: rows with k <= kSortSmallK take a 256-thread
+// workgroup with a 512-entry sort buffer (several rows per CU at once), the
+// rest the 1024-thread, 2048-entry one.
 hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL(sorted_rows_kernel, dim3((unsigned)args.slots), dim3(kThreads), 0, stream, args);
+  if (args.k <= kSortSmallK)
+    hipLaunchKernelGGL((sorted_rows_kernel<kSortSmallThreads, kSortSmallK, 2 * kSortSmallK>), dim3((unsigned)args.slots),
+                       dim3(kSortSmallThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((sorted_rows_kernel<kThreads, kMaxK, 2 * kMaxK>), dim3((unsigned)args.slots), dim3(kThreads), 0,
+                       stream, args);
   return hipGetLastError();
 }
 
-hipError_t sorted_occupancy(int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(&sorted_rows_kernel),
-                                                      kThreads, 0);
+hipError_t sorted_occupancy(int k, int* blocks_per_cu) {
+  if (k <= kSortSmallK)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu,
+        reinterpret_cast<const void*>(&sorted_rows_kernel<kSortSmallThreads, kSortSmallK, 2 * kSortSmallK>),
+        kSortSmallThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks_per_cu, reinterpret_cast<const void*>(&sorted_rows_kernel<kThreads, kMaxK, 2 * kMaxK>), kThreads, 0);
 }
 
 int stream_variant_threads(int variant) {

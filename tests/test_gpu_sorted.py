@@ -77,7 +77,7 @@ def test_sorted_every_path(lib, path, ept, wgs, shape, kind):
     orders -0 before +0, "wide" mixes subnormals and infinities."""
     W = {"stream": 50001, "sstream": 90001}.get(path, 3 * 4096 + 123)
     seq = [W, W - 1, W // 3, 2049, 5000, 0, 513, -2]
-    for k in (1, 700, 2048):
+    for k in (1, 512, 700, 2048):   # 512: the largest k of the small finish shape
         w = workloads.custom(300 + ept + wgs + k, len(seq), W, k, 16, seq_lens=seq, kind=kind, table="perm")
         note(f"sorted path={path} ept={ept} wgs={wgs} shape={shape} kind={kind} k={k}")
         if path == "sstream":
