@@ -136,10 +136,13 @@ topk_status_t topk_transform(const float* scores, const int32_t* seq_lens, const
  * Cost: the row is selected as by topk_transform; then the selected
  * positions' scores are gathered (when ties at the threshold value are cut,
  * the row is read once more to take the lowest tied positions), and the n_b
- * chosen pairs are sorted in LDS (a bitonic network).
- * Besides the workspace, one 16-byte record per row is kept per (device,
- * stream) between the two launches; it is allocated on first use (call once
- * outside graph capture), grown on demand, and freed by
+ * chosen pairs are put in order: by one workgroup per row with a bitonic
+ * network in LDS, or, for batches of fewer rows than CUs, by several
+ * workgroups per row that each count, for their share of the pairs, the
+ * larger pairs (topk_set_sorted_finish).
+ * Besides the workspace, one 32-byte record and k raw positions per row are
+ * kept per (device, stream) between the two launches; they are allocated on
+ * first use (call once outside graph capture), grown on demand, and freed by
  * topk_release_workspaces.
  */
 topk_status_t topk_transform_sorted(const float* scores, const int32_t* seq_lens, const int32_t* page_table,
@@ -247,6 +250,22 @@ topk_status_t topk_set_stream_shape(int32_t shape);
  * other values.
  */
 topk_status_t topk_set_split_stream(int32_t shape, int32_t wgs_per_row);
+
+/*
+ * Testing and tuning override of the sorted finish of topk_transform_sorted,
+ * process-wide:
+ *   -1  automatic: the rank finish for batches of fewer rows than CUs, else
+ *       one workgroup per row;
+ *    0  one workgroup per row, persistent over rows: the selected pairs are
+ *       bitonic-sorted in LDS;
+ *    1  the rank finish: G workgroups per row (about two per CU, at least 64
+ *       pairs each) each compute the final slot of their share of the row's
+ *       pairs by counting the larger pairs, bucketed by a data-fitted digit.
+ * Rows whose threshold bin was cut take the one-workgroup path in both
+ * forms.  Both are exact for every input (the output is unique); the choice
+ * only moves time.  Returns TOPK_ERROR_INVALID_VALUE for other values.
+ */
+topk_status_t topk_set_sorted_finish(int32_t mode);
 
 /* Synchronises `stream`, then reports whether a split-row launch queued on
  * it (or, on this device, through topk_transform_noalloc) gave up a bounded

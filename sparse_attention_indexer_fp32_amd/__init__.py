@@ -25,6 +25,7 @@ TOPK_ERROR_DEVICE_FAULT = 5
 
 EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_transform_noalloc", "topk_init", "topk_status_string", "topk_last_error", "topk_last_launch",
             "topk_release_workspaces", "topk_set_dispatch_override", "topk_set_stream_shape", "topk_set_split_stream",
+            "topk_set_sorted_finish",
             "topk_check_faults", "topk_set_wait_limit", "topk_set_scratch_limit", "topk_abi_version",
             "indexer_logits", "indexer_topk",
             "indexer_set_window_override")
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.topk_set_dispatch_override.restype = ctypes.c_int
     lib.topk_set_stream_shape.argtypes = [c_i32]
     lib.topk_set_stream_shape.restype = ctypes.c_int
+    lib.topk_set_sorted_finish.argtypes = [c_i32]
+    lib.topk_set_sorted_finish.restype = ctypes.c_int
     lib.topk_set_split_stream.argtypes = [c_i32, c_i32]
     lib.topk_set_split_stream.restype = ctypes.c_int
     lib.topk_check_faults.argtypes = [c_vp]
@@ -204,6 +207,12 @@ def topk_set_split_stream(shape: int = -1, wgs_per_row: int = 0) -> None:
 
 def topk_set_stream_shape(shape: int = -1) -> None:
     _check(load().topk_set_stream_shape(int(shape)))
+
+
+def topk_set_sorted_finish(mode: int = -1) -> None:
+    """Testing/tuning override of the sorted finish: -1 automatic, 0 one
+    workgroup per row (LDS bitonic sort), 1 rank finish (G workgroups per row)."""
+    _check(load().topk_set_sorted_finish(int(mode)))
 
 
 def topk_check_faults(stream=None) -> None:

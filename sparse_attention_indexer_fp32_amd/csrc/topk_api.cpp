@@ -77,6 +77,7 @@ int g_override_ept = 0;
 int g_override_wgs = 0;
 int g_stream_variant = -1;   // -1: the default streaming shape
 int g_ss_variant = -1;       // split streaming override: -1 automatic, else the shape forced
+int g_sorted_finish = -1;    // sorted finish override: -1 automatic, 0 one workgroup per row, 1 rank finish
 int g_ss_wgs = 0;            // ... with this many workgroups per row
 uint32_t g_spin_limit = topk::kDefaultSpinLimit;
 size_t g_scratch_limit = 0;  // words of the static scratch the no-allocation entry point may use; 0: all
@@ -524,12 +525,14 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   a.fault_host = nullptr;
   a.spread = plan.kind == Kind::kSplitStream && plan.ss_spread ? info->cus : 0;
   if (sorted) {
-    // the selection launch always writes raw positions: the caller's out_raw,
-    // else a scratch area after the records
+    // the selection launch writes its raw positions to a scratch area after
+    // the records, never to the caller's out_raw: the rank finish's
+    // workgroups read a row's positions while others of the row write its
+    // output
     const int64_t rec = (int64_t)batch * (int64_t)topk::kMetaWords;
-    st = get_meta(dev, stream, rec + (out_raw ? 0 : (int64_t)batch * k), &a.meta);
+    st = get_meta(dev, stream, rec + (int64_t)batch * k, &a.meta);
     if (st != TOPK_SUCCESS) return st;
-    if (!out_raw) a.out_raw = reinterpret_cast<int32_t*>(a.meta + rec);
+    a.out_raw = reinterpret_cast<int32_t*>(a.meta + rec);
     a.sel = a.out_raw;
   }
   if (plan.kind == Kind::kSplit || plan.kind == Kind::kSplitStream ||
@@ -575,26 +578,45 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   else
     e = topk::launch_rows(plan.ept_idx, plan.kind == Kind::kSplit, a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  int64_t sorted_slots = 0;
+  int64_t sorted_slots = 0, sorted_g = 0;
   if (sorted) {
     // the finish reads every row's record once the selection launch is done (stream order)
     topk::KernelArgs f = a;
     f.out_raw = out_raw;   // the caller's (or none); f.sel holds the selection launch's positions
-    sorted_slots = (int64_t)(k <= topk::kSortSmallK ? info->sorted_occ_small : info->sorted_occ) * info->cus;
-    if (sorted_slots > batch) sorted_slots = batch;
-    if (sorted_slots < 1) sorted_slots = 1;
-    f.slots = (int32_t)sorted_slots;
-    f.wgs_per_row = 1;
-    e = topk::launch_sorted_rows(f, stream);
+    // the rank finish, G workgroups per row (at least 64 pairs each; about
+    // two 256-thread workgroups per CU for k <= 512, one 1024-thread
+    // workgroup per CU above, the most MI355X holds at once of that shape),
+    // unless the one-workgroup-per-row finish is forced
+    const bool rank = g_sorted_finish != 0;
+    if (rank) {
+      int64_t G = (k <= topk::kSortSmallK ? 2 : 1) * (int64_t)info->cus / batch;
+      if (G > k / 64) G = k / 64;
+      if (G < 1) G = 1;
+      sorted_g = G;
+      f.slots = batch;
+      f.wgs_per_row = (int32_t)G;
+      e = topk::launch_sorted_rank(f, stream);
+    } else {
+      sorted_slots = (int64_t)(k <= topk::kSortSmallK ? info->sorted_occ_small : info->sorted_occ) * info->cus;
+      if (sorted_slots > batch) sorted_slots = batch;
+      if (sorted_slots < 1) sorted_slots = 1;
+      f.slots = (int32_t)sorted_slots;
+      f.wgs_per_row = 1;
+      e = topk::launch_sorted_rows(f, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "sorted finish launch");
   }
-  char buf[200];
+  char sorted_note[64] = "";
+  if (sorted)
+    std::snprintf(sorted_note, sizeof(sorted_note), sorted_g > 0 ? " + sorted-finish rank G=%lld" : " + sorted-finish rows",
+                  (long long)sorted_g);
+  char buf[240];
   std::snprintf(buf, sizeof(buf), "%s%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s",
                 kind_name(plan.kind), plan.ss_spread ? " length-aware" : "",
                 plan.kind == Kind::kStream || plan.kind == Kind::kSplitStream ? 0 : topk::kEptValues[plan.ept_idx],
                 (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G),
                 plan.kind == Kind::kStream ? topk::stream_variant_threads(plan.stream_variant) : topk::kThreads, a.vec,
-                sorted ? " + sorted-finish" : "", noalloc ? " (static scratch)" : "");
+                sorted_note, noalloc ? " (static scratch)" : "");
   t_last_launch = buf;
   return TOPK_SUCCESS;
 }
@@ -725,6 +747,13 @@ topk_status_t topk_set_stream_shape(int32_t shape) {
   return TOPK_SUCCESS;
 }
 
+topk_status_t topk_set_sorted_finish(int32_t mode) {
+  if (mode < -1 || mode > 1) return fail(TOPK_ERROR_INVALID_VALUE, "mode must be -1 (automatic), 0 or 1");
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_sorted_finish = mode;
+  return TOPK_SUCCESS;
+}
+
 topk_status_t topk_check_faults(hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -764,6 +793,6 @@ topk_status_t topk_set_scratch_limit(uint64_t words) {
   return TOPK_SUCCESS;
 }
 
-int32_t topk_abi_version(void) { return 3; }
+int32_t topk_abi_version(void) { return 4; }
 
 }  // extern "C"

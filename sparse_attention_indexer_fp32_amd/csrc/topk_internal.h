@@ -157,6 +157,11 @@ hipError_t split_stream_occupancy(int variant, int* blocks_per_cu);
 // shape depends on k (kSortSmallK); sorted_occupancy reports the one for k.
 hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream);
 hipError_t sorted_occupancy(int k, int* blocks_per_cu);
+// Rank finish (small batches): wgs_per_row workgroups per row, grid = batch *
+// wgs_per_row, no synchronisation among them; each ranks its share of the
+// row's selected pairs (rows whose bin was cut are finished by their first
+// workgroup as in launch_sorted_rows).
+hipError_t launch_sorted_rank(const KernelArgs& args, hipStream_t stream);
 
 // The library's static device scratch: the workspace of the entry point that
 // allocates nothing (topk_transform_noalloc).  One copy per device, 24 MiB,

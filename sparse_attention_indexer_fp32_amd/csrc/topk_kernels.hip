@@ -1820,7 +1820,11 @@ split_stream_kernel(KernelArgs a) {
 // members than the tie list holds, the same select runs over the row in
 // memory.  The n chosen (key, ~position) pairs are then bitonic-sorted in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kSortCV = 4;   // float4 groups per thread per streamed chunk
+// float4 groups per thread per streamed chunk: 64 KB of the row per chunk for
+// 512 threads and more; 16 KB for the 256-thread shape, whose registers set
+// how many workgroups a CU holds
+template <int NT>
+constexpr int sort_cv() { return NT >= 512 ? 4096 / NT : 4; }
 
 // One pass over the row for the memory fallback of the tie select: with
 // `collect` false, histograms the digit of v = ~position at dshift (12 bits
@@ -1832,12 +1836,12 @@ __device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp,
                                                 uint32_t prefix, int shift, uint32_t floor, uint32_t vprefix,
                                                 int vshift, int dshift, uint32_t* sh_hist, uint64_t* sh_sort,
                                                 uint32_t base, uint32_t* sh_var, int tid) {
-  constexpr uint32_t span = (uint32_t)NT * 4u * kSortCV;
+  constexpr uint32_t span = (uint32_t)NT * 4u * sort_cv<NT>();
   for (uint32_t c = 0; c < L; c += span) {
-    uint32_t raw[4 * kSortCV];
-    load_raw<NT, kSortCV, kLoadReuse>(raw, rowp, c, L, vec, tid);
+    uint32_t raw[4 * sort_cv<NT>()];
+    load_raw<NT, sort_cv<NT>(), kLoadReuse>(raw, rowp, c, L, vec, tid);
 #pragma unroll
-    for (int j = 0; j < 4 * kSortCV; ++j) {
+    for (int j = 0; j < 4 * sort_cv<NT>(); ++j) {
       const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (NT * 4) + (uint32_t)(j & 3);
       if (pos >= L) continue;
       const uint32_t x = order_key_bits(raw[j]);
@@ -1855,19 +1859,17 @@ __device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp,
   __syncthreads();
 }
 
+// The sorted finish of one row by one NT-thread workgroup (contains barriers:
+// call uniformly).  sh_sort holds CAP pairs, sh_tk / sh_tp TIES entries each,
+// sh_hist kBinsWide words.
 template <int NT, int CAP, int TIES>
-__global__ void __launch_bounds__(NT) sorted_rows_kernel(KernelArgs a) {
-  __shared__ uint64_t sh_sort[CAP];    // (key << 32) | ~position of the selected
-  __shared__ uint32_t sh_tk[TIES];     // threshold-bin members: key
-  __shared__ uint32_t sh_tp[TIES];     //                        position
-  __shared__ uint32_t sh_hist[kBinsWide];
-  __shared__ uint32_t sh_scan[64];
-  __shared__ uint32_t sh_var[16];
-  constexpr uint32_t span = (uint32_t)NT * 4u * kSortCV;
+__device__ void sorted_row(const KernelArgs& a, int64_t row, uint64_t* sh_sort, uint32_t* sh_tk, uint32_t* sh_tp,
+                           uint32_t* sh_hist, uint32_t* sh_scan, uint32_t* sh_var) {
+  constexpr uint32_t span = (uint32_t)NT * 4u * sort_cv<NT>();
   const int64_t W = a.width;
   const int k = a.k;
   const bool vec = a.vec != 0;
-  for (int64_t row = blockIdx.x; row < a.batch; row += gridDim.x) {
+  {
     const int tid = opaque_tid();
     const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
     const uint32_t L = sl < 0 ? 0u : ((int64_t)sl > W ? (uint32_t)W : (uint32_t)sl);
@@ -1895,10 +1897,10 @@ __global__ void __launch_bounds__(NT) sorted_rows_kernel(KernelArgs a) {
     } else {
       // 1. keys above the bin -> sh_sort; the bin's members -> tie list
       for (uint32_t c = 0; c < L; c += span) {
-        uint32_t raw[4 * kSortCV];
-        load_raw<NT, kSortCV, kLoadReuse>(raw, rowp, c, L, vec, tid);
+        uint32_t raw[4 * sort_cv<NT>()];
+        load_raw<NT, sort_cv<NT>(), kLoadReuse>(raw, rowp, c, L, vec, tid);
 #pragma unroll
-        for (int j = 0; j < 4 * kSortCV; ++j) {
+        for (int j = 0; j < 4 * sort_cv<NT>(); ++j) {
           const uint32_t pos = c + (uint32_t)tid * 4u + (uint32_t)(j >> 2) * (NT * 4) + (uint32_t)(j & 3);
           if (pos >= L) continue;
           const uint32_t x = order_key_bits(raw[j]);
@@ -2017,6 +2019,183 @@ __global__ void __launch_bounds__(NT) sorted_rows_kernel(KernelArgs a) {
     }
     __syncthreads();
   }
+}
+
+template <int NT, int CAP, int TIES>
+__global__ void __launch_bounds__(NT) sorted_rows_kernel(KernelArgs a) {
+  __shared__ uint64_t sh_sort[CAP];    // (key << 32) | ~position of the selected
+  __shared__ uint32_t sh_tk[TIES];     // threshold-bin members: key
+  __shared__ uint32_t sh_tp[TIES];     //                        position
+  __shared__ uint32_t sh_hist[kBinsWide];
+  __shared__ uint32_t sh_scan[64];
+  __shared__ uint32_t sh_var[16];
+  for (int64_t row = blockIdx.x; row < a.batch; row += gridDim.x)
+    sorted_row<NT, CAP, TIES>(a, row, sh_sort, sh_tk, sh_tp, sh_hist, sh_scan, sh_var);
+}
+
+// Rank finish: the sorted finish for batches too small to fill the device one
+// row per workgroup.  G = a.wgs_per_row workgroups share a row (grid = batch
+// x G) and need no synchronisation among them.  Where the record says the bin
+// was not cut, the selected set is canonical and only its order is missing:
+// each workgroup gathers all n pairs P = (key << 32) | ~position (distinct,
+// since positions are) and computes, for its own n/G of them, the rank
+// #{P' > P}, the slot the pair takes in the plain definition's order.  To
+// compare fewer pairs than all n, the pairs are first grouped into NB
+// buckets by (P - Pmin) >> s, s chosen so that the row's span Pmax - Pmin
+// fills the NB buckets (a monotone map: the buckets are ranges of P).  A
+// pair's rank is then the number of pairs in higher buckets plus a count over
+// its own bucket only.
+// Rows whose bin was cut need the row read again: workgroup 0 of the row runs
+// the one-workgroup finish, the others leave.
+template <int NT, int CAP, int TIES, int NB>
+__global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
+  constexpr int kDigit = NB == 4096 ? 12 : (NB == 2048 ? 11 : (NB == 1024 ? 10 : -1));
+  static_assert(kDigit > 0 && NB % NT == 0 && NB <= kBinsWide && 2 * CAP + NB <= 2 * TIES, "rank finish shape");
+  __shared__ uint64_t sh_sort[CAP];
+  __shared__ uint32_t sh_t[2 * TIES];   // cut rows: the tie list's keys, then positions
+  __shared__ uint32_t sh_hist[kBinsWide];
+  __shared__ uint32_t sh_scan[64];
+  __shared__ uint32_t sh_var[16];
+  __shared__ uint64_t sh_mm[2];
+  // workgroup-major over rows: the rows' first workgroups (which alone finish
+  // cut rows) are dispatched first and spread over the XCDs, and when the
+  // batch is a multiple of 8 a row's workgroups share one XCD (and its L2,
+  // for the gather of the row's keys)
+  const int G = a.wgs_per_row;
+  const int64_t row = (int64_t)(blockIdx.x % (uint32_t)a.batch);
+  const uint32_t g = blockIdx.x / (uint32_t)a.batch;
+  if (g >= (uint32_t)G) return;
+  if (uniform(a.meta[row * kMetaWords + 4]) != 0u) {   // cut
+    if (g == 0) sorted_row<NT, CAP, TIES>(a, row, sh_sort, sh_t, sh_t + TIES, sh_hist, sh_scan, sh_var);
+    return;
+  }
+  const int tid = opaque_tid();
+  const int64_t W = a.width;
+  const int k = a.k;
+  const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+  const uint32_t L = sl < 0 ? 0u : ((int64_t)sl > W ? (uint32_t)W : (uint32_t)sl);
+  const uint32_t n = L < (uint32_t)k ? L : (uint32_t)k;
+  const float* rowp = a.scores + row * W;
+  const int32_t* sel = a.sel + row * (int64_t)k;
+  uint64_t* const sh_a = sh_sort;                                // the pairs in the selection's order
+  uint64_t* const sh_b = reinterpret_cast<uint64_t*>(sh_t);      // the pairs grouped by bucket
+  uint32_t* const sh_beg = sh_t + 2 * CAP;                       // bucket b's first slot in sh_b
+  uint32_t* const sh_cnt = sh_hist;                              // bucket b's pair count
+
+  // 1. the pairs, and the largest and smallest of them
+  for (int b = tid; b < NB; b += NT) sh_cnt[b] = 0;
+  if (tid == 0) {
+    sh_mm[0] = 0ull;
+    sh_mm[1] = ~0ull;
+  }
+  __syncthreads();
+  uint64_t hi = 0ull, lo = ~0ull;
+  for (uint32_t j = (uint32_t)tid; j < n; j += NT) {
+    const int32_t p = sel[j];
+    // a slot left without a position (none is, for valid input) sorts after every
+    // key and is written as -1; j keeps such pairs distinct
+    uint64_t P = (uint64_t)j;
+    if (p >= 0 && (uint32_t)p < L) P = ((uint64_t)order_key_bits(__float_as_uint(rowp[p])) << 32) | (uint64_t)(~(uint32_t)p);
+    sh_a[j] = P;
+    hi = P > hi ? P : hi;
+    lo = P < lo ? P : lo;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t h2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(hi >> 32), off, 64) << 32) |
+                        (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)hi, off, 64);
+    const uint64_t l2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(lo >> 32), off, 64) << 32) |
+                        (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)lo, off, 64);
+    hi = h2 > hi ? h2 : hi;
+    lo = l2 < lo ? l2 : lo;
+  }
+  if ((tid & 63) == 0 && lo <= hi) {
+    atomicMax(reinterpret_cast<unsigned long long*>(&sh_mm[0]), (unsigned long long)hi);
+    atomicMin(reinterpret_cast<unsigned long long*>(&sh_mm[1]), (unsigned long long)lo);
+  }
+  __syncthreads();
+
+  // 2. bucket counts
+  const uint64_t pmin = sh_mm[1];
+  const uint64_t range = sh_mm[0] - pmin;
+  const int top = range != 0ull ? 63 - __builtin_clzll(range) : 0;
+  const int bs = top >= kDigit - 1 ? top - (kDigit - 1) : 0;
+  for (uint32_t j = (uint32_t)tid; j < n; j += NT)
+    atomicAdd(&sh_cnt[(uint32_t)((sh_a[j] - pmin) >> bs) & (uint32_t)(NB - 1)], 1u);
+  __syncthreads();
+
+  // 3. first slots, buckets in descending order: thread t owns buckets
+  // NB-1-(NB/NT)t down to NB-(NB/NT)(t+1)
+  {
+    constexpr int kPer = NB / NT;
+    uint32_t c[kPer], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      c[i] = sh_cnt[NB - 1 - kPer * tid - i];
+      sum += c[i];
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<NT>(sum, sh_scan, total, tid);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      sh_beg[NB - 1 - kPer * tid - i] = run;
+      run += c[i];
+    }
+  }
+  __syncthreads();
+
+  // 4. group the pairs by bucket (order within a bucket does not matter); the
+  // cursors end one past each bucket, so the first slots are end - count
+  for (uint32_t j = (uint32_t)tid; j < n; j += NT) {
+    const uint64_t P = sh_a[j];
+    sh_b[atomicAdd(&sh_beg[(uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1)], 1u)] = P;
+  }
+  __syncthreads();
+
+  // 5. ranks of this workgroup's pairs, tpe threads per pair, and the output
+  const uint32_t j0 = (uint32_t)(((uint64_t)g * n) / (uint32_t)G);
+  const uint32_t j1 = (uint32_t)(((uint64_t)(g + 1) * n) / (uint32_t)G);
+  const uint32_t cnt_here = j1 - j0;
+  uint32_t tpe = 64;
+  while (tpe > 1 && tpe * cnt_here > (uint32_t)NT) tpe >>= 1;
+  const uint32_t per = (uint32_t)NT / tpe;
+  const uint32_t q = (uint32_t)tid & (tpe - 1u);
+  const int s = a.log2_page;
+  const uint32_t pmask = (1u << s) - 1u;
+  int32_t* o = a.out + row * (int64_t)k;
+  int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
+  const int32_t* pt = a.page_table + row * a.pages_per_row;
+  for (uint32_t base = 0; base < cnt_here; base += per) {
+    const uint32_t e = j0 + base + (uint32_t)tid / tpe;
+    const bool act = e < j1;
+    uint64_t P = 0ull;
+    uint32_t first = 0, c = 0;
+    if (act) {
+      P = sh_a[e];
+      const uint32_t b = (uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1);
+      const uint32_t end = sh_beg[b];
+      first = end - sh_cnt[b];
+      for (uint32_t i = first + q; i < end; i += tpe) c += sh_b[i] > P ? 1u : 0u;
+    }
+    for (uint32_t off = 1; off < tpe; off <<= 1) c += (uint32_t)__shfl_xor((int)c, (int)off, 64);
+    if (act && q == 0) {
+      const uint32_t r = first + c;
+      const uint32_t p = ~(uint32_t)P;
+      int32_t rv = -1, v = -1;
+      if (p < L) {
+        rv = (int32_t)p;
+        const int64_t pg = (int64_t)(p >> s);
+        if (pg < a.pages_per_row) v = (int32_t)(((uint32_t)pt[pg] << s) | (p & pmask));
+      }
+      o[r] = v;
+      if (orw) orw[r] = rv;
+    }
+  }
+  if (g == 0)
+    for (int j = (int)n + tid; j < k; j += NT) {
+      o[j] = -1;
+      if (orw) orw[j] = -1;
+    }
 }
 
 // Resident workgroups per CU of a kernel's two load forms (the launch picks
@@ -2199,6 +2378,16 @@ hipError_t launch_sorted_rows(const KernelArgs& args, hipStream_t stream) {
   else
     hipLaunchKernelGGL((sorted_rows_kernel<kThreads, kMaxK, 2 * kMaxK>), dim3((unsigned)args.slots), dim3(kThreads), 0,
                        stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_sorted_rank(const KernelArgs& args, hipStream_t stream) {
+  const unsigned grid = (unsigned)((int64_t)args.batch * args.wgs_per_row);
+  if (args.k <= kSortSmallK)
+    hipLaunchKernelGGL((sorted_rank_kernel<kSortSmallThreads, kSortSmallK, 2 * kSortSmallK, 1024>), dim3(grid),
+                       dim3(kSortSmallThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((sorted_rank_kernel<kThreads, kMaxK, 2 * kMaxK, 4096>), dim3(grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert topk.topk_abi_version() == 3
+    assert topk.topk_abi_version() == 4
     for code, name in topk.STATUS.items():
         assert topk.topk_status_string(code) == name
     assert topk.topk_status_string(99) == "TOPK_UNKNOWN_STATUS"
@@ -89,6 +89,15 @@ def test_split_stream_override_validation(lib):
     assert lib.topk_set_split_stream(0, -1) == 1
     assert lib.topk_set_split_stream(-2, 0) == 1
     assert lib.topk_set_split_stream(-1, 0) == 0
+
+
+def test_sorted_finish_override_validation(lib):
+    """-1 (automatic), 0 (one workgroup per row) and 1 (rank finish) only."""
+    for mode in (-1, 0, 1):
+        assert lib.topk_set_sorted_finish(mode) == 0
+    assert lib.topk_set_sorted_finish(2) == 1
+    assert lib.topk_set_sorted_finish(-2) == 1
+    assert lib.topk_set_sorted_finish(-1) == 0
 
 
 def test_wait_limit_setter(lib):

@@ -50,12 +50,33 @@ def test_sorted_configs(lib, name):
     assert np.array_equal(out2, out)
 
 
-def test_sorted_c4a_sampled(lib):
-    note("sorted config c4a")
+@pytest.mark.parametrize("finish", [0, 1])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3_b1", "c4b"])
+def test_sorted_configs_forced_finish(lib, name, finish):
+    """Both finishes on configs the automatic choice gives the other one (or
+    the same one), against the oracle."""
+    note(f"sorted config {name} finish={finish}")
+    w = workloads.make(name)
+    lib.topk_set_sorted_finish(finish)
+    try:
+        out, raw = run_sorted(lib, w, raw=True)
+        note(f"sorted config {name}: {lib.topk_last_launch()}")
+    finally:
+        lib.topk_set_sorted_finish(-1)
+    check_exact(w, out, raw)
+
+
+@pytest.mark.parametrize("finish", [-1, 1])
+def test_sorted_c4a_sampled(lib, finish):
+    note(f"sorted config c4a finish={finish}")
     w = workloads.c4a()
     lib.topk_set_dispatch_override(0, 0)
-    out, raw = run_sorted(lib, w, raw=True)
-    note(f"sorted config c4a: {lib.topk_last_launch()}")
+    lib.topk_set_sorted_finish(finish)
+    try:
+        out, raw = run_sorted(lib, w, raw=True)
+        note(f"sorted config c4a: {lib.topk_last_launch()}")
+    finally:
+        lib.topk_set_sorted_finish(-1)
     rng = np.random.Generator(np.random.PCG64(78))
     rows = sorted(rng.choice(w.batch, size=192, replace=False).tolist())
     check_exact(w, out, raw, rows=rows)
@@ -68,18 +89,21 @@ SORTED_SHAPES = [("stream", 0, 1, 0), ("stream", 0, 1, 1), ("stream", 0, 1, 2), 
                  ("sstream", 0, 2, 1)]
 
 
+@pytest.mark.parametrize("finish", [0, 1])
 @pytest.mark.parametrize("path,ept,wgs,shape", SORTED_SHAPES)
 @pytest.mark.parametrize("kind", ["normal", "ties", "const", "asc", "desc", "neginf", "int", "zeros", "wide"])
-def test_sorted_every_path(lib, path, ept, wgs, shape, kind):
+def test_sorted_every_path(lib, path, ept, wgs, shape, kind, finish):
     """Adversarial kinds drive the streaming kernel through its gate raise,
     overflow and low-count fallbacks, and the finish through its memory tie
     select (constant rows have more tied members than its LDS list); "zeros"
-    orders -0 before +0, "wide" mixes subnormals and infinities."""
+    orders -0 before +0, "wide" mixes subnormals and infinities.  `finish`
+    forces the one-workgroup-per-row finish (0) or the rank finish (1)."""
     W = {"stream": 50001, "sstream": 90001}.get(path, 3 * 4096 + 123)
     seq = [W, W - 1, W // 3, 2049, 5000, 0, 513, -2]
     for k in (1, 512, 700, 2048):   # 512: the largest k of the small finish shape
         w = workloads.custom(300 + ept + wgs + k, len(seq), W, k, 16, seq_lens=seq, kind=kind, table="perm")
-        note(f"sorted path={path} ept={ept} wgs={wgs} shape={shape} kind={kind} k={k}")
+        note(f"sorted path={path} ept={ept} wgs={wgs} shape={shape} kind={kind} k={k} finish={finish}")
+        lib.topk_set_sorted_finish(finish)
         if path == "sstream":
             lib.topk_set_split_stream(shape, wgs)
         else:
@@ -91,6 +115,7 @@ def test_sorted_every_path(lib, path, ept, wgs, shape, kind):
             lib.topk_set_dispatch_override(0, 0)
             lib.topk_set_stream_shape(-1)
             lib.topk_set_split_stream(-1, 0)
+            lib.topk_set_sorted_finish(-1)
         check_exact(w, out, raw)
 
 
