@@ -521,6 +521,7 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   a.vec = (width % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
   a.meta = nullptr;
   a.sel = nullptr;
+  a.sel_key = nullptr;
   a.spin_limit = g_spin_limit;
   a.fault_host = nullptr;
   a.spread = plan.kind == Kind::kSplitStream && plan.ss_spread ? info->cus : 0;
@@ -530,10 +531,11 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     // workgroups read a row's positions while others of the row write its
     // output
     const int64_t rec = (int64_t)batch * (int64_t)topk::kMetaWords;
-    st = get_meta(dev, stream, rec + (int64_t)batch * k, &a.meta);
+    st = get_meta(dev, stream, rec + 2 * (int64_t)batch * k, &a.meta);
     if (st != TOPK_SUCCESS) return st;
     a.out_raw = reinterpret_cast<int32_t*>(a.meta + rec);
     a.sel = a.out_raw;
+    a.sel_key = a.meta + rec + (int64_t)batch * k;
   }
   if (plan.kind == Kind::kSplit || plan.kind == Kind::kSplitStream ||
       (plan.kind == Kind::kStream && batch > plan.slots)) {

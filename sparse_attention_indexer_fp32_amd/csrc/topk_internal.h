@@ -100,7 +100,8 @@ constexpr size_t kSsPos = kSsKeys + kSsCap;
 constexpr size_t kSsRowWords = kSsPos + kSsCap;
 inline size_t split_stream_words(int64_t batch) { return kHdrWords + (size_t)batch * kSsRowWords; }
 
-// Sorted mode: per-row selection record (prefix, shift, need, floor, cut).
+// Sorted mode: per-row selection record (prefix, shift, need, floor, cut,
+// keys written).
 constexpr size_t kMetaWords = 8;
 
 struct KernelArgs {
@@ -121,6 +122,8 @@ struct KernelArgs {
   int32_t vec;                // rows are 16-byte aligned: use dwordx4 loads
   uint32_t* meta;             // (batch, kMetaWords): how each row's selection ended, for the sorted finish; or nullptr
   const int32_t* sel;         // sorted finish: (batch, k) raw positions the selection launch wrote
+  uint32_t* sel_key;          // sorted mode: (batch, k) order keys of those positions, written where a
+                              // selection has them at hand (the record says so), else nullptr
   uint32_t spin_limit;        // split rows: polls of a barrier wait before it gives up
   uint32_t* fault_host;       // split rows: host-visible copy of the workspace's fault count, or nullptr
   int32_t spread;             // split streaming: 0 = wgs_per_row parts per row; else per-row parts from

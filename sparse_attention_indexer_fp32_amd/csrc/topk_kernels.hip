@@ -370,8 +370,9 @@ __device__ __forceinline__ void write_slot(const KernelArgs& a, int64_t row, uin
 // cut) the selected set is the canonical one, whatever the order.  shift 32
 // with floor 0 and prefix 0 selects every position below the row's length
 // (rows with L <= k).  Called by one thread.
+// `keys`: the row's selected keys were also written to a.sel_key.
 __device__ __forceinline__ void record_selection(const KernelArgs& a, int64_t row, uint32_t prefix, int shift,
-                                                 uint32_t need, uint32_t cnt, uint32_t floor) {
+                                                 uint32_t need, uint32_t cnt, uint32_t floor, bool keys = false) {
   if (a.meta == nullptr) return;
   uint32_t* m = a.meta + row * kMetaWords;
   m[0] = prefix;
@@ -379,6 +380,7 @@ __device__ __forceinline__ void record_selection(const KernelArgs& a, int64_t ro
   m[2] = need;
   m[3] = floor;
   m[4] = cnt != need ? 1u : 0u;
+  m[5] = keys ? 1u : 0u;
 }
 
 // Histogram of one radix digit over the register-resident keys that match the
@@ -452,13 +454,15 @@ __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass
 // them were selected.
 // With `fill`, slots [0, n) of sh_raw are first set to -1 (nothing else
 // has written them yet).  With INDEX the slots receive candidate indices
-// (into sh_ckey / sh_cpos) instead of positions.
+// (into sh_ckey / sh_cpos) instead of positions.  With `key_out` (global
+// memory, the row's k slots) each slot's key is written there too.
 template <int NT, bool INDEX = false>
 __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, int& shift, uint32_t& cnt,
                                                   uint32_t& need, uint32_t gt_base, uint32_t n,
                                                   uint32_t* sh_hist, const uint32_t* sh_ckey,
                                                   const int32_t* sh_cpos, int32_t* sh_raw, uint32_t* sh_scan,
-                                                  uint32_t* sh_var, int tid, bool fill = false) {
+                                                  uint32_t* sh_var, int tid, bool fill = false,
+                                                  uint32_t* key_out = nullptr) {
   while (shift > 0 && cnt != need) {
     for (int b = tid; b < kBinsNarrow; b += NT) sh_hist[b] = 0;
     __syncthreads();
@@ -484,13 +488,20 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, i
     for (uint32_t j = (uint32_t)tid; j < n; j += NT) sh_raw[j] = -1;
   __syncthreads();
   for (int i = tid; i < ncand; i += NT) {
-    const uint32_t x = sh_ckey[i] >> shift;
+    const uint32_t key = sh_ckey[i];
+    const uint32_t x = key >> shift;
     if (x > prefix) {
       const uint32_t s = atomicAdd(&sh_var[8], 1u);
-      if (s < gt_end) sh_raw[s] = INDEX ? i : sh_cpos[i];
-    } else if (x == prefix && sh_ckey[i] != 0u) {
+      if (s < gt_end) {
+        sh_raw[s] = INDEX ? i : sh_cpos[i];
+        if (key_out) key_out[s] = key;
+      }
+    } else if (x == prefix && key != 0u) {
       const uint32_t e = atomicAdd(&sh_var[9], 1u);
-      if (e < need) sh_raw[gt_end + e] = INDEX ? i : sh_cpos[i];
+      if (e < need) {
+        sh_raw[gt_end + e] = INDEX ? i : sh_cpos[i];
+        if (key_out) key_out[gt_end + e] = key;
+      }
     }
   }
   __syncthreads();
@@ -1378,9 +1389,12 @@ stream_rows_kernel(KernelArgs a) {
       // windowed: the threshold's 22-bit prefix, with `above` keys over it
       uint32_t fprefix = windowed ? wbase + t0 : t0, fneed = (uint32_t)n - above - gt0, fcnt = cnt0;
       int fshift = windowed ? 10 : 20;
+      // sorted mode: the selected keys go out with the positions (the sorted
+      // finish then need not gather them from the row)
+      uint32_t* const key_out = a.sel_key ? a.sel_key + row * (int64_t)k : nullptr;
       select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                            sh_raw, sh_scan, sh_var, tid, true);
-      if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, gate);
+                            sh_raw, sh_scan, sh_var, tid, true, key_out);
+      if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, gate, key_out != nullptr);
     } else {
       for (int j = tid; j < k; j += NT) sh_raw[j] = -1;
       __syncthreads();
@@ -2077,6 +2091,8 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
   const uint32_t n = L < (uint32_t)k ? L : (uint32_t)k;
   const float* rowp = a.scores + row * W;
   const int32_t* sel = a.sel + row * (int64_t)k;
+  const uint32_t* skey =
+      a.sel_key != nullptr && uniform(a.meta[row * kMetaWords + 5]) != 0u ? a.sel_key + row * (int64_t)k : nullptr;
   uint64_t* const sh_a = sh_sort;                                // the pairs in the selection's order
   uint64_t* const sh_b = reinterpret_cast<uint64_t*>(sh_t);      // the pairs grouped by bucket
   uint32_t* const sh_beg = sh_t + 2 * CAP;                       // bucket b's first slot in sh_b
@@ -2095,7 +2111,8 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
     // a slot left without a position (none is, for valid input) sorts after every
     // key and is written as -1; j keeps such pairs distinct
     uint64_t P = (uint64_t)j;
-    if (p >= 0 && (uint32_t)p < L) P = ((uint64_t)order_key_bits(__float_as_uint(rowp[p])) << 32) | (uint64_t)(~(uint32_t)p);
+    if (p >= 0 && (uint32_t)p < L)
+      P = ((uint64_t)(skey ? skey[j] : order_key_bits(__float_as_uint(rowp[p]))) << 32) | (uint64_t)(~(uint32_t)p);
     sh_a[j] = P;
     hi = P > hi ? P : hi;
     lo = P < lo ? P : lo;
