@@ -1873,6 +1873,196 @@ __device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp,
   __syncthreads();
 }
 
+// Sorts a row's pairs sh_sort[0, n) descending with a bitonic network over
+// the next power of two P >= n (sh_sort[n, P) must hold distinct pads below
+// every pair, e.g. their indices), then writes the row's k output slots:
+// slot j < n the position of pair j (-1 if not below L) transformed through
+// the page table, the rest -1.  Contains barriers: call uniformly.
+template <int NT>
+__device__ void bitonic_write(const KernelArgs& a, int64_t row, uint32_t n, uint32_t L, uint64_t* sh_sort, int tid) {
+  const int k = a.k;
+  uint32_t P = 1;
+  while (P < n) P <<= 1;
+  for (uint32_t size = 2; size <= P; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      for (uint32_t i = (uint32_t)tid; i < P / 2; i += NT) {
+        const uint32_t lo = 2 * i - (i & (stride - 1));
+        const uint32_t hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x = sh_sort[lo], y = sh_sort[hi];
+        if ((x < y) == desc) {
+          sh_sort[lo] = y;
+          sh_sort[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int s = a.log2_page;
+  const uint32_t pmask = (1u << s) - 1u;
+  int32_t* o = a.out + row * (int64_t)k;
+  int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
+  const int32_t* pt = a.page_table + row * a.pages_per_row;
+  for (int j = tid; j < k; j += NT) {
+    int32_t r = -1, v = -1;
+    if ((uint32_t)j < n) {
+      const uint32_t p = ~(uint32_t)sh_sort[j];
+      if (p < L) {
+        r = (int32_t)p;
+        const int64_t pg = (int64_t)(p >> s);
+        if (pg < a.pages_per_row) v = (int32_t)(((uint32_t)pt[pg] << s) | (p & pmask));
+      }
+    }
+    o[j] = v;
+    if (orw) orw[j] = r;
+  }
+}
+
+// Prepares rank_pairs_write's inputs for pairs that thread tid saw (hi, lo:
+// the largest and smallest of them; lo > hi if none): sh_mm = {Pmax, Pmin}
+// of the workgroup.  sh_mm must hold {0, ~0} beforehand (pairs_span_init,
+// then a barrier); ends with a barrier.
+__device__ __forceinline__ void pairs_span(uint64_t hi, uint64_t lo, uint64_t* sh_mm, int tid) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t h2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(hi >> 32), off, 64) << 32) |
+                        (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)hi, off, 64);
+    const uint64_t l2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(lo >> 32), off, 64) << 32) |
+                        (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)lo, off, 64);
+    hi = h2 > hi ? h2 : hi;
+    lo = l2 < lo ? l2 : lo;
+  }
+  if ((tid & 63) == 0 && lo <= hi) {
+    atomicMax(reinterpret_cast<unsigned long long*>(&sh_mm[0]), (unsigned long long)hi);
+    atomicMin(reinterpret_cast<unsigned long long*>(&sh_mm[1]), (unsigned long long)lo);
+  }
+  __syncthreads();
+}
+
+// Zeroes rank_pairs_write's bucket counts and resets its span and largest
+// bucket words (a barrier must follow before pairs_span).
+template <int NT, int NB>
+__device__ __forceinline__ void pairs_span_init(uint32_t* sh_cnt, uint64_t* sh_mm, uint32_t* sh_scan, int tid) {
+  for (int b = tid; b < NB; b += NT) sh_cnt[b] = 0;
+  if (tid == 0) {
+    sh_mm[0] = 0ull;
+    sh_mm[1] = ~0ull;
+    sh_scan[48] = 0;   // the largest bucket (a block scan uses sh_scan[0, NT/64])
+  }
+}
+
+// Writes pairs sh_a[j0, j1) of a row's n distinct pairs P = (key << 32) |
+// ~position (sh_a[0, n) filled and visible) to their slots in the canonical
+// order: slot = rank = #{P' > P}, transformed through the page table; a pair
+// whose position is not below L is written as -1.  The pairs are grouped into
+// NB buckets by (P - Pmin) >> s, s chosen so that the row's span Pmax - Pmin
+// fills the buckets (a monotone map: each bucket is a range of P); a rank is
+// then the number of pairs in higher buckets plus a count over the pair's own
+// bucket, split over up to 64 threads per pair.  sh_b holds n pairs, sh_beg
+// and sh_cnt NB words each.  On entry (after a barrier) sh_mm = {Pmax, Pmin},
+// sh_cnt is zero and sh_scan[48] is zero (see pairs_span).  Returns false,
+// having written nothing, when a
+// bucket holds more than kRankMaxBucket pairs (many equal keys: every pair
+// of one key falls in one bucket), which the caller orders otherwise.
+// Contains barriers: call uniformly.
+constexpr uint32_t kRankMaxBucket = 256;
+template <int NT, int NB>
+__device__ bool rank_pairs_write(const KernelArgs& a, int64_t row, uint32_t n, uint32_t L, uint32_t j0, uint32_t j1,
+                                 const uint64_t* sh_a, uint64_t* sh_b, uint32_t* sh_beg, uint32_t* sh_cnt,
+                                 uint64_t* sh_mm, uint32_t* sh_scan, int tid) {
+  constexpr int kDigit = NB == 4096 ? 12 : (NB == 2048 ? 11 : (NB == 1024 ? 10 : -1));
+  static_assert(kDigit > 0 && NB % NT == 0, "rank digit");
+  const int k = a.k;
+  // 2. bucket counts
+  const uint64_t pmin = sh_mm[1];
+  const uint64_t range = sh_mm[0] - pmin;
+  const int top = range != 0ull ? 63 - __builtin_clzll(range) : 0;
+  const int bs = top >= kDigit - 1 ? top - (kDigit - 1) : 0;
+  for (uint32_t j = (uint32_t)tid; j < n; j += NT)
+    atomicAdd(&sh_cnt[(uint32_t)((sh_a[j] - pmin) >> bs) & (uint32_t)(NB - 1)], 1u);
+  __syncthreads();
+
+  // 3. first slots, buckets in descending order: thread t owns buckets
+  // NB-1-(NB/NT)t down to NB-(NB/NT)(t+1)
+  {
+    constexpr int kPer = NB / NT;
+    uint32_t c[kPer], sum = 0, big = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      c[i] = sh_cnt[NB - 1 - kPer * tid - i];
+      sum += c[i];
+      big = c[i] > big ? c[i] : big;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o2 = (uint32_t)__shfl_xor((int)big, off, 64);
+      big = o2 > big ? o2 : big;
+    }
+    if ((tid & 63) == 0) atomicMax(&sh_scan[48], big);
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<NT>(sum, sh_scan, total, tid);   // ends with a barrier
+    if (uniform(sh_scan[48]) > kRankMaxBucket) return false;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      sh_beg[NB - 1 - kPer * tid - i] = run;
+      run += c[i];
+    }
+  }
+  __syncthreads();
+
+  // 4. group the pairs by bucket (order within a bucket does not matter); the
+  // cursors end one past each bucket, so the first slots are end - count
+  for (uint32_t j = (uint32_t)tid; j < n; j += NT) {
+    const uint64_t P = sh_a[j];
+    sh_b[atomicAdd(&sh_beg[(uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1)], 1u)] = P;
+  }
+  __syncthreads();
+
+  // 5. ranks of pairs [j0, j1), tpe threads per pair, and the output
+  const uint32_t cnt_here = j1 - j0;
+  uint32_t tpe = 64;
+  while (tpe > 1 && tpe * cnt_here > (uint32_t)NT) tpe >>= 1;
+  const uint32_t per = (uint32_t)NT / tpe;
+  const uint32_t q = (uint32_t)tid & (tpe - 1u);
+  const int s = a.log2_page;
+  const uint32_t pmask = (1u << s) - 1u;
+  int32_t* o = a.out + row * (int64_t)k;
+  int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
+  const int32_t* pt = a.page_table + row * a.pages_per_row;
+  for (uint32_t base = 0; base < cnt_here; base += per) {
+    const uint32_t e = j0 + base + (uint32_t)tid / tpe;
+    const bool act = e < j1;
+    uint64_t P = 0ull;
+    uint32_t first = 0, c = 0;
+    if (act) {
+      P = sh_a[e];
+      const uint32_t b = (uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1);
+      const uint32_t end = sh_beg[b];
+      first = end - sh_cnt[b];
+      uint32_t i = first + q;
+      for (; i + 3u * tpe < end; i += 4u * tpe) {   // four independent reads in flight
+        const uint64_t b0 = sh_b[i], b1 = sh_b[i + tpe], b2 = sh_b[i + 2u * tpe], b3 = sh_b[i + 3u * tpe];
+        c += (b0 > P ? 1u : 0u) + (b1 > P ? 1u : 0u) + (b2 > P ? 1u : 0u) + (b3 > P ? 1u : 0u);
+      }
+      for (; i < end; i += tpe) c += sh_b[i] > P ? 1u : 0u;
+    }
+    for (uint32_t off = 1; off < tpe; off <<= 1) c += (uint32_t)__shfl_xor((int)c, (int)off, 64);
+    if (act && q == 0) {
+      const uint32_t r = first + c;
+      const uint32_t p = ~(uint32_t)P;
+      int32_t rv = -1, v = -1;
+      if (p < L) {
+        rv = (int32_t)p;
+        const int64_t pg = (int64_t)(p >> s);
+        if (pg < a.pages_per_row) v = (int32_t)(((uint32_t)pt[pg] << s) | (p & pmask));
+      }
+      o[r] = v;
+      if (orw) orw[r] = rv;
+    }
+  }
+  return true;
+}
+
 // The sorted finish of one row by one NT-thread workgroup (contains barriers:
 // call uniformly).  sh_sort holds CAP pairs, sh_tk / sh_tp TIES entries each,
 // sh_hist kBinsWide words.
@@ -1896,7 +2086,7 @@ __device__ void sorted_row(const KernelArgs& a, int64_t row, uint64_t* sh_sort, 
     const bool cut = uniform(m[4]) != 0u;
     const float* rowp = a.scores + row * W;
     if (tid < 16) sh_var[tid] = 0;
-    for (int i = tid; i < CAP; i += NT) sh_sort[i] = 0ull;   // unfilled slots read as no position
+    for (int i = tid; i < CAP; i += NT) sh_sort[i] = (uint64_t)i;   // unfilled slots: no position, distinct
     __syncthreads();
     if (!cut) {
       const int32_t* sel = a.sel + row * (int64_t)k;
@@ -1991,46 +2181,9 @@ __device__ void sorted_row(const KernelArgs& a, int64_t row, uint64_t* sh_sort, 
 
     }
 
-    // 4. bitonic sort, descending, over the next power of two >= n (pads are 0)
-    uint32_t P = 1;
-    while (P < n) P <<= 1;
-    for (uint32_t size = 2; size <= P; size <<= 1) {
-      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (uint32_t i = (uint32_t)tid; i < P / 2; i += NT) {
-          const uint32_t lo = 2 * i - (i & (stride - 1));
-          const uint32_t hi = lo + stride;
-          const bool desc = (lo & size) == 0;
-          const uint64_t x = sh_sort[lo], y = sh_sort[hi];
-          if ((x < y) == desc) {
-            sh_sort[lo] = y;
-            sh_sort[hi] = x;
-          }
-        }
-        __syncthreads();
-      }
-    }
 
-    // 5. output, transformed through the page table
-    {
-      const int s = a.log2_page;
-      const uint32_t pmask = (1u << s) - 1u;
-      int32_t* o = a.out + row * (int64_t)k;
-      int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
-      const int32_t* pt = a.page_table + row * a.pages_per_row;
-      for (int j = tid; j < k; j += NT) {
-        int32_t r = -1, v = -1;
-        if ((uint32_t)j < n) {
-          const uint32_t p = ~(uint32_t)sh_sort[j];
-          if (p < L) {
-            r = (int32_t)p;
-            const int64_t pg = (int64_t)(p >> s);
-            if (pg < a.pages_per_row) v = (int32_t)(((uint32_t)pt[pg] << s) | (p & pmask));
-          }
-        }
-        o[j] = v;
-        if (orw) orw[j] = r;
-      }
-    }
+    // 4-5. bitonic sort and output
+    bitonic_write<NT>(a, row, n, L, sh_sort, tid);
     __syncthreads();
   }
 }
@@ -2047,24 +2200,18 @@ __global__ void __launch_bounds__(NT) sorted_rows_kernel(KernelArgs a) {
     sorted_row<NT, CAP, TIES>(a, row, sh_sort, sh_tk, sh_tp, sh_hist, sh_scan, sh_var);
 }
 
-// Rank finish: the sorted finish for batches too small to fill the device one
-// row per workgroup.  G = a.wgs_per_row workgroups share a row (grid = batch
-// x G) and need no synchronisation among them.  Where the record says the bin
-// was not cut, the selected set is canonical and only its order is missing:
-// each workgroup gathers all n pairs P = (key << 32) | ~position (distinct,
-// since positions are) and computes, for its own n/G of them, the rank
-// #{P' > P}, the slot the pair takes in the plain definition's order.  To
-// compare fewer pairs than all n, the pairs are first grouped into NB
-// buckets by (P - Pmin) >> s, s chosen so that the row's span Pmax - Pmin
-// fills the NB buckets (a monotone map: the buckets are ranges of P).  A
-// pair's rank is then the number of pairs in higher buckets plus a count over
-// its own bucket only.
-// Rows whose bin was cut need the row read again: workgroup 0 of the row runs
-// the one-workgroup finish, the others leave.
+// Rank finish: the default sorted finish.  G = a.wgs_per_row workgroups
+// share a row (grid = batch x G) and need no synchronisation among them.
+// Where the record says the bin was not cut, the selected set is canonical
+// and only its order is missing: each workgroup reads all n pairs P =
+// (key << 32) | ~position (the keys from the selection launch where it wrote
+// them, else gathered from the row) and writes its own n/G of them to their
+// slots (rank_pairs_write; a row with a crowded bucket is sorted by its first
+// workgroup instead).  Rows whose bin was cut need the row read again: the
+// row's first workgroup runs the one-workgroup finish, and the others leave.
 template <int NT, int CAP, int TIES, int NB>
 __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
-  constexpr int kDigit = NB == 4096 ? 12 : (NB == 2048 ? 11 : (NB == 1024 ? 10 : -1));
-  static_assert(kDigit > 0 && NB % NT == 0 && NB <= kBinsWide && 2 * CAP + NB <= 2 * TIES, "rank finish shape");
+  static_assert(NB <= kBinsWide && 2 * CAP + NB <= 2 * TIES, "rank finish shape");
   __shared__ uint64_t sh_sort[CAP];
   __shared__ uint32_t sh_t[2 * TIES];   // cut rows: the tie list's keys, then positions
   __shared__ uint32_t sh_hist[kBinsWide];
@@ -2093,17 +2240,8 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
   const int32_t* sel = a.sel + row * (int64_t)k;
   const uint32_t* skey =
       a.sel_key != nullptr && uniform(a.meta[row * kMetaWords + 5]) != 0u ? a.sel_key + row * (int64_t)k : nullptr;
-  uint64_t* const sh_a = sh_sort;                                // the pairs in the selection's order
-  uint64_t* const sh_b = reinterpret_cast<uint64_t*>(sh_t);      // the pairs grouped by bucket
-  uint32_t* const sh_beg = sh_t + 2 * CAP;                       // bucket b's first slot in sh_b
-  uint32_t* const sh_cnt = sh_hist;                              // bucket b's pair count
-
-  // 1. the pairs, and the largest and smallest of them
-  for (int b = tid; b < NB; b += NT) sh_cnt[b] = 0;
-  if (tid == 0) {
-    sh_mm[0] = 0ull;
-    sh_mm[1] = ~0ull;
-  }
+  uint32_t* const sh_cnt = sh_hist;
+  pairs_span_init<NT, NB>(sh_cnt, sh_mm, sh_scan, tid);
   __syncthreads();
   uint64_t hi = 0ull, lo = ~0ull;
   for (uint32_t j = (uint32_t)tid; j < n; j += NT) {
@@ -2113,106 +2251,31 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
     uint64_t P = (uint64_t)j;
     if (p >= 0 && (uint32_t)p < L)
       P = ((uint64_t)(skey ? skey[j] : order_key_bits(__float_as_uint(rowp[p]))) << 32) | (uint64_t)(~(uint32_t)p);
-    sh_a[j] = P;
+    sh_sort[j] = P;
     hi = P > hi ? P : hi;
     lo = P < lo ? P : lo;
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t h2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(hi >> 32), off, 64) << 32) |
-                        (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)hi, off, 64);
-    const uint64_t l2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(lo >> 32), off, 64) << 32) |
-                        (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)lo, off, 64);
-    hi = h2 > hi ? h2 : hi;
-    lo = l2 < lo ? l2 : lo;
-  }
-  if ((tid & 63) == 0 && lo <= hi) {
-    atomicMax(reinterpret_cast<unsigned long long*>(&sh_mm[0]), (unsigned long long)hi);
-    atomicMin(reinterpret_cast<unsigned long long*>(&sh_mm[1]), (unsigned long long)lo);
-  }
-  __syncthreads();
-
-  // 2. bucket counts
-  const uint64_t pmin = sh_mm[1];
-  const uint64_t range = sh_mm[0] - pmin;
-  const int top = range != 0ull ? 63 - __builtin_clzll(range) : 0;
-  const int bs = top >= kDigit - 1 ? top - (kDigit - 1) : 0;
-  for (uint32_t j = (uint32_t)tid; j < n; j += NT)
-    atomicAdd(&sh_cnt[(uint32_t)((sh_a[j] - pmin) >> bs) & (uint32_t)(NB - 1)], 1u);
-  __syncthreads();
-
-  // 3. first slots, buckets in descending order: thread t owns buckets
-  // NB-1-(NB/NT)t down to NB-(NB/NT)(t+1)
-  {
-    constexpr int kPer = NB / NT;
-    uint32_t c[kPer], sum = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      c[i] = sh_cnt[NB - 1 - kPer * tid - i];
-      sum += c[i];
-    }
-    uint32_t total;
-    uint32_t run = block_exclusive_scan<NT>(sum, sh_scan, total, tid);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      sh_beg[NB - 1 - kPer * tid - i] = run;
-      run += c[i];
-    }
-  }
-  __syncthreads();
-
-  // 4. group the pairs by bucket (order within a bucket does not matter); the
-  // cursors end one past each bucket, so the first slots are end - count
-  for (uint32_t j = (uint32_t)tid; j < n; j += NT) {
-    const uint64_t P = sh_a[j];
-    sh_b[atomicAdd(&sh_beg[(uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1)], 1u)] = P;
-  }
-  __syncthreads();
-
-  // 5. ranks of this workgroup's pairs, tpe threads per pair, and the output
+  pairs_span(hi, lo, sh_mm, tid);
   const uint32_t j0 = (uint32_t)(((uint64_t)g * n) / (uint32_t)G);
   const uint32_t j1 = (uint32_t)(((uint64_t)(g + 1) * n) / (uint32_t)G);
-  const uint32_t cnt_here = j1 - j0;
-  uint32_t tpe = 64;
-  while (tpe > 1 && tpe * cnt_here > (uint32_t)NT) tpe >>= 1;
-  const uint32_t per = (uint32_t)NT / tpe;
-  const uint32_t q = (uint32_t)tid & (tpe - 1u);
-  const int s = a.log2_page;
-  const uint32_t pmask = (1u << s) - 1u;
-  int32_t* o = a.out + row * (int64_t)k;
-  int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
-  const int32_t* pt = a.page_table + row * a.pages_per_row;
-  for (uint32_t base = 0; base < cnt_here; base += per) {
-    const uint32_t e = j0 + base + (uint32_t)tid / tpe;
-    const bool act = e < j1;
-    uint64_t P = 0ull;
-    uint32_t first = 0, c = 0;
-    if (act) {
-      P = sh_a[e];
-      const uint32_t b = (uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1);
-      const uint32_t end = sh_beg[b];
-      first = end - sh_cnt[b];
-      for (uint32_t i = first + q; i < end; i += tpe) c += sh_b[i] > P ? 1u : 0u;
+  if (!rank_pairs_write<NT, NB>(a, row, n, L, j0, j1, sh_sort, reinterpret_cast<uint64_t*>(sh_t), sh_t + 2 * CAP,
+                                sh_cnt, sh_mm, sh_scan, tid)) {
+    // a crowded bucket: the row's first workgroup sorts all n pairs instead
+    if (g == 0) {
+      for (uint32_t j = n + (uint32_t)tid; j < (uint32_t)CAP; j += NT) sh_sort[j] = (uint64_t)j;
+      __syncthreads();
+      bitonic_write<NT>(a, row, n, L, sh_sort, tid);
     }
-    for (uint32_t off = 1; off < tpe; off <<= 1) c += (uint32_t)__shfl_xor((int)c, (int)off, 64);
-    if (act && q == 0) {
-      const uint32_t r = first + c;
-      const uint32_t p = ~(uint32_t)P;
-      int32_t rv = -1, v = -1;
-      if (p < L) {
-        rv = (int32_t)p;
-        const int64_t pg = (int64_t)(p >> s);
-        if (pg < a.pages_per_row) v = (int32_t)(((uint32_t)pt[pg] << s) | (p & pmask));
-      }
-      o[r] = v;
-      if (orw) orw[r] = rv;
-    }
+    return;
   }
-  if (g == 0)
+  if (g == 0) {
+    int32_t* o = a.out + row * (int64_t)k;
+    int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
     for (int j = (int)n + tid; j < k; j += NT) {
       o[j] = -1;
       if (orw) orw[j] = -1;
     }
+  }
 }
 
 // Resident workgroups per CU of a kernel's two load forms (the launch picks

@@ -119,6 +119,27 @@ def test_sorted_every_path(lib, path, ept, wgs, shape, kind, finish):
         check_exact(w, out, raw)
 
 
+@pytest.mark.parametrize("finish", [0, 1])
+@pytest.mark.parametrize("k", [512, 2048])
+def test_sorted_crowded_bucket(lib, k, finish):
+    """Short rows (every position selected, so the bin is not cut) holding
+    hundreds of equal keys beside a few larger and smaller ones: the rank
+    finish's span-fitted buckets put each key's pairs in one bucket, and the
+    row is sorted by one workgroup instead.  The last row is long: ties at its
+    threshold cut the bin."""
+    W = 3000
+    seq = [k - 7, k // 2, 300, W]
+    w = workloads.custom(41 + k, len(seq), W, k, 16, seq_lens=seq, kind="crowded", table="perm")
+    note(f"sorted crowded k={k} finish={finish}")
+    lib.topk_set_sorted_finish(finish)
+    try:
+        out, raw = run_sorted(lib, w, raw=True)
+        note(f"sorted crowded: {lib.topk_last_launch()}")
+    finally:
+        lib.topk_set_sorted_finish(-1)
+    check_exact(w, out, raw)
+
+
 def test_sorted_matches_unsorted_set(lib):
     """Same selected set as topk_transform wherever the threshold is not cut
     (distinct scores: the set is unique), in canonical order."""

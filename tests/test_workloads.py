@@ -57,7 +57,7 @@ def test_c5_structure():
 
 
 def test_custom_kinds():
-    for kind in ("normal", "ties", "const", "neginf", "zeros", "asc", "desc", "int", "wide"):
+    for kind in ("normal", "ties", "const", "neginf", "zeros", "asc", "desc", "int", "wide", "crowded"):
         w = workloads.custom(1, 3, 1000, 64, 16, seq_lens=[0, 500, 1000], kind=kind)
         assert w.scores.shape == (3, 1000) and w.page_table.shape == (3, 63)
         assert np.all(np.isposinf(w.scores[1, 500:]))

@@ -270,7 +270,9 @@ def custom(seed: int, batch: int, width: int, k: int, page_size: int,
     (every valid entry equal), "neginf" (every valid entry -inf), "zeros" (a mix
     of +0.0 and -0.0), "asc" / "desc" (strictly increasing / decreasing in the
     position), "int" (small integers, heavy ties), "wide" (log-uniform
-    magnitudes of both signs, including subnormals and +-inf).
+    magnitudes of both signs, including subnormals and +-inf), "crowded"
+    (97 % of entries 1.0, 2 % 4.0, 1 % -2.0: hundreds of equal keys next to a
+    few far larger and smaller ones).
     table: "identity" or "perm".
     """
     rng = _rng(seed)
@@ -299,6 +301,11 @@ def custom(seed: int, batch: int, width: int, k: int, page_size: int,
                                  shape).copy()
     elif kind == "int":
         scores = rng.integers(-3, 4, size=shape).astype(np.float32)
+    elif kind == "crowded":
+        scores = np.ones(shape, dtype=np.float32)
+        r = rng.random(shape)
+        scores[r < 0.02] = np.float32(4.0)
+        scores[(r >= 0.02) & (r < 0.03)] = np.float32(-2.0)
     elif kind == "wide":
         mag = np.exp2(rng.uniform(-149.0, 127.9, size=shape)).astype(np.float32)
         sign = np.where(rng.random(shape) < 0.5, np.float32(-1), np.float32(1))
