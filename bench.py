@@ -34,6 +34,8 @@ shape of LiteTopk PR #32094 (8192 query rows over 262144 keys, H 32, D 128,
 fp8 inputs, top-2048): the fused scoring + exact top-k (indexer_topk) against
 the dense path (indexer_logits, then topk_transform over the dense scores),
 with the scoring kernels' matrix-core throughput against the bf16 dense peak.
+"indexer_short_prefill" does the same on a causal prefill of 1024 query rows
+over 65536 keys, where each row's window is short.
 
 Prints ONE JSON line on stdout.
 """
@@ -260,13 +262,13 @@ def indexer_counters_run(topk) -> int:
     return 0
 
 
-def indexer_leg(topk, steps: int, warmup: int) -> dict:
-    """Fused vs dense indexer scoring + top-k on the prefill shape; HIP-event
+def indexer_leg(topk, steps: int, warmup: int, config: str = "prefill_8192x256k_k2048") -> dict:
+    """Fused vs dense indexer scoring + top-k on a prefill shape; HIP-event
     averages over `steps` calls on the stream the calls are queued on."""
     import numpy as np
     import torch
     from workloads import indexer as wl
-    w = wl.make_config("prefill_8192x256k_k2048")
+    w = wl.make_config(config)
     dev = torch.device("cuda", 0)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     q, wt, kv, sc, ks, ke = t(w.q), t(w.weights), t(w.kv), t(w.kv_scale), t(w.ks), t(w.ke)
@@ -417,6 +419,8 @@ def main() -> int:
             torch.cuda.empty_cache()
 
     indexer = None if args.no_indexer else indexer_leg(topk, steps=5, warmup=2)
+    indexer_short = None if args.no_indexer or args.headline_only else \
+        indexer_leg(topk, steps=10, warmup=3, config="prefill_1024x64k_k2048")
 
     result = {
         "metric": METRIC,
@@ -452,6 +456,8 @@ def main() -> int:
     }
     if indexer is not None:
         result["indexer"] = indexer
+    if indexer_short is not None:
+        result["indexer_short_prefill"] = indexer_short
     if extra:
         result["other_workloads"] = extra
     print(json.dumps(result), flush=True)

@@ -79,12 +79,20 @@ topk_status_t indexer_logits(const uint8_t* q, const float* weights, const uint8
  *              The order within [0, n_r) is unspecified.
  *   stream, num_q, num_kv              as in indexer_logits.
  *
- * Working memory: per (device, stream), candidate lists of
+ * Two internal forms, same result contract.  Where each workgroup's window
+ * of key positions is long against k (window >= 64 k), or the score buffer
+ * would exceed 8 GiB, the fused scan keeps gated candidate lists and the
+ * exact top-k of the candidates runs through topk_transform on the same
+ * stream.  On shorter windows every window keeps a large share of its
+ * positions, and the list work costs more than writing every score: those
+ * calls score densely into a buffer and select from it with topk_transform
+ * (indexer_set_select_mode forces either form).
+ * Working memory: per (device, stream), the fused form's candidate lists of
  * num_q x windows x max(4k, 4096) (score, position) pairs plus num_q x
- * windows x k packed candidates, allocated on first need, grown on demand and
+ * windows x k packed candidates, or the dense form's num_q x num_kv scores
+ * plus num_q x (k + 1) words, allocated on first need, grown on demand and
  * freed by topk_release_workspaces() (the first call that grows it
- * synchronises `stream`).  The exact top-k of the packed candidates runs
- * through topk_transform on the same stream.
+ * synchronises `stream`).
  * Errors: as indexer_logits, plus TOPK_ERROR_INVALID_VALUE for k outside
  * [1, TOPK_MAX_K] and TOPK_ERROR_OUT_OF_MEMORY.
  */
@@ -101,6 +109,16 @@ topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t
  * Returns TOPK_ERROR_INVALID_VALUE for other values.
  */
 topk_status_t indexer_set_window_override(int64_t window);
+
+/*
+ * Testing and tuning override of indexer_topk's internal form, process-wide:
+ * -1 automatic (the default: dense when the window is shorter than 64 k and
+ * the score buffer fits 8 GiB), 0
+ * the fused scan, 1 dense scores + select.  Both give a result that meets
+ * indexer_topk's contract; the choice only moves time and working memory.
+ * Returns TOPK_ERROR_INVALID_VALUE for other values.
+ */
+topk_status_t indexer_set_select_mode(int32_t mode);
 
 #ifdef __cplusplus
 }

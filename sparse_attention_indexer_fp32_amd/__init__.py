@@ -28,7 +28,7 @@ EXPORTED = ("topk_transform", "topk_transform_sorted", "topk_transform_noalloc",
             "topk_set_sorted_finish",
             "topk_check_faults", "topk_set_wait_limit", "topk_set_scratch_limit", "topk_abi_version",
             "indexer_logits", "indexer_topk",
-            "indexer_set_window_override")
+            "indexer_set_window_override", "indexer_set_select_mode")
 INDEXER_HEADS = 32
 INDEXER_HEAD_DIM = 128
 
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.indexer_topk.restype = ctypes.c_int
     lib.indexer_set_window_override.argtypes = [c_i64]
     lib.indexer_set_window_override.restype = ctypes.c_int
+    lib.indexer_set_select_mode.argtypes = [c_i32]
+    lib.indexer_set_select_mode.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -304,3 +306,9 @@ def indexer_topk(q, weights, kv, kv_scale, ks, ke, k: int, out=None, stream=None
 def indexer_set_window_override(window: int = 0) -> None:
     """Key positions per workgroup window (0 = automatic; else a multiple of 64)."""
     _check(load().indexer_set_window_override(int(window)))
+
+
+def indexer_set_select_mode(mode: int = -1) -> None:
+    """Testing/tuning override of indexer_topk's internal form: -1 automatic,
+    0 the fused scan, 1 dense scores into a buffer + select."""
+    _check(load().indexer_set_select_mode(int(mode)))

@@ -29,6 +29,7 @@ std::mutex& g_mu = topk::lib_mutex();   // the library's one lock
 std::map<int, int> g_cus;                                   // device -> CUs (gfx950 only)
 std::map<std::pair<int, hipStream_t>, Buffers> g_bufs;
 int64_t g_window_override = 0;                              // 0: automatic
+int g_select_mode = -1;                                     // indexer_topk: -1 automatic, 0 fused, 1 dense
 
 topk_status_t fail(topk_status_t st, const std::string& msg) {
   topk::set_last_error(msg.c_str());
@@ -199,6 +200,50 @@ topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t
   a.num_kv = num_kv;
   a.k = k;
   plan_windows(num_q, num_kv, cus, &a.nwin, &a.window);
+  // Windows shorter than kDenseWindowRatio x k: every window keeps at least k
+  // of its positions, and the fused scan's list work costs more than writing
+  // every score and selecting from the buffer (MI355X, causal prefills: 16K
+  // windows at k 2048 fused 1.16 ms against dense 0.60 ms; 64K windows at
+  // k 2048 2.64-2.77 against 2.19-2.23 ms; 16K windows at k 512 1.47
+  // against 1.01 ms).  Those calls score densely into a buffer (up to
+  // kDenseMaxBytes) and select from it.  Longer windows (the 262144-key
+  // prefill: 17.3 against 16.9 ms, a 8.6 GB buffer) keep the fused scan.
+  constexpr int64_t kDenseWindowRatio = 64;
+  constexpr double kDenseMaxBytes = 8.0 * (1ull << 30);
+  const bool dense = g_select_mode == 1 ||
+                     (g_select_mode < 0 && (int64_t)k * kDenseWindowRatio > a.window &&
+                      (double)num_q * (double)num_kv * 4.0 <= kDenseMaxBytes);
+  if (dense) {
+    const int64_t width = num_kv;   // score rows' stride: no clamped range is longer
+    const size_t scores = (size_t)num_q * (size_t)width;
+    const size_t bytes = scores * 4 + (size_t)num_q * 4 + (size_t)num_q * (size_t)k * 4 + 256;
+    void* base = nullptr;
+    st = get_buffers(dev, stream, bytes, &base);
+    if (st != TOPK_SUCCESS) return st;
+    char* p = static_cast<char*>(base);
+    float* sc = reinterpret_cast<float*>(p);
+    p += scores * 4;
+    int32_t* len = reinterpret_cast<int32_t*>(p);
+    p += (size_t)num_q * 4;
+    int32_t* rel = reinterpret_cast<int32_t*>(p);
+    a.logits = sc;
+    a.logits_stride = width;
+    hipError_t e = indexer::launch_logits(a, a.nwin, stream);
+    if (e == hipSuccess) e = indexer::launch_row_lengths(a, len, stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer dense launch");
+    // row-relative positions through out_raw (no page table: out_idx gets -1
+    // from the select and is then overwritten with the absolute positions)
+    st = topk::transform_locked(sc, len, nullptr, k, 1, out_idx, rel, stream, num_q, width, 0);
+    if (st != TOPK_SUCCESS) return st;
+    e = indexer::launch_absolute_positions(a, rel, out_idx, stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer position launch");
+    char buf[200];
+    std::snprintf(buf, sizeof(buf), "indexer-topk dense grid=%lldx%d window=%lld + select %s",
+                  (long long)ceil_div(num_q, indexer::rows_per_workgroup()), a.nwin, (long long)a.window,
+                  topk_last_launch());
+    topk::set_last_launch(buf);
+    return TOPK_SUCCESS;
+  }
   // a list never holds more than its window; a capacity below the window
   // leaves room for k entries plus a tile after every trim
   int64_t cap = 4 * (int64_t)k > 4096 ? 4 * (int64_t)k : 4096;
@@ -243,6 +288,13 @@ topk_status_t indexer_topk(const uint8_t* q, const float* weights, const uint8_t
                 (long long)ceil_div(num_q, indexer::rows_per_workgroup()), a.nwin, (long long)a.window, a.cap,
                 a.inplace ? " in-place" : "", topk_last_launch());
   topk::set_last_launch(buf);
+  return TOPK_SUCCESS;
+}
+
+topk_status_t indexer_set_select_mode(int32_t mode) {
+  if (mode < -1 || mode > 1) return fail(TOPK_ERROR_INVALID_VALUE, "mode must be -1 (automatic), 0 or 1");
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_select_mode = mode;
   return TOPK_SUCCESS;
 }
 

@@ -39,6 +39,10 @@ struct ScanArgs {
 
 hipError_t launch_logits(const ScanArgs& a, int nwin, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, int nwin, hipStream_t stream);
+// Dense select of indexer_topk: len[r] = row r's clamped range length; out =
+// rel (num_q x k row-relative positions, -1 padded) + each row's range start.
+hipError_t launch_row_lengths(const ScanArgs& a, int32_t* len, hipStream_t stream);
+hipError_t launch_absolute_positions(const ScanArgs& a, const int32_t* rel, int32_t* out, hipStream_t stream);
 int rows_per_workgroup();
 
 // The indexer's per-(device, stream) buffers: whether any are held, and

@@ -793,6 +793,24 @@ __global__ void zero_counts_kernel(int32_t* p, int64_t n) {
   if (i < n) p[i] = 0;
 }
 
+// Dense select: each row's clamped range length (the select's seq_len) ...
+__global__ void row_lengths_kernel(ScanArgs a, int32_t* len) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < a.num_q) {
+    const RowRange rr = row_range(a, r);
+    len[r] = rr.hi > rr.lo ? (int32_t)(rr.hi - rr.lo) : 0;
+  }
+}
+
+// ... and the select's row-relative positions turned into absolute ones.
+__global__ void absolute_positions_kernel(ScanArgs a, const int32_t* rel, int32_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.num_q * (int64_t)a.k) {
+    const int32_t v = rel[i];
+    out[i] = v >= 0 ? (int32_t)(row_range(a, i / a.k).lo + v) : -1;
+  }
+}
+
 hipError_t launch_logits(const ScanArgs& a, int nwin, hipStream_t stream) {
   const dim3 grid((unsigned)((a.num_q + kRowsPerWg - 1) / kRowsPerWg), (unsigned)nwin);
   hipLaunchKernelGGL(logits_kernel<false>, grid, dim3(kThreads), 0, stream, a);
@@ -808,6 +826,17 @@ hipError_t launch_scan(const ScanArgs& a, int nwin, hipStream_t stream) {
   }
   const dim3 grid((unsigned)((a.num_q + kRowsPerWg - 1) / kRowsPerWg), (unsigned)nwin);
   hipLaunchKernelGGL(logits_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_lengths(const ScanArgs& a, int32_t* len, hipStream_t stream) {
+  hipLaunchKernelGGL(row_lengths_kernel, dim3((unsigned)((a.num_q + 255) / 256)), dim3(256), 0, stream, a, len);
+  return hipGetLastError();
+}
+
+hipError_t launch_absolute_positions(const ScanArgs& a, const int32_t* rel, int32_t* out, hipStream_t stream) {
+  const int64_t n = a.num_q * (int64_t)a.k;
+  hipLaunchKernelGGL(absolute_positions_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a, rel, out);
   return hipGetLastError();
 }
 

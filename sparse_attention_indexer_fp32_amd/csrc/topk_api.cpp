@@ -795,6 +795,6 @@ topk_status_t topk_set_scratch_limit(uint64_t words) {
   return TOPK_SUCCESS;
 }
 
-int32_t topk_abi_version(void) { return 4; }
+int32_t topk_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert topk.topk_abi_version() == 4
+    assert topk.topk_abi_version() == 5
     for code, name in topk.STATUS.items():
         assert topk.topk_status_string(code) == name
     assert topk.topk_status_string(99) == "TOPK_UNKNOWN_STATUS"
@@ -162,6 +162,14 @@ def test_indexer_topk_validation_without_device(lib, k, num_q, num_kv, expect):
 def test_indexer_logits_validation_without_device(lib, num_q, num_kv, stride, expect):
     st = lib.indexer_logits(None, None, None, None, None, None, None, None, num_q, num_kv, stride)
     assert st == expect, topk.topk_last_error()
+
+
+def test_indexer_select_mode_validation(lib):
+    for mode in (-1, 0, 1):
+        assert lib.indexer_set_select_mode(mode) == 0
+    assert lib.indexer_set_select_mode(2) == 1
+    assert lib.indexer_set_select_mode(-2) == 1
+    assert lib.indexer_set_select_mode(-1) == 0
 
 
 def test_indexer_window_override_validation(lib):

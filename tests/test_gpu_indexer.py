@@ -21,6 +21,21 @@ pytestmark = pytest.mark.gpu
 SMALL = ["odd_widths_k512", "short_8x1k_k2048", "flat_8x16k_k2048", "ragged_3req_k2048", "single_32x32k_k512"]
 
 
+class _select_mode:
+    """Forces indexer_topk's select mode for a block: 0 the fused scan, 1 dense
+    scores + select, -1 automatic (the default, restored on exit)."""
+
+    def __init__(self, lib, mode):
+        self.lib, self.mode = lib, mode
+
+    def __enter__(self):
+        self.lib.indexer_set_select_mode(self.mode)
+
+    def __exit__(self, *exc):
+        self.lib.indexer_set_select_mode(-1)
+        return False
+
+
 def _upload(w):
     import torch
     dev = torch.device("cuda", 0)
@@ -146,14 +161,18 @@ def test_logits_narrower_than_rows(lib):
         assert np.all(np.isnan(got[r, n:])), f"row {r}: written past min(length, width)"
 
 
+@pytest.mark.parametrize("mode", [0, 1, -1])
 @pytest.mark.parametrize("name", SMALL)
-def test_indexer_topk_vs_oracle(lib, name):
+def test_indexer_topk_vs_oracle(lib, name, mode):
+    """Each select mode: the fused scan (0), dense scores + select (1) and the
+    automatic choice (-1)."""
     import torch
     w = wl.make_config(name)
-    note(f"indexer_topk {name} num_q={w.num_q} num_kv={w.num_kv} k={w.k}")
+    note(f"indexer_topk {name} num_q={w.num_q} num_kv={w.num_kv} k={w.k} mode={mode}")
     tensors = _upload(w)
     out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
-    lib.indexer_topk(*tensors, w.k, out=out)
+    with _select_mode(lib, mode):
+        lib.indexer_topk(*tensors, w.k, out=out)
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     _check_topk(w, o, range(w.num_q))
@@ -187,7 +206,8 @@ def test_indexer_topk_trims(lib, requests, k, distinct, window):
     tensors = _upload(w)
     out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
     try:
-        lib.indexer_topk(*tensors, w.k, out=out)
+        with _select_mode(lib, 0):   # the fused scan, whatever the window
+            lib.indexer_topk(*tensors, w.k, out=out)
         torch.cuda.synchronize()
     finally:
         lib.indexer_set_window_override(0)
@@ -211,7 +231,8 @@ def test_indexer_topk_narrow_scores(lib, k):
     tensors = _upload(w)
     out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
     try:
-        lib.indexer_topk(*tensors, w.k, out=out)
+        with _select_mode(lib, 0):   # the fused scan, whatever the window
+            lib.indexer_topk(*tensors, w.k, out=out)
         torch.cuda.synchronize()
     finally:
         lib.indexer_set_window_override(0)
@@ -243,7 +264,8 @@ def test_indexer_topk_calibration_overrated(lib, k):
     tensors = _upload(w)
     out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
     try:
-        lib.indexer_topk(*tensors, w.k, out=out)
+        with _select_mode(lib, 0):   # the fused scan, whatever the window
+            lib.indexer_topk(*tensors, w.k, out=out)
         torch.cuda.synchronize()
     finally:
         lib.indexer_set_window_override(0)
@@ -252,16 +274,18 @@ def test_indexer_topk_calibration_overrated(lib, k):
     _check_exact_on_logits(w, o, _logits(lib, w, tensors))
 
 
-def test_indexer_edge_ranges(lib):
+@pytest.mark.parametrize("mode", [0, 1])
+def test_indexer_edge_ranges(lib, mode):
     """Empty, inverted, clamped and shorter-than-k ranges; rows not a multiple of 8."""
     import torch
     w = wl.make([(5, 3000)], 256, seed=7200)
     w.ks = np.array([0, 100, 2000, -50, 2990], np.int32)
     w.ke = np.array([0, 90, 9999, 40, 3000], np.int32)   # empty, inverted, past the end, before 0, 10 positions
-    note("indexer_topk edge ranges")
+    note(f"indexer_topk edge ranges mode={mode}")
     tensors = _upload(w)
     out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
-    lib.indexer_topk(*tensors, w.k, out=out)
+    with _select_mode(lib, mode):
+        lib.indexer_topk(*tensors, w.k, out=out)
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     assert np.all(o[0] == -1) and np.all(o[1] == -1)
@@ -269,15 +293,18 @@ def test_indexer_edge_ranges(lib):
     _check_logits(w, _logits(lib, w, tensors), range(w.num_q))
 
 
-def test_indexer_repeat_calls_and_smaller_input(lib):
-    """A second call on a smaller batch reuses the buffers and clears its counters."""
+@pytest.mark.parametrize("modes", [(0, 0), (1, 1), (1, 0), (0, 1)])
+def test_indexer_repeat_calls_and_smaller_input(lib, modes):
+    """A second call on a smaller batch reuses the buffers and clears its
+    counters, in either select mode after either."""
     import torch
-    for reqs in ([(24, 20000)], [(6, 5000)]):
+    for reqs, mode in zip(([(24, 20000)], [(6, 5000)]), modes):
         w = wl.make(reqs, 512, seed=7300 + reqs[0][0])
-        note(f"indexer_topk repeat {reqs}")
+        note(f"indexer_topk repeat {reqs} mode={mode}")
         tensors = _upload(w)
         out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
-        lib.indexer_topk(*tensors, w.k, out=out)
+        with _select_mode(lib, mode):
+            lib.indexer_topk(*tensors, w.k, out=out)
         torch.cuda.synchronize()
         _check_topk(w, out.cpu().numpy(), range(w.num_q))
 
@@ -300,3 +327,25 @@ def test_indexer_prefill_full_size_sampled(lib):
         head = o[r, :n].astype(np.int64)
         assert len(np.unique(head)) == n and np.all((head >= lo[r]) & (head < lo[r] + L[r]))
     _check_topk(w, o, [0, 1, 2047, 4095, 6000, 8190, 8191])
+
+
+def test_indexer_short_prefill_sampled(lib):
+    """The causal prefill of 1024 query rows over 65536 keys, top-2048: the
+    windows are short (16K positions), so the automatic choice scores densely
+    and selects; sampled rows against the oracle, every row's properties."""
+    import torch
+    w = wl.make_config("prefill_1024x64k_k2048")
+    note("indexer_topk prefill 1024 x 65536 k=2048 (sampled)")
+    tensors = _upload(w)
+    out = torch.full((w.num_q, w.k), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    lib.indexer_topk(*tensors, w.k, out=out)
+    torch.cuda.synchronize()
+    assert lib.topk_last_launch().startswith("indexer-topk dense"), lib.topk_last_launch()
+    o = out.cpu().numpy()
+    lo, L = _lengths(w)
+    for r in range(w.num_q):
+        n = min(w.k, int(L[r]))
+        assert np.all(o[r, n:] == -1)
+        head = o[r, :n].astype(np.int64)
+        assert len(np.unique(head)) == n and np.all((head >= lo[r]) & (head < lo[r] + L[r]))
+    _check_topk(w, o, [0, 1, 511, 1022, 1023])

@@ -108,6 +108,7 @@ CONFIGS = {
     "odd_widths_k512": dict(requests=[(9, 4099), (5, 1023)], k=512, seed=7005),
     "flat_8x16k_k2048": dict(requests=[(8, 16384)], k=2048, seed=7006, flat=True),
     "prefill_8192x256k_k2048": dict(requests=[(8192, 262144)], k=2048, seed=7010),
+    "prefill_1024x64k_k2048": dict(requests=[(1024, 65536)], k=2048, seed=7011),
 }
 
 
