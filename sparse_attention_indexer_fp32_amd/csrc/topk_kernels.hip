@@ -1767,9 +1767,11 @@ split_stream_kernel(KernelArgs a) {
     // windowed: the threshold's 22-bit prefix, with `above` keys over it
     uint32_t fprefix = windowed ? wbase + t0 : t0, fneed = (uint32_t)n - above - gt0, fcnt = cnt0;
     int fshift = windowed ? 10 : 20;
+    // sorted mode: the selected keys go out with the positions
+    uint32_t* const key_out = a.sel_key ? a.sel_key + row * (int64_t)k : nullptr;
     select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                          sh_raw, sh_scan, sh_var, tid, true);
-    if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, floor);
+                          sh_raw, sh_scan, sh_var, tid, true, key_out);
+    if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, floor, key_out != nullptr);
   } else {
     for (int j = tid; j < k; j += NT) sh_raw[j] = -1;
     __syncthreads();
