@@ -90,9 +90,9 @@ topk_status_t indexer_logits(const uint8_t* q, const float* weights, const uint8
  * Working memory: per (device, stream), the fused form's candidate lists of
  * num_q x windows x max(4k, 4096) (score, position) pairs plus num_q x
  * windows x k packed candidates, or the dense form's num_q x num_kv scores
- * plus num_q x (k + 1) words, allocated on first need, grown on demand and
- * freed by topk_release_workspaces() (the first call that grows it
- * synchronises `stream`).
+ * plus num_q x (k + 1) words, allocated on first need, grown on demand (a
+ * replaced buffer stays allocated, so graphs captured with it stay valid) and
+ * freed by topk_release_workspaces().
  * Errors: as indexer_logits, plus TOPK_ERROR_INVALID_VALUE for k outside
  * [1, TOPK_MAX_K] and TOPK_ERROR_OUT_OF_MEMORY.
  */

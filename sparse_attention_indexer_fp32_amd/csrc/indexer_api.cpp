@@ -67,19 +67,15 @@ topk_status_t get_buffers(int dev, hipStream_t stream, size_t bytes, void** ptr)
     *ptr = b.ptr;
     return TOPK_SUCCESS;
   }
-  if (b.ptr) {
-    hipError_t e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    (void)hipFree(b.ptr);
-    b.ptr = nullptr;
-    b.bytes = 0;
-  }
   void* p = nullptr;
   hipError_t e = hipMalloc(&p, bytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
-    return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("indexer candidate buffers hipMalloc: ") + hipGetErrorString(e));
+    return fail(TOPK_ERROR_OUT_OF_MEMORY, std::string("indexer buffers hipMalloc: ") + hipGetErrorString(e));
   }
+  // the smaller buffer stays allocated until topk_release_workspaces: work
+  // queued on it (or a graph captured with it) may still use it
+  topk::retire_buffer(b.ptr);
   b.ptr = p;
   b.bytes = bytes;
   *ptr = p;

@@ -207,9 +207,9 @@ topk_status_t get_workspace(DeviceInfo& info, int dev, hipStream_t stream, size_
 }
 
 // Caller holds g_mu.  Sorted mode's buffer: per-row selection records, then
-// the selection launch's raw positions (batch x k) when the caller passes no
-// out_raw.  Every row is written by the selection launch before the finish
-// reads it, so the buffer needs no clearing.
+// the selection launch's raw positions (batch x k) and the keys it writes
+// beside them (batch x k).  Every row's record is written by the selection
+// launch before the finish reads it, so the buffer needs no clearing.
 topk_status_t get_meta(int dev, hipStream_t stream, int64_t words, uint32_t** ptr) {
   Workspace& w = g_meta[std::make_pair(dev, stream)];
   if (w.ptr && w.words >= (size_t)words) {
@@ -636,6 +636,9 @@ topk_status_t run_transform(const float* scores, const int32_t* seq_lens, const 
 namespace topk {
 void set_last_error(const char* msg) { t_last_error = msg; }
 void set_last_launch(const char* msg) { t_last_launch = msg; }
+void retire_buffer(void* p) {
+  if (p) g_retired.push_back(p);
+}
 std::mutex& lib_mutex() {
   static std::mutex m;
   return m;

@@ -20,6 +20,11 @@ void set_last_launch(const char* msg);
 // per-(device, stream) state holds it.
 std::mutex& lib_mutex();
 
+// A device buffer replaced by a larger one: kept allocated until
+// topk_release_workspaces (a graph captured before the growth still names
+// it).  Caller holds lib_mutex().
+void retire_buffer(void* p);
+
 // topk_transform for a caller that already holds lib_mutex().
 topk_status_t transform_locked(const float* scores, const int32_t* seq_lens, const int32_t* page_table, int32_t k,
                                int32_t page_size, int32_t* out_idx, int32_t* out_raw, hipStream_t stream,
