@@ -441,6 +441,40 @@ __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass
   }
 }
 
+// Among the candidates whose key equals `key`, finds the `need` (< their
+// count) with the lowest positions, by an MSB-first radix select on v =
+// ~position (the largest v are the lowest positions; positions are distinct,
+// so it ends with exactly `need`): on return exactly those members have
+// (v >> vshift) >= vprefix.  Digits of 11, 11 and 10 bits, so sh_hist needs
+// 2048 words.  Contains barriers: call uniformly.
+template <int NT>
+__device__ void lowest_positions(int ncand, uint32_t key, uint32_t need, const uint32_t* sh_ckey,
+                                 const int32_t* sh_cpos, uint32_t* sh_hist, uint32_t* sh_scan, uint32_t* sh_var,
+                                 int tid, uint32_t& vprefix, int& vshift) {
+  vprefix = 0;
+  vshift = 32;
+  uint32_t vneed = need;
+  for (int level = 0; level < 3; ++level) {
+    const int dshift = level == 0 ? 21 : (level == 1 ? 10 : 0);
+    const uint32_t mask = level == 2 ? 1023u : 2047u;
+    for (int b = tid; b < 2048; b += NT) sh_hist[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < ncand; i += NT) {
+      if (sh_ckey[i] != key) continue;
+      const uint32_t v = ~(uint32_t)sh_cpos[i];
+      if (vshift >= 32 || (v >> vshift) == vprefix) atomicAdd(&sh_hist[(v >> dshift) & mask], 1u);
+    }
+    __syncthreads();
+    if (level == 2) find_threshold<NT, kBinsNarrow>(sh_hist, vneed, sh_scan, sh_var, tid);
+    else find_threshold<NT, 2048>(sh_hist, vneed, sh_scan, sh_var, tid);
+    const uint32_t bin = uniform(sh_var[0]), gtc = uniform(sh_var[1]), cnt = uniform(sh_var[2]);
+    vneed -= gtc;
+    vprefix = level == 0 ? bin : ((vprefix << (level == 1 ? 11 : 10)) | bin);
+    vshift = dshift;
+    if (cnt == vneed) break;
+  }
+}
+
 // Finishes a row from candidates held in LDS.  (prefix, shift) name the
 // current threshold bin (the candidates' keys >> shift), `cnt` how many keys
 // it holds and `need` how many of its keys are still to be selected; the
@@ -455,14 +489,18 @@ __device__ __forceinline__ void hist_resident(const uint32_t (&key)[E], int pass
 // With `fill`, slots [0, n) of sh_raw are first set to -1 (nothing else
 // has written them yet).  With INDEX the slots receive candidate indices
 // (into sh_ckey / sh_cpos) instead of positions.  With `key_out` (global
-// memory, the row's k slots) each slot's key is written there too.
+// memory, the row's k slots) each slot's key is written there too.  With
+// `canon`, a final bin that has to be cut (equal keys, more than `need` of
+// them) gives its `need` lowest positions, the plain definition's choice,
+// and `cnt` returns equal to `need`: the selected set is then the canonical
+// one (the sorted entry point's finish only orders it).
 template <int NT, bool INDEX = false>
 __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, int& shift, uint32_t& cnt,
                                                   uint32_t& need, uint32_t gt_base, uint32_t n,
                                                   uint32_t* sh_hist, const uint32_t* sh_ckey,
                                                   const int32_t* sh_cpos, int32_t* sh_raw, uint32_t* sh_scan,
                                                   uint32_t* sh_var, int tid, bool fill = false,
-                                                  uint32_t* key_out = nullptr) {
+                                                  uint32_t* key_out = nullptr, bool canon = false) {
   while (shift > 0 && cnt != need) {
     for (int b = tid; b < kBinsNarrow; b += NT) sh_hist[b] = 0;
     __syncthreads();
@@ -478,7 +516,14 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, i
     prefix = (prefix << 10) | bin;
     shift -= 10;
   }
-  // With shift == 0 the keys left in the bin are identical: any `need` of them.
+  // With shift == 0 the keys left in the bin are identical: any `need` of
+  // them, or with `canon` the `need` lowest positions.
+  uint32_t vprefix = 0;
+  int vshift = 32;
+  if (canon && cnt != need) {
+    lowest_positions<NT>(ncand, prefix, need, sh_ckey, sh_cpos, sh_hist, sh_scan, sh_var, tid, vprefix, vshift);
+    cnt = need;
+  }
   const uint32_t gt_end = n - need;
   if (tid == 0) {
     sh_var[8] = gt_base;
@@ -496,7 +541,7 @@ __device__ __forceinline__ void select_candidates(int ncand, uint32_t& prefix, i
         sh_raw[s] = INDEX ? i : sh_cpos[i];
         if (key_out) key_out[s] = key;
       }
-    } else if (x == prefix && key != 0u) {
+    } else if (x == prefix && key != 0u && (vshift >= 32 || (~(uint32_t)sh_cpos[i] >> vshift) >= vprefix)) {
       const uint32_t e = atomicAdd(&sh_var[9], 1u);
       if (e < need) {
         sh_raw[gt_end + e] = INDEX ? i : sh_cpos[i];
@@ -920,7 +965,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
           shift -= 10;
         }
         select_candidates<kThreads, true>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                                          sh_raw, sh_scan, sh_var, tid);
+                                          sh_raw, sh_scan, sh_var, tid, false, nullptr, a.meta != nullptr);
         __syncthreads();
         // A split row has L > k: n = k, and the candidates fill [n_gt, k).
         int32_t* o = a.out + row * (int64_t)k;
@@ -941,7 +986,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
         }
         __syncthreads();
         select_candidates<kThreads>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
-                          sh_scan, sh_var, tid);
+                          sh_scan, sh_var, tid, false, nullptr, a.meta != nullptr);
         __syncthreads();
         write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid, nullptr, (int)n_gt);
       }
@@ -1393,7 +1438,7 @@ stream_rows_kernel(KernelArgs a) {
       // finish then need not gather them from the row)
       uint32_t* const key_out = a.sel_key ? a.sel_key + row * (int64_t)k : nullptr;
       select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                            sh_raw, sh_scan, sh_var, tid, true, key_out);
+                            sh_raw, sh_scan, sh_var, tid, true, key_out, a.meta != nullptr);
       if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, gate, key_out != nullptr);
     } else {
       for (int j = tid; j < k; j += NT) sh_raw[j] = -1;
@@ -1422,7 +1467,7 @@ stream_rows_kernel(KernelArgs a) {
                                  sh_cpos, sh_raw, sh_var, tid);
       if (collect)
         select_candidates<NT>((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist,
-                              sh_ckey, sh_cpos, sh_raw, sh_scan, sh_var, tid);
+                              sh_ckey, sh_cpos, sh_raw, sh_scan, sh_var, tid, false, nullptr, a.meta != nullptr);
       if (tid == 0) record_selection(a, row, prefix, shift, need, cnt, floor);
     }
     // the candidate list is free again: it holds the page-table row
@@ -1486,7 +1531,10 @@ __device__ __forceinline__ void g_max(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool REFINE, bool VEC>
+// SORTED: the sorted entry point's selection launch (canonical ties, keys
+// written beside the positions); a separate instantiation, so that the
+// unsorted kernel carries none of that code.
+template <int NT, int SV, int CV, int NBUF, int CAP, int WAVES, bool REFINE, bool VEC, bool SORTED>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 split_stream_kernel(KernelArgs a) {
   constexpr uint32_t kSampleSpan = (uint32_t)NT * 4u * SV;
@@ -1768,9 +1816,9 @@ split_stream_kernel(KernelArgs a) {
     uint32_t fprefix = windowed ? wbase + t0 : t0, fneed = (uint32_t)n - above - gt0, fcnt = cnt0;
     int fshift = windowed ? 10 : 20;
     // sorted mode: the selected keys go out with the positions
-    uint32_t* const key_out = a.sel_key ? a.sel_key + row * (int64_t)k : nullptr;
+    uint32_t* const key_out = SORTED && a.sel_key ? a.sel_key + row * (int64_t)k : nullptr;
     select_candidates<NT>((int)count, fprefix, fshift, fcnt, fneed, 0u, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                          sh_raw, sh_scan, sh_var, tid, true, key_out);
+                          sh_raw, sh_scan, sh_var, tid, true, key_out, SORTED);
     if (tid == 0) record_selection(a, row, fprefix, fshift, fneed, fcnt, floor, key_out != nullptr);
   } else {
     for (int j = tid; j < k; j += NT) sh_raw[j] = -1;
@@ -1799,7 +1847,7 @@ split_stream_kernel(KernelArgs a) {
                                sh_cpos, sh_raw, sh_var, tid);
     if (collect)
       select_candidates<NT>((int)cnt, prefix, shift, cnt, need, (uint32_t)n - need, (uint32_t)n, sh_hist, sh_ckey,
-                            sh_cpos, sh_raw, sh_scan, sh_var, tid);
+                            sh_cpos, sh_raw, sh_scan, sh_var, tid, false, nullptr, SORTED);
     if (tid == 0) record_selection(a, row, prefix, shift, need, cnt, floor);
   }
   __syncthreads();
@@ -2338,11 +2386,17 @@ hipError_t launch_split_stream_variant(int variant, const KernelArgs& args, hipS
   switch (variant) {
 #define TOPK_SS_LAUNCH_CASE(id, nt, sv, cv, nbuf, cap, waves, refine)                                            \
   case id:                                                                                                  \
-    if (args.vec)                                                                                           \
-      hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, true>),                 \
+    if (args.meta && args.vec)                                                                              \
+      hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, true, true>),           \
+                         dim3((unsigned)args.batch * (unsigned)args.wgs_per_row), dim3(nt), 0, stream, args); \
+    else if (args.meta)                                                                                     \
+      hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, false, true>),          \
+                         dim3((unsigned)args.batch * (unsigned)args.wgs_per_row), dim3(nt), 0, stream, args); \
+    else if (args.vec)                                                                                      \
+      hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, true, false>),          \
                          dim3((unsigned)args.batch * (unsigned)args.wgs_per_row), dim3(nt), 0, stream, args); \
     else                                                                                                    \
-      hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, false>),                \
+      hipLaunchKernelGGL((split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, false, false>),         \
                          dim3((unsigned)args.batch * (unsigned)args.wgs_per_row), dim3(nt), 0, stream, args); \
     return hipGetLastError();
     TOPK_SPLIT_STREAM_VARIANTS(TOPK_SS_LAUNCH_CASE)
@@ -2355,9 +2409,10 @@ hipError_t occupancy_split_stream_variant(int variant, int* blocks) {
   switch (variant) {
 #define TOPK_SS_OCC_CASE(id, nt, sv, cv, nbuf, cap, waves, refine)                                               \
   case id:                                                                                              \
-    return occupancy_pair(reinterpret_cast<const void*>(&split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, true>), \
-                          reinterpret_cast<const void*>(&split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, false>), \
-                          nt, blocks);
+    return occupancy_pair(                                                                               \
+        reinterpret_cast<const void*>(&split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, true, false>),  \
+        reinterpret_cast<const void*>(&split_stream_kernel<nt, sv, cv, nbuf, cap, waves, refine, false, false>), \
+        nt, blocks);
     TOPK_SPLIT_STREAM_VARIANTS(TOPK_SS_OCC_CASE)
 #undef TOPK_SS_OCC_CASE
     default: return hipErrorInvalidValue;
