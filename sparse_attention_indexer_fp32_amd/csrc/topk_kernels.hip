@@ -965,7 +965,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
           shift -= 10;
         }
         select_candidates<kThreads, true>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos,
-                                          sh_raw, sh_scan, sh_var, tid, false, nullptr, a.meta != nullptr);
+                                          sh_raw, sh_scan, sh_var, tid);
         __syncthreads();
         // A split row has L > k: n = k, and the candidates fill [n_gt, k).
         int32_t* o = a.out + row * (int64_t)k;
@@ -986,7 +986,7 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
         }
         __syncthreads();
         select_candidates<kThreads>(ncand, prefix, shift, cnt, need, n_gt, (uint32_t)n, sh_hist, sh_ckey, sh_cpos, sh_raw,
-                          sh_scan, sh_var, tid, false, nullptr, a.meta != nullptr);
+                          sh_scan, sh_var, tid);
         __syncthreads();
         write_row_output<kThreads>(a, row, L, n, false, sh_raw, tid, nullptr, (int)n_gt);
       }
