@@ -2276,31 +2276,46 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
   const int64_t row = (int64_t)(blockIdx.x % (uint32_t)a.batch);
   const uint32_t g = blockIdx.x / (uint32_t)a.batch;
   if (g >= (uint32_t)G) return;
-  if (uniform(a.meta[row * kMetaWords + 4]) != 0u) {   // cut
-    if (g == 0) sorted_row<NT, CAP, TIES>(a, row, sh_sort, sh_t, sh_t + TIES, sh_hist, sh_scan, sh_var);
-    return;
-  }
   const int tid = opaque_tid();
   const int64_t W = a.width;
   const int k = a.k;
+  // one round trip: the row's positions and keys (k slots each, in bounds
+  // whatever the record says) are requested with the record and the length
+  constexpr int kPer = CAP / NT;
+  const int32_t* sel = a.sel + row * (int64_t)k;
+  const uint32_t* key_row = a.sel_key + row * (int64_t)k;
+  int32_t sp[kPer];
+  uint32_t sk[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int j = tid + q * NT;
+    sp[q] = j < k ? sel[j] : -1;
+    sk[q] = j < k ? key_row[j] : 0u;
+  }
+  const uint32_t rec_cut = a.meta[row * kMetaWords + 4], rec_keys = a.meta[row * kMetaWords + 5];
   const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+  if (uniform(rec_cut) != 0u) {   // cut
+    if (g == 0) sorted_row<NT, CAP, TIES>(a, row, sh_sort, sh_t, sh_t + TIES, sh_hist, sh_scan, sh_var);
+    return;
+  }
+  const bool have_keys = uniform(rec_keys) != 0u;
   const uint32_t L = sl < 0 ? 0u : ((int64_t)sl > W ? (uint32_t)W : (uint32_t)sl);
   const uint32_t n = L < (uint32_t)k ? L : (uint32_t)k;
   const float* rowp = a.scores + row * W;
-  const int32_t* sel = a.sel + row * (int64_t)k;
-  const uint32_t* skey =
-      a.sel_key != nullptr && uniform(a.meta[row * kMetaWords + 5]) != 0u ? a.sel_key + row * (int64_t)k : nullptr;
   uint32_t* const sh_cnt = sh_hist;
   pairs_span_init<NT, NB>(sh_cnt, sh_mm, sh_scan, tid);
   __syncthreads();
   uint64_t hi = 0ull, lo = ~0ull;
-  for (uint32_t j = (uint32_t)tid; j < n; j += NT) {
-    const int32_t p = sel[j];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const uint32_t j = (uint32_t)(tid + q * NT);
+    if (j >= n) continue;
+    const int32_t p = sp[q];
     // a slot left without a position (none is, for valid input) sorts after every
     // key and is written as -1; j keeps such pairs distinct
     uint64_t P = (uint64_t)j;
     if (p >= 0 && (uint32_t)p < L)
-      P = ((uint64_t)(skey ? skey[j] : order_key_bits(__float_as_uint(rowp[p]))) << 32) | (uint64_t)(~(uint32_t)p);
+      P = ((uint64_t)(have_keys ? sk[q] : order_key_bits(__float_as_uint(rowp[p]))) << 32) | (uint64_t)(~(uint32_t)p);
     sh_sort[j] = P;
     hi = P > hi ? P : hi;
     lo = P < lo ? P : lo;
