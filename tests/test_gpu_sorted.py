@@ -140,6 +140,33 @@ def test_sorted_crowded_bucket(lib, k, finish):
     check_exact(w, out, raw)
 
 
+@pytest.mark.parametrize("name", ["c1", "c4b"])
+def test_sorted_graph_replay(lib, name):
+    """The sorted entry point (selection launch + rank finish) captured in a
+    HIP graph: every replay, with eager calls between them, gives the
+    oracle's output."""
+    import torch
+    w = workloads.make(name)
+    s, sl, pt = upload(w)
+    out = torch.empty((w.batch, w.k), dtype=torch.int32, device=s.device)
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        lib.topk_transform_sorted(s, sl, pt, w.k, w.page_size, out=out)   # buffers allocated outside capture
+        stream.synchronize()
+        note(f"sorted graph {name}: {lib.topk_last_launch()}")
+        check_exact(w, out.cpu().numpy(), None)
+        with torch.cuda.graph(g, stream=stream):
+            lib.topk_transform_sorted(s, sl, pt, w.k, w.page_size, out=out)
+    for rep in range(3):
+        out.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        check_exact(w, out.cpu().numpy(), None)
+        lib.topk_transform_sorted(s, sl, pt, w.k, w.page_size, out=out)   # an eager call between replays
+        torch.cuda.synchronize()
+
+
 def test_sorted_matches_unsorted_set(lib):
     """Same selected set as topk_transform wherever the threshold is not cut
     (distinct scores: the set is unique), in canonical order."""
