@@ -89,6 +89,13 @@ __device__ __forceinline__ void launder(uint32_t (&key)[E]) {
 // declared uniform so control flow that depends on it stays scalar.
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// p[i] at a wave-uniform index, read through the scalar data cache (for
+// arrays no kernel writes): the read waits on the scalar counter, not behind
+// vector loads issued before it.
+__device__ __forceinline__ int32_t scalar_read(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 // ---- agent-scope (whole-GPU, across XCDs) memory operations ----------------
 __device__ __forceinline__ void g_add(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -167,7 +174,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return r;
 }
 
-// Threshold bin of histogram h[0, NB), NB = 4096 or 1024: the highest bin t
+// Threshold bin of histogram h[0, NB), NB = 4096, 2048 or 1024: the highest bin t
 // with sum_{b >= t} h[b] >= need.  Writes sh_var[0] = t, sh_var[1] = count in
 // bins above t, sh_var[2] = h[t].  (If the histogram holds fewer than `need`
 // elements -- impossible for valid input -- it reports bin 0 with counts 0.)
@@ -636,7 +643,15 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     const int tid = opaque_tid();
     const int64_t row = (int64_t)slot + (int64_t)it * a.slots;
     if (row >= a.batch) break;
-    const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+    // Without SHORT, a workgroup's share of the row does not depend on the
+    // row's length, so its loads are issued before the length is read
+    // (bounded by the width; the keys past the length are masked once it is
+    // known) and the length's round trip overlaps them.
+    const float* rowp = a.scores + row * W;
+    const uint32_t c0 = COOP && !SHORT ? (uint32_t)g * (uint32_t)C : 0u;
+    uint32_t key[E];
+    if (!SHORT) load_raw<kThreads, E / 4>(key, rowp, c0, (uint32_t)W, a.vec != 0, tid);
+    const int32_t sl = scalar_read(a.seq_lens, row);
     const int64_t L = sl < 0 ? 0 : ((int64_t)sl > W ? W : (int64_t)sl);
     const int n = L < (int64_t)k ? (int)L : k;
     // Rows that need no cross-workgroup merge -- every position selected
@@ -664,12 +679,15 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
 
     for (int j = tid; j < k; j += kThreads) sh_raw[j] = -1;
 
-    // ---- load this workgroup's share of the row into registers (one HBM read)
-    const float* rowp = a.scores + row * W;
-    const uint32_t c0 = split ? (uint32_t)g * (uint32_t)C : 0u;
-    const uint32_t pbase = c0 + (uint32_t)tid * 4u;
-    uint32_t key[E];
-    load_keys<kThreads, E / 4>(key, rowp, c0, (uint32_t)L, a.vec != 0, tid);
+    // ---- this workgroup's share of the row in registers (one HBM read)
+    if (SHORT) {
+      const uint32_t cs = split ? (uint32_t)g * (uint32_t)C : 0u;
+      load_keys<kThreads, E / 4>(key, rowp, cs, (uint32_t)L, a.vec != 0, tid);
+    } else {
+#pragma unroll
+      for (int j = 0; j < E; ++j) key[j] = slot_key<kThreads>(key[j], j, c0, (uint32_t)L, tid);
+    }
+    const uint32_t pbase = (split ? (uint32_t)g * (uint32_t)C : 0u) + (uint32_t)tid * 4u;
     auto pos_of = [&](int j) -> int32_t {
       return (int32_t)(pbase + (uint32_t)(j >> 2) * (kThreads * 4) + (uint32_t)(j & 3));
     };
@@ -1559,11 +1577,26 @@ split_stream_kernel(KernelArgs a) {
   int64_t row;
   uint32_t part;
   int32_t seq;
+  // Part `part` of G of a row of Lx positions: [a0, a1), whole multiples of
+  // one float4 per thread, so every segment starts 16-byte aligned.
+  auto segment = [&](uint32_t Lx, uint32_t& a0, uint32_t& a1) {
+    const uint32_t per = (Lx + (uint32_t)G - 1u) / (uint32_t)G;
+    const uint32_t seglen = (per + 4u * NT - 1u) / (4u * NT) * (4u * NT);
+    a0 = part * seglen < Lx ? part * seglen : Lx;
+    a1 = Lx - a0 > seglen ? a0 + seglen : Lx;
+  };
+  // The sample's loads are issued before the row's length is read, for the
+  // segment of a row as long as the width (the usual case); they are issued
+  // again for the real segment if it differs.
+  uint32_t sk[4 * SV];
+  uint32_t s0w = 1u, s1w = 0u;   // the speculative segment (none for length-aware parts)
   if (a.spread == 0) {   // G parts for every row
     row = (int64_t)(blockIdx.x / (uint32_t)G);
     part = blockIdx.x - (uint32_t)row * (uint32_t)G;
     if (row >= a.batch) return;
-    seq = (int32_t)uniform((uint32_t)a.seq_lens[row]);
+    segment((uint32_t)W, s0w, s1w);
+    load_raw<NT, SV>(sk, a.scores + row * W, s0w, s1w, vec, opaque_tid());
+    seq = scalar_read(a.seq_lens, row);
   } else {
     // Length-aware: every workgroup reads the batch's lengths (at most
     // kSsMaxRows rows) and gives row r G_r = ceil(L_r / T) parts, between 1
@@ -1612,12 +1645,8 @@ split_stream_kernel(KernelArgs a) {
     }
     return;
   }
-  // Segment [s0, s1): whole multiples of one float4 per thread, so every
-  // segment starts 16-byte aligned.
-  const uint32_t per = (L + (uint32_t)G - 1u) / (uint32_t)G;
-  const uint32_t seglen = (per + 4u * NT - 1u) / (4u * NT) * (4u * NT);
-  const uint32_t s0 = part * seglen < L ? part * seglen : L;
-  const uint32_t s1 = L - s0 > seglen ? s0 + seglen : L;
+  uint32_t s0, s1;   // this part's segment
+  segment(L, s0, s1);
   uint32_t* const ctr = a.ws + kSsCtr + 4 * (size_t)row;
   uint32_t* const area = a.ws + kHdrWords + (size_t)row * kSsRowWords;
   const float* rowp = a.scores + row * W;
@@ -1628,8 +1657,7 @@ split_stream_kernel(KernelArgs a) {
   uint32_t gate = 0u;
   if (s0 < s1) {
     // 1. sample: the first kSampleSpan positions of the segment
-    uint32_t sk[4 * SV];
-    load_raw<NT, SV>(sk, rowp, s0, s1, vec, tid);
+    if (s0 != s0w || s1 != s1w) load_raw<NT, SV>(sk, rowp, s0, s1, vec, tid);
     const uint32_t seg = s1 - s0;
     const uint32_t nch = seg > kSampleSpan ? (seg - kSampleSpan + kChunkSpan - 1) / kChunkSpan : 0u;
 #pragma unroll
