@@ -2044,7 +2044,7 @@ __device__ __forceinline__ void pairs_span_init(uint32_t* sh_cnt, uint64_t* sh_m
 // of one key falls in one bucket), which the caller orders otherwise.
 // Contains barriers: call uniformly.
 constexpr uint32_t kRankMaxBucket = 256;
-template <int NT, int NB>
+template <int NT, int NB, int CAP>
 __device__ bool rank_pairs_write(const KernelArgs& a, int64_t row, uint32_t n, uint32_t L, uint32_t j0, uint32_t j1,
                                  const uint64_t* sh_a, uint64_t* sh_b, uint32_t* sh_beg, uint32_t* sh_cnt,
                                  uint64_t* sh_mm, uint32_t* sh_scan, int tid) {
@@ -2107,7 +2107,25 @@ __device__ bool rank_pairs_write(const KernelArgs& a, int64_t row, uint32_t n, u
   int32_t* o = a.out + row * (int64_t)k;
   int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
   const int32_t* pt = a.page_table + row * a.pages_per_row;
-  for (uint32_t base = 0; base < cnt_here; base += per) {
+  // The page-table entries of this thread's pairs are requested before any
+  // rank is counted (a pair's position is known already), so the gathers'
+  // round trip overlaps the counting.  A thread handles at most CAP / NT
+  // pairs: tpe = 1 gives ceil(cnt / NT) rounds, a larger tpe one round.
+  constexpr int kRounds = CAP / NT;
+  int32_t page[kRounds];
+#pragma unroll
+  for (int it = 0; it < kRounds; ++it) {
+    const uint32_t e = j0 + (uint32_t)it * per + (uint32_t)tid / tpe;
+    page[it] = 0;
+    if (e < j1 && q == 0) {
+      const uint32_t p = ~(uint32_t)sh_a[e];
+      if (p < L && (int64_t)(p >> s) < a.pages_per_row) page[it] = pt[p >> s];
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kRounds; ++it) {
+    const uint32_t base = (uint32_t)it * per;
+    if (base >= cnt_here) break;   // uniform
     const uint32_t e = j0 + base + (uint32_t)tid / tpe;
     const bool act = e < j1;
     uint64_t P = 0ull;
@@ -2131,8 +2149,7 @@ __device__ bool rank_pairs_write(const KernelArgs& a, int64_t row, uint32_t n, u
       int32_t rv = -1, v = -1;
       if (p < L) {
         rv = (int32_t)p;
-        const int64_t pg = (int64_t)(p >> s);
-        if (pg < a.pages_per_row) v = (int32_t)(((uint32_t)pt[pg] << s) | (p & pmask));
+        if ((int64_t)(p >> s) < a.pages_per_row) v = (int32_t)(((uint32_t)page[it] << s) | (p & pmask));
       }
       o[r] = v;
       if (orw) orw[r] = rv;
@@ -2351,7 +2368,7 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
   pairs_span(hi, lo, sh_mm, tid);
   const uint32_t j0 = (uint32_t)(((uint64_t)g * n) / (uint32_t)G);
   const uint32_t j1 = (uint32_t)(((uint64_t)(g + 1) * n) / (uint32_t)G);
-  if (!rank_pairs_write<NT, NB>(a, row, n, L, j0, j1, sh_sort, reinterpret_cast<uint64_t*>(sh_t), sh_t + 2 * CAP,
+  if (!rank_pairs_write<NT, NB, CAP>(a, row, n, L, j0, j1, sh_sort, reinterpret_cast<uint64_t*>(sh_t), sh_t + 2 * CAP,
                                 sh_cnt, sh_mm, sh_scan, tid)) {
     // a crowded bucket: the row's first workgroup sorts all n pairs instead
     if (g == 0) {
