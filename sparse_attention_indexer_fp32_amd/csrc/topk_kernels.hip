@@ -2036,50 +2036,89 @@ __device__ __forceinline__ void pairs_span_init(uint32_t* sh_cnt, uint64_t* sh_m
 // NB buckets by (P - Pmin) >> s, s chosen so that the row's span Pmax - Pmin
 // fills the buckets (a monotone map: each bucket is a range of P); a rank is
 // then the number of pairs in higher buckets plus a count over the pair's own
-// bucket, split over up to 64 threads per pair.  sh_b holds n pairs, sh_beg
-// and sh_cnt NB words each.  On entry (after a barrier) sh_mm = {Pmax, Pmin},
-// sh_cnt is zero and sh_scan[48] is zero (see pairs_span).  Returns false,
-// having written nothing, when a
-// bucket holds more than kRankMaxBucket pairs (many equal keys: every pair
-// of one key falls in one bucket), which the caller orders otherwise.
-// Contains barriers: call uniformly.
+// bucket, split over up to 64 threads per pair.
+//
+// A bucket of more than kRankMaxBucket pairs (many equal keys: the pairs of
+// one key differ only in their positions, and when the row's span is set by
+// other keys they share a bucket) is split once more, by kSubBins
+// sub-buckets fitted to its own span (for equal keys, the positions' span),
+// and its pairs are ranked within their sub-bucket.  Returns false, having
+// written nothing and with sh_a[0, n) holding the row's pairs again, when a
+// sub-bucket is still crowded; the caller then orders the row otherwise.
+//
+// sh_b holds n pairs, sh_beg and sh_cnt NB words each, sh_sub kSubWords
+// words, sh_mm2 two.  On entry (after a barrier) sh_mm = {Pmax, Pmin},
+// sh_cnt is zero and sh_scan[48] is zero (see pairs_span).  sh_a is
+// scratch once the pairs are grouped.  Contains barriers: call uniformly.
 constexpr uint32_t kRankMaxBucket = 256;
+constexpr int kSubBins = 256;
+constexpr int kRankMaxCrowded = 8;   // > n / (kRankMaxBucket + 1) for n <= kMaxK
+constexpr int kSubCnt = 0, kSubBeg = kSubBins, kSubCrowdN = 2 * kSubBins, kSubBig = kSubCrowdN + 1,
+              kSubCrowd = kSubBig + 1, kSubWords = kSubCrowd + kRankMaxCrowded;
 template <int NT, int NB, int CAP>
 __device__ bool rank_pairs_write(const KernelArgs& a, int64_t row, uint32_t n, uint32_t L, uint32_t j0, uint32_t j1,
-                                 const uint64_t* sh_a, uint64_t* sh_b, uint32_t* sh_beg, uint32_t* sh_cnt,
-                                 uint64_t* sh_mm, uint32_t* sh_scan, int tid) {
+                                 uint64_t* sh_a, uint64_t* sh_b, uint32_t* sh_beg, uint32_t* sh_cnt,
+                                 uint64_t* sh_mm, uint32_t* sh_scan, uint32_t* sh_sub, uint64_t* sh_mm2, int tid) {
   constexpr int kDigit = NB == 4096 ? 12 : (NB == 2048 ? 11 : (NB == 1024 ? 10 : -1));
   static_assert(kDigit > 0 && NB % NT == 0, "rank digit");
+  static_assert(NT >= kSubBins, "one sub-bucket per thread");
   const int k = a.k;
+  // 1. this thread's pairs (e = j0 + it * per + tid / tpe, tpe threads per
+  // pair), held in registers since sh_a becomes scratch, and their page-table
+  // entries requested before any rank is counted (so the output's gather
+  // overlaps the counting).  A thread handles at most CAP / NT pairs: tpe = 1
+  // gives ceil(cnt / NT) rounds, a larger tpe one round.
+  const uint32_t cnt_here = j1 - j0;
+  uint32_t tpe = 64;
+  while (tpe > 1 && tpe * cnt_here > (uint32_t)NT) tpe >>= 1;
+  const uint32_t per = (uint32_t)NT / tpe;
+  const uint32_t q = (uint32_t)tid & (tpe - 1u);
+  const int s = a.log2_page;
+  const uint32_t pmask = (1u << s) - 1u;
+  const int32_t* pt = a.page_table + row * a.pages_per_row;
+  constexpr int kRounds = CAP / NT;
+  uint64_t mine[kRounds];
+  int32_t page[kRounds];
+  uint32_t rk[kRounds];   // ranks of pairs in refined buckets (lane q == 0)
+#pragma unroll
+  for (int it = 0; it < kRounds; ++it) {
+    const uint32_t e = j0 + (uint32_t)it * per + (uint32_t)tid / tpe;
+    mine[it] = e < j1 ? sh_a[e] : 0ull;
+    page[it] = 0;
+    rk[it] = 0u;
+    if (e < j1 && q == 0) {
+      const uint32_t p = ~(uint32_t)mine[it];
+      if (p < L && (int64_t)(p >> s) < a.pages_per_row) page[it] = pt[p >> s];
+    }
+  }
+
   // 2. bucket counts
   const uint64_t pmin = sh_mm[1];
   const uint64_t range = sh_mm[0] - pmin;
   const int top = range != 0ull ? 63 - __builtin_clzll(range) : 0;
   const int bs = top >= kDigit - 1 ? top - (kDigit - 1) : 0;
-  for (uint32_t j = (uint32_t)tid; j < n; j += NT)
-    atomicAdd(&sh_cnt[(uint32_t)((sh_a[j] - pmin) >> bs) & (uint32_t)(NB - 1)], 1u);
+  auto bucket = [&](uint64_t P) { return (uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1); };
+  if (tid == 0) sh_sub[kSubCrowdN] = 0u;
+  for (uint32_t j = (uint32_t)tid; j < n; j += NT) atomicAdd(&sh_cnt[bucket(sh_a[j])], 1u);
   __syncthreads();
 
   // 3. first slots, buckets in descending order: thread t owns buckets
-  // NB-1-(NB/NT)t down to NB-(NB/NT)(t+1)
+  // NB-1-(NB/NT)t down to NB-(NB/NT)(t+1); crowded buckets are listed
   {
     constexpr int kPer = NB / NT;
-    uint32_t c[kPer], sum = 0, big = 0;
+    uint32_t c[kPer], sum = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       c[i] = sh_cnt[NB - 1 - kPer * tid - i];
       sum += c[i];
-      big = c[i] > big ? c[i] : big;
+      if (c[i] > kRankMaxBucket) {
+        const uint32_t slot = atomicAdd(&sh_sub[kSubCrowdN], 1u);
+        if (slot < (uint32_t)kRankMaxCrowded) sh_sub[kSubCrowd + slot] = (uint32_t)(NB - 1 - kPer * tid - i);
+      }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t o2 = (uint32_t)__shfl_xor((int)big, off, 64);
-      big = o2 > big ? o2 : big;
-    }
-    if ((tid & 63) == 0) atomicMax(&sh_scan[48], big);
     uint32_t total;
     uint32_t run = block_exclusive_scan<NT>(sum, sh_scan, total, tid);   // ends with a barrier
-    if (uniform(sh_scan[48]) > kRankMaxBucket) return false;
+    if (uniform(sh_sub[kSubCrowdN]) > (uint32_t)kRankMaxCrowded) return false;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       sh_beg[NB - 1 - kPer * tid - i] = run;
@@ -2092,59 +2131,108 @@ __device__ bool rank_pairs_write(const KernelArgs& a, int64_t row, uint32_t n, u
   // cursors end one past each bucket, so the first slots are end - count
   for (uint32_t j = (uint32_t)tid; j < n; j += NT) {
     const uint64_t P = sh_a[j];
-    sh_b[atomicAdd(&sh_beg[(uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1)], 1u)] = P;
+    sh_b[atomicAdd(&sh_beg[bucket(P)], 1u)] = P;
   }
   __syncthreads();
 
-  // 5. ranks of pairs [j0, j1), tpe threads per pair, and the output
-  const uint32_t cnt_here = j1 - j0;
-  uint32_t tpe = 64;
-  while (tpe > 1 && tpe * cnt_here > (uint32_t)NT) tpe >>= 1;
-  const uint32_t per = (uint32_t)NT / tpe;
-  const uint32_t q = (uint32_t)tid & (tpe - 1u);
-  const int s = a.log2_page;
-  const uint32_t pmask = (1u << s) - 1u;
+  // 5. crowded buckets, one at a time: sub-buckets fitted to the bucket's
+  // span, the bucket's pairs regrouped by sub-bucket (descending) in place,
+  // and the ranks of this thread's pairs in it counted over their sub-bucket
+  const uint32_t ncrowd = uniform(sh_sub[kSubCrowdN]);
+  for (uint32_t ci = 0; ci < ncrowd; ++ci) {
+    const uint32_t b = uniform(sh_sub[kSubCrowd + ci]);
+    const uint32_t bend = sh_beg[b], bfirst = bend - sh_cnt[b];
+    if (tid == 0) {
+      sh_mm2[0] = 0ull;
+      sh_mm2[1] = ~0ull;
+      sh_sub[kSubBig] = 0u;
+    }
+    if (tid < kSubBins) sh_sub[kSubCnt + tid] = 0u;
+    __syncthreads();
+    uint64_t hi = 0ull, lo = ~0ull;
+    for (uint32_t i = bfirst + (uint32_t)tid; i < bend; i += NT) {
+      const uint64_t P = sh_b[i];
+      hi = P > hi ? P : hi;
+      lo = P < lo ? P : lo;
+    }
+    pairs_span(hi, lo, sh_mm2, tid);
+    const uint64_t smin = sh_mm2[1];
+    const uint64_t srange = sh_mm2[0] - smin;
+    const int stop = srange != 0ull ? 63 - __builtin_clzll(srange) : 0;
+    const int sbs = stop >= 7 ? stop - 7 : 0;   // kSubBins = 2^8
+    auto sub = [&](uint64_t P) { return (uint32_t)((P - smin) >> sbs) & (uint32_t)(kSubBins - 1); };
+    for (uint32_t i = bfirst + (uint32_t)tid; i < bend; i += NT) atomicAdd(&sh_sub[kSubCnt + sub(sh_b[i])], 1u);
+    __syncthreads();
+    // descending sub-bucket starts (relative to bfirst); thread t owns sub-bucket kSubBins-1-t
+    const uint32_t sc = tid < kSubBins ? sh_sub[kSubCnt + kSubBins - 1 - tid] : 0u;
+    uint32_t big = sc;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o2 = (uint32_t)__shfl_xor((int)big, off, 64);
+      big = o2 > big ? o2 : big;
+    }
+    if ((tid & 63) == 0) atomicMax(&sh_sub[kSubBig], big);
+    uint32_t total;
+    const uint32_t srun = block_exclusive_scan<NT>(sc, sh_scan, total, tid);   // ends with a barrier
+    if (uniform(sh_sub[kSubBig]) > kRankMaxBucket) {
+      // still crowded: hand the caller the row's pairs back in sh_a
+      for (uint32_t j = (uint32_t)tid; j < n; j += NT) sh_a[j] = sh_b[j];
+      __syncthreads();
+      return false;
+    }
+    if (tid < kSubBins) sh_sub[kSubBeg + kSubBins - 1 - tid] = srun;
+    for (uint32_t i = bfirst + (uint32_t)tid; i < bend; i += NT) sh_a[i] = sh_b[i];
+    __syncthreads();
+    for (uint32_t i = bfirst + (uint32_t)tid; i < bend; i += NT) {
+      const uint64_t P = sh_a[i];
+      sh_b[bfirst + atomicAdd(&sh_sub[kSubBeg + sub(P)], 1u)] = P;
+    }
+    __syncthreads();
+    // the cursors end one past each sub-bucket
+#pragma unroll
+    for (int it = 0; it < kRounds; ++it) {
+      const uint32_t e = j0 + (uint32_t)it * per + (uint32_t)tid / tpe;
+      const uint64_t P = mine[it];
+      if (e < j1 && q == 0 && bucket(P) == b) {
+        const uint32_t sb = sub(P);
+        const uint32_t send = bfirst + sh_sub[kSubBeg + sb], sfirst = send - sh_sub[kSubCnt + sb];
+        uint32_t c = 0;
+        for (uint32_t i = sfirst; i < send; ++i) c += sh_b[i] > P ? 1u : 0u;
+        rk[it] = sfirst + c;
+      }
+    }
+    __syncthreads();
+  }
+
+  // 6. ranks of pairs [j0, j1), tpe threads per pair, and the output
   int32_t* o = a.out + row * (int64_t)k;
   int32_t* orw = a.out_raw ? a.out_raw + row * (int64_t)k : nullptr;
-  const int32_t* pt = a.page_table + row * a.pages_per_row;
-  // The page-table entries of this thread's pairs are requested before any
-  // rank is counted (a pair's position is known already), so the gathers'
-  // round trip overlaps the counting.  A thread handles at most CAP / NT
-  // pairs: tpe = 1 gives ceil(cnt / NT) rounds, a larger tpe one round.
-  constexpr int kRounds = CAP / NT;
-  int32_t page[kRounds];
-#pragma unroll
-  for (int it = 0; it < kRounds; ++it) {
-    const uint32_t e = j0 + (uint32_t)it * per + (uint32_t)tid / tpe;
-    page[it] = 0;
-    if (e < j1 && q == 0) {
-      const uint32_t p = ~(uint32_t)sh_a[e];
-      if (p < L && (int64_t)(p >> s) < a.pages_per_row) page[it] = pt[p >> s];
-    }
-  }
 #pragma unroll
   for (int it = 0; it < kRounds; ++it) {
     const uint32_t base = (uint32_t)it * per;
     if (base >= cnt_here) break;   // uniform
     const uint32_t e = j0 + base + (uint32_t)tid / tpe;
     const bool act = e < j1;
-    uint64_t P = 0ull;
+    const uint64_t P = mine[it];
     uint32_t first = 0, c = 0;
+    bool refined = false;
     if (act) {
-      P = sh_a[e];
-      const uint32_t b = (uint32_t)((P - pmin) >> bs) & (uint32_t)(NB - 1);
-      const uint32_t end = sh_beg[b];
-      first = end - sh_cnt[b];
-      uint32_t i = first + q;
-      for (; i + 3u * tpe < end; i += 4u * tpe) {   // four independent reads in flight
-        const uint64_t b0 = sh_b[i], b1 = sh_b[i + tpe], b2 = sh_b[i + 2u * tpe], b3 = sh_b[i + 3u * tpe];
-        c += (b0 > P ? 1u : 0u) + (b1 > P ? 1u : 0u) + (b2 > P ? 1u : 0u) + (b3 > P ? 1u : 0u);
+      const uint32_t b = bucket(P);
+      refined = sh_cnt[b] > kRankMaxBucket;
+      if (!refined) {
+        const uint32_t end = sh_beg[b];
+        first = end - sh_cnt[b];
+        uint32_t i = first + q;
+        for (; i + 3u * tpe < end; i += 4u * tpe) {   // four independent reads in flight
+          const uint64_t b0 = sh_b[i], b1 = sh_b[i + tpe], b2 = sh_b[i + 2u * tpe], b3 = sh_b[i + 3u * tpe];
+          c += (b0 > P ? 1u : 0u) + (b1 > P ? 1u : 0u) + (b2 > P ? 1u : 0u) + (b3 > P ? 1u : 0u);
+        }
+        for (; i < end; i += tpe) c += sh_b[i] > P ? 1u : 0u;
       }
-      for (; i < end; i += tpe) c += sh_b[i] > P ? 1u : 0u;
     }
     for (uint32_t off = 1; off < tpe; off <<= 1) c += (uint32_t)__shfl_xor((int)c, (int)off, 64);
     if (act && q == 0) {
-      const uint32_t r = first + c;
+      const uint32_t r = refined ? rk[it] : first + c;
       const uint32_t p = ~(uint32_t)P;
       int32_t rv = -1, v = -1;
       if (p < L) {
@@ -2313,6 +2401,8 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
   __shared__ uint32_t sh_scan[64];
   __shared__ uint32_t sh_var[16];
   __shared__ uint64_t sh_mm[2];
+  __shared__ uint32_t sh_sub[kSubWords];   // rank_pairs_write's crowded-bucket tables
+  __shared__ uint64_t sh_mm2[2];
   // workgroup-major over rows: the rows' first workgroups (which alone finish
   // cut rows) are dispatched first and spread over the XCDs, and when the
   // batch is a multiple of 8 a row's workgroups share one XCD (and its L2,
@@ -2369,7 +2459,7 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
   const uint32_t j0 = (uint32_t)(((uint64_t)g * n) / (uint32_t)G);
   const uint32_t j1 = (uint32_t)(((uint64_t)(g + 1) * n) / (uint32_t)G);
   if (!rank_pairs_write<NT, NB, CAP>(a, row, n, L, j0, j1, sh_sort, reinterpret_cast<uint64_t*>(sh_t), sh_t + 2 * CAP,
-                                sh_cnt, sh_mm, sh_scan, tid)) {
+                                sh_cnt, sh_mm, sh_scan, sh_sub, sh_mm2, tid)) {
     // a crowded bucket: the row's first workgroup sorts all n pairs instead
     if (g == 0) {
       for (uint32_t j = n + (uint32_t)tid; j < (uint32_t)CAP; j += NT) sh_sort[j] = (uint64_t)j;
