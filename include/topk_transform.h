@@ -260,7 +260,10 @@ topk_status_t topk_set_split_stream(int32_t shape, int32_t wgs_per_row);
  *       bitonic-sorted in LDS;
  *    1  the rank finish: G workgroups per row (about two per CU, at least 64
  *       pairs each) each compute the final slot of their share of the row's
- *       pairs by counting the larger pairs, bucketed by a data-fitted digit.
+ *       pairs by counting the larger pairs, bucketed by a data-fitted digit
+ *       (a bucket crowded by tied keys is split again by a digit fitted to
+ *       its own span; a row whose split stays crowded is sorted by its
+ *       first workgroup as in mode 0).
  * Rows whose threshold bin was cut take the one-workgroup path in both
  * forms.  Both are exact for every input (the output is unique); the choice
  * only moves time.  Returns TOPK_ERROR_INVALID_VALUE for other values.

@@ -124,9 +124,9 @@ def test_sorted_every_path(lib, path, ept, wgs, shape, kind, finish):
 def test_sorted_crowded_bucket(lib, k, finish):
     """Short rows (every position selected, so the bin is not cut) holding
     hundreds of equal keys beside a few larger and smaller ones: the rank
-    finish's span-fitted buckets put each key's pairs in one bucket, and the
-    row is sorted by one workgroup instead.  The last row is long: ties at its
-    threshold cut the bin."""
+    finish's span-fitted buckets put each key's pairs in one bucket, which is
+    then split by the positions.  The last row is long: ties at its threshold
+    cut the bin."""
     W = 3000
     seq = [k - 7, k // 2, 300, W]
     w = workloads.custom(41 + k, len(seq), W, k, 16, seq_lens=seq, kind="crowded", table="perm")
@@ -135,6 +135,45 @@ def test_sorted_crowded_bucket(lib, k, finish):
     try:
         out, raw = run_sorted(lib, w, raw=True)
         note(f"sorted crowded: {lib.topk_last_launch()}")
+    finally:
+        lib.topk_set_sorted_finish(-1)
+    check_exact(w, out, raw)
+
+
+@pytest.mark.parametrize("k", [512, 1024])
+def test_sorted_rank_crowded_splits(lib, k):
+    """The rank finish on rows built so that tied keys crowd its buckets
+    (every position of a short row is selected):
+      * one far key and one tie group: the group's bucket is split by its
+        positions;
+      * one far key and two tie groups one ulp apart: both groups share a
+        bucket and, split by that bucket's span, one sub-bucket each, so the
+        row falls back to its first workgroup's sort;
+      * three tie groups of spread keys, and a constant row;
+      * a long row beside them (its threshold cut)."""
+    W = 4096
+    L = k - 24
+    one = np.float32(1.0)
+    up = np.nextafter(one, np.float32(2.0))
+    rng = np.random.Generator(np.random.PCG64(4100 + k))
+    rows = []
+    r = np.full(W, one, np.float32); r[rng.integers(0, L)] = 100.0; rows.append(r)
+    r = np.where(rng.random(W) < 0.5, one, up).astype(np.float32); r[rng.integers(0, L)] = 100.0; rows.append(r)
+    r = rng.choice(np.array([-3.0, 0.25, 7.5], np.float32), W).astype(np.float32); rows.append(r)
+    rows.append(np.full(W, np.float32(-2.0), np.float32))
+    rows.append(rng.choice(np.array([1.0, 2.0, 3.0, 4.0], np.float32), W).astype(np.float32))
+    scores = np.stack(rows)
+    seq = np.array([L, L, L, L, W], np.int32)
+    workloads.poison_scores(scores, seq)
+    P = -(-W // 16)
+    pt = workloads.identity_table(len(seq), P, seq, 16)
+    w = workloads.Workload("sorted_rank_crowded", "tie groups crowding the rank finish's buckets", scores, seq, pt, k,
+                           16, True, 4100 + k)
+    note(f"sorted rank crowded splits k={k}")
+    lib.topk_set_sorted_finish(1)
+    try:
+        out, raw = run_sorted(lib, w, raw=True)
+        assert "rank" in lib.topk_last_launch(), lib.topk_last_launch()
     finally:
         lib.topk_set_sorted_finish(-1)
     check_exact(w, out, raw)
