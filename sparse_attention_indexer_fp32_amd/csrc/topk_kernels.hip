@@ -89,9 +89,10 @@ __device__ __forceinline__ void launder(uint32_t (&key)[E]) {
 // declared uniform so control flow that depends on it stays scalar.
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// p[i] at a wave-uniform index, read through the scalar data cache (for
-// arrays no kernel writes): the read waits on the scalar counter, not behind
-// vector loads issued before it.
+// p[i] at a wave-uniform index, read through the scalar data cache (only for
+// arrays that nothing writes while the kernel runs, such as the row lengths:
+// that cache is not kept coherent within a launch): the read waits on the
+// scalar counter, not behind vector loads issued before it.
 __device__ __forceinline__ int32_t scalar_read(const int32_t* p, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
