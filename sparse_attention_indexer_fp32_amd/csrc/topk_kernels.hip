@@ -1919,16 +1919,22 @@ split_stream_kernel(KernelArgs a) {
 template <int NT>
 constexpr int sort_cv() { return NT >= 512 ? 4096 / NT : 4; }
 
+// Histogram bins of the sorted finish (the rank finish's buckets, the cut
+// rows' tie select): 1024 for the small shape (k <= kSortSmallK), whose LDS
+// sets how many workgroups a CU holds, else 4096.
+template <int CAP>
+constexpr int sort_hist_bins() { return CAP <= kSortSmallK ? kBinsNarrow : kBinsWide; }
+
 // One pass over the row for the memory fallback of the tie select: with
-// `collect` false, histograms the digit of v = ~position at dshift (12 bits
-// at dshift 20, else 10) of the bin members whose v >> (vshift) == vprefix
-// (vshift 32: all); with `collect` true, appends the members with
-// v >> vshift >= vprefix to sh_sort from slot `base` on.
+// `collect` false, histograms the digit (v >> dshift) & dmask of v =
+// ~position of the bin members whose v >> (vshift) == vprefix (vshift 32:
+// all); with `collect` true, appends the members with v >> vshift >= vprefix
+// to sh_sort from slot `base` on.
 template <int NT, int CAP>
 __device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp, uint32_t L, bool vec,
                                                 uint32_t prefix, int shift, uint32_t floor, uint32_t vprefix,
-                                                int vshift, int dshift, uint32_t* sh_hist, uint64_t* sh_sort,
-                                                uint32_t base, uint32_t* sh_var, int tid) {
+                                                int vshift, int dshift, uint32_t dmask, uint32_t* sh_hist,
+                                                uint64_t* sh_sort, uint32_t base, uint32_t* sh_var, int tid) {
   constexpr uint32_t span = (uint32_t)NT * 4u * sort_cv<NT>();
   for (uint32_t c = 0; c < L; c += span) {
     uint32_t raw[4 * sort_cv<NT>()];
@@ -1942,7 +1948,7 @@ __device__ __forceinline__ void sorted_tie_pass(bool collect, const float* rowp,
       const uint32_t v = ~pos;
       const uint32_t vp = vshift >= 32 ? 0u : v >> vshift;
       if (!collect) {
-        if (vshift >= 32 || vp == vprefix) atomicAdd(&sh_hist[(v >> dshift) & (dshift == 20 ? 4095u : 1023u)], 1u);
+        if (vshift >= 32 || vp == vprefix) atomicAdd(&sh_hist[(v >> dshift) & dmask], 1u);
       } else if (vp >= vprefix) {
         const uint32_t s = base + atomicAdd(&sh_var[2], 1u);
         if (s < (uint32_t)CAP) sh_sort[s] = ((uint64_t)x << 32) | (uint64_t)v;
@@ -2249,8 +2255,9 @@ __device__ bool rank_pairs_write(const KernelArgs& a, int64_t row, uint32_t n, u
 
 // The sorted finish of one row by one NT-thread workgroup (contains barriers:
 // call uniformly).  sh_sort holds CAP pairs, sh_tk / sh_tp TIES entries each,
-// sh_hist kBinsWide words.
-template <int NT, int CAP, int TIES>
+// sh_hist HB words (the tie select's digit width: 12 bits first with 4096, all 10
+// bits with 1024).
+template <int NT, int CAP, int TIES, int HB>
 __device__ void sorted_row(const KernelArgs& a, int64_t row, uint64_t* sh_sort, uint32_t* sh_tk, uint32_t* sh_tp,
                            uint32_t* sh_hist, uint32_t* sh_scan, uint32_t* sh_var) {
   constexpr uint32_t span = (uint32_t)NT * 4u * sort_cv<NT>();
@@ -2316,31 +2323,36 @@ __device__ void sorted_row(const KernelArgs& a, int64_t row, uint64_t* sh_sort, 
       uint32_t vprefix = 0;
       int vshift = 32;
       if (nties > need) {
+        // MSB-first digits of v: with HB = 4096 bins, 12 + 10 + 10 bits; with
+        // HB = 1024 (the small shape, whose histogram is kept small so more
+        // workgroups fit a CU), 10 + 10 + 10 + 2 bits
+        constexpr int kLevels = HB == kBinsWide ? 3 : 4;
         uint32_t vneed = need;
-        for (int level = 0; level < 3; ++level) {
-          const int dshift = level == 0 ? 20 : (level == 1 ? 10 : 0);
-          const int nb = level == 0 ? kBinsWide : kBinsNarrow;
+        for (int level = 0; level < kLevels; ++level) {
+          const int dshift = HB == kBinsWide ? (level == 0 ? 20 : (level == 1 ? 10 : 0)) : (level < 3 ? 22 - 10 * level : 0);
+          const int width = HB == kBinsWide ? (level == 0 ? 12 : 10) : (level < 3 ? 10 : 2);
+          const uint32_t dmask = (1u << width) - 1u;
+          const int nb = HB == kBinsWide && level == 0 ? kBinsWide : kBinsNarrow;
           for (int b = tid; b < nb; b += NT) sh_hist[b] = 0;
           __syncthreads();
           if (in_lds) {
             for (uint32_t i = (uint32_t)tid; i < nties; i += NT) {
               const uint32_t v = ~sh_tp[i];
-              if (vshift >= 32 || (v >> vshift) == vprefix)
-                atomicAdd(&sh_hist[(v >> dshift) & (level == 0 ? 4095u : 1023u)], 1u);
+              if (vshift >= 32 || (v >> vshift) == vprefix) atomicAdd(&sh_hist[(v >> dshift) & dmask], 1u);
             }
             __syncthreads();
           } else {
-            sorted_tie_pass<NT, CAP>(false, rowp, L, vec, prefix, shift, floor, vprefix, vshift, dshift, sh_hist, sh_sort, 0u,
-                            sh_var, tid);
+            sorted_tie_pass<NT, CAP>(false, rowp, L, vec, prefix, shift, floor, vprefix, vshift, dshift, dmask, sh_hist,
+                                     sh_sort, 0u, sh_var, tid);
           }
           uint32_t bin, gtc, cnt;
-          if (level == 0) find_threshold<NT, kBinsWide>(sh_hist, vneed, sh_scan, sh_var, tid);
+          if (nb == kBinsWide) find_threshold<NT, (HB > kBinsNarrow ? HB : kBinsNarrow)>(sh_hist, vneed, sh_scan, sh_var, tid);
           else find_threshold<NT, kBinsNarrow>(sh_hist, vneed, sh_scan, sh_var, tid);
           bin = uniform(sh_var[0]);
           gtc = uniform(sh_var[1]);
           cnt = uniform(sh_var[2]);
           vneed -= gtc;
-          vprefix = level == 0 ? bin : ((vprefix << 10) | bin);
+          vprefix = vshift >= 32 ? bin : ((vprefix << width) | bin);
           vshift = dshift;
           if (cnt == vneed) break;   // positions are distinct: at the last digit the bin holds one
         }
@@ -2359,8 +2371,8 @@ __device__ void sorted_row(const KernelArgs& a, int64_t row, uint64_t* sh_sort, 
         }
         __syncthreads();
       } else {
-        sorted_tie_pass<NT, CAP>(true, rowp, L, vec, prefix, shift, floor, vprefix, vshift, 0, sh_hist, sh_sort, base, sh_var,
-                        tid);
+        sorted_tie_pass<NT, CAP>(true, rowp, L, vec, prefix, shift, floor, vprefix, vshift, 0, 0u, sh_hist, sh_sort, base,
+                                 sh_var, tid);
       }
 
     }
@@ -2377,11 +2389,12 @@ __global__ void __launch_bounds__(NT) sorted_rows_kernel(KernelArgs a) {
   __shared__ uint64_t sh_sort[CAP];    // (key << 32) | ~position of the selected
   __shared__ uint32_t sh_tk[TIES];     // threshold-bin members: key
   __shared__ uint32_t sh_tp[TIES];     //                        position
-  __shared__ uint32_t sh_hist[kBinsWide];
+  constexpr int HB = sort_hist_bins<CAP>();
+  __shared__ uint32_t sh_hist[HB];
   __shared__ uint32_t sh_scan[64];
   __shared__ uint32_t sh_var[16];
   for (int64_t row = blockIdx.x; row < a.batch; row += gridDim.x)
-    sorted_row<NT, CAP, TIES>(a, row, sh_sort, sh_tk, sh_tp, sh_hist, sh_scan, sh_var);
+    sorted_row<NT, CAP, TIES, HB>(a, row, sh_sort, sh_tk, sh_tp, sh_hist, sh_scan, sh_var);
 }
 
 // Rank finish: the default sorted finish.  G = a.wgs_per_row workgroups
@@ -2394,11 +2407,12 @@ __global__ void __launch_bounds__(NT) sorted_rows_kernel(KernelArgs a) {
 // workgroup instead).  Rows whose bin was cut need the row read again: the
 // row's first workgroup runs the one-workgroup finish, and the others leave.
 template <int NT, int CAP, int TIES, int NB>
-__global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
-  static_assert(NB <= kBinsWide && 2 * CAP + NB <= 2 * TIES, "rank finish shape");
+__global__ void __launch_bounds__(NT, NT <= 256 ? 8 : 1) sorted_rank_kernel(KernelArgs a) {
+  constexpr int HB = sort_hist_bins<CAP>();
+  static_assert(NB <= HB && 2 * CAP + NB <= 2 * TIES, "rank finish shape");
   __shared__ uint64_t sh_sort[CAP];
   __shared__ uint32_t sh_t[2 * TIES];   // cut rows: the tie list's keys, then positions
-  __shared__ uint32_t sh_hist[kBinsWide];
+  __shared__ uint32_t sh_hist[HB];
   __shared__ uint32_t sh_scan[64];
   __shared__ uint32_t sh_var[16];
   __shared__ uint64_t sh_mm[2];
@@ -2431,7 +2445,7 @@ __global__ void __launch_bounds__(NT) sorted_rank_kernel(KernelArgs a) {
   const uint32_t rec_cut = a.meta[row * kMetaWords + 4], rec_keys = a.meta[row * kMetaWords + 5];
   const int32_t sl = (int32_t)uniform((uint32_t)a.seq_lens[row]);
   if (uniform(rec_cut) != 0u) {   // cut
-    if (g == 0) sorted_row<NT, CAP, TIES>(a, row, sh_sort, sh_t, sh_t + TIES, sh_hist, sh_scan, sh_var);
+    if (g == 0) sorted_row<NT, CAP, TIES, HB>(a, row, sh_sort, sh_t, sh_t + TIES, sh_hist, sh_scan, sh_var);
     return;
   }
   const bool have_keys = uniform(rec_keys) != 0u;
