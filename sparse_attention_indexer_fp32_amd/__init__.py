@@ -95,6 +95,25 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
+_raw_stream = None   # torch's accessor of the current stream's raw handle, when it has one
+
+
+def _stream_handle(stream, dev) -> int:
+    """The HIP stream handle for a call: `stream`'s, or the current stream of
+    device `dev`.  The current stream is read through torch's raw accessor
+    (the one torch._dynamo uses), which builds no Stream object: about 0.2 us
+    per call instead of 2 us."""
+    global _raw_stream
+    if stream is not None:
+        return stream.cuda_stream
+    import torch
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream and dev.index is not None:
+        return _raw_stream(dev.index)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
 def _check(status: int) -> None:
     if status != 0:
         text = load().topk_last_error().decode(errors="replace")
@@ -165,10 +184,8 @@ def _call(fn, scores, seq_lens, page_table, k, page_size, out, out_raw, want_raw
     if out_raw is not None and (out_raw.shape != (B, k) or out_raw.dtype != torch.int32
                                 or not out_raw.is_contiguous() or out_raw.device != dev):
         raise ValueError("out_raw must be a contiguous int32 tensor of shape (B, k)")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
     args = (scores.data_ptr(), seq_lens.data_ptr(), page_table.data_ptr(), int(k), int(page_size), out.data_ptr(),
-            out_raw.data_ptr() if out_raw is not None else None, ctypes.c_void_p(stream.cuda_stream), int(B), int(W),
+            out_raw.data_ptr() if out_raw is not None else None, _stream_handle(stream, dev), int(B), int(W),
             int(page_table.shape[1]))
     # The library works on the current device: switch only when the tensors
     # live on another one (the switch costs a device get/set round trip).
@@ -274,12 +291,10 @@ def indexer_logits(q, weights, kv, kv_scale, ks, ke, width: int, out=None, strea
         out = torch.empty((nq, int(width)), dtype=torch.float32, device=dev)
     elif out.shape != (nq, int(width)) or out.dtype != torch.float32 or not out.is_contiguous() or out.device != dev:
         raise ValueError("out must be a contiguous float32 tensor of shape (num_q, width)")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
+    handle = _stream_handle(stream, dev)
     with torch.cuda.device(dev):
         st = load().indexer_logits(q.data_ptr(), weights.data_ptr(), kv.data_ptr(), kv_scale.data_ptr(),
-                                   ks.data_ptr(), ke.data_ptr(), out.data_ptr(), ctypes.c_void_p(stream.cuda_stream),
-                                   int(nq), int(nkv), int(width))
+                                   ks.data_ptr(), ke.data_ptr(), out.data_ptr(), handle, int(nq), int(nkv), int(width))
     _check(st)
     return out
 
@@ -293,12 +308,10 @@ def indexer_topk(q, weights, kv, kv_scale, ks, ke, k: int, out=None, stream=None
         out = torch.empty((nq, int(k)), dtype=torch.int32, device=dev)
     elif out.shape != (nq, int(k)) or out.dtype != torch.int32 or not out.is_contiguous() or out.device != dev:
         raise ValueError("out must be a contiguous int32 tensor of shape (num_q, k)")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
+    handle = _stream_handle(stream, dev)
     with torch.cuda.device(dev):
         st = load().indexer_topk(q.data_ptr(), weights.data_ptr(), kv.data_ptr(), kv_scale.data_ptr(),
-                                 ks.data_ptr(), ke.data_ptr(), int(k), out.data_ptr(),
-                                 ctypes.c_void_p(stream.cuda_stream), int(nq), int(nkv))
+                                 ks.data_ptr(), ke.data_ptr(), int(k), out.data_ptr(), handle, int(nq), int(nkv))
     _check(st)
     return out
 
