@@ -109,7 +109,10 @@ typedef enum topk_status_t {
  *
  * Split rows rely on every workgroup of a row being resident at once: the
  * grid is sized to the device's resident capacity and launched normally (no
- * cooperative launch).  If that fails, a bounded wait gives up and the call's
+ * cooperative launch).  When a batch's rows cannot all be resident at once
+ * they are cycled over the resident slots, and two shapes are queued (more
+ * workgroups per row, or more rows at once); the device runs the one the
+ * row lengths favour and the other exits.  The override below forces one.  If that fails, a bounded wait gives up and the call's
  * outputs are invalid; this is reported as TOPK_ERROR_DEVICE_FAULT, never
  * silently.
  *

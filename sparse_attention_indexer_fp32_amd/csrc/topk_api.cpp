@@ -258,6 +258,12 @@ struct Plan {
   int ept_idx = 0;
   int64_t G = 1;
   int64_t slots = 1;
+  // Cycled split rows: a second shape (smaller E, more workgroups per row)
+  // launched before this one; the device picks one of the two from the row
+  // lengths (alt_ept_idx < 0: none)
+  int alt_ept_idx = -1;
+  int64_t alt_G = 0;
+  int64_t alt_slots = 0;
 };
 
 const char* kind_name(Kind k) {
@@ -419,6 +425,23 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
         const double t_stream = 4.0 * (double)Wc / 27000.0 + 10.0;
         if (t_split < t_stream) chosen = i;
       }
+      // The estimate above assumes every row is long.  When few are (a
+      // decode batch of a few long requests among short ones), E = 16 with
+      // four times the workgroups per row finishes them in one round, and the
+      // short rows run on one workgroup each meanwhile (measured on MI355X:
+      // 4 x 1M + 28 x 16K, k 2048: 30.1-30.5 us at E 16 against 45.9-46.5 us
+      // at E 64; 32 x 1M: 147 against 72.8 us).  Only the device knows the
+      // lengths, so both shapes are launched and each counts the rows that
+      // need more than one E = 16 workgroup: the E = 16 launch runs if they
+      // fit its slots at once, else the E = 64 one.
+      const int a16 = 2;   // kEptValues[2] = 16
+      const int64_t G16 = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[a16]);
+      const int64_t slots16 = (int64_t)dev.occ[1][a16] * dev.cus / G16;
+      if (chosen == i && slots16 >= 1 && slots16 < B && G16 <= (int64_t)topk::kBarGroup * topk::kBarMaxGroups) {
+        plan->alt_ept_idx = a16;
+        plan->alt_G = G16;
+        plan->alt_slots = slots16;
+      }
     }
     if (chosen < 0) {
       // too many rows to hold resident: stream them, G workgroups per row
@@ -501,7 +524,7 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   st = plan_launch(*info, batch, width, k, &plan);
   if (st != TOPK_SUCCESS) return st;
 
-  topk::KernelArgs a;
+  topk::KernelArgs a{};
   a.scores = scores;
   a.seq_lens = seq_lens;
   a.page_table = page_table;
@@ -542,7 +565,7 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     // split rows synchronise through per-slot regions, split streaming rows
     // through per-row areas; streamed rows beyond the grid are handed out
     // through a counter in the header
-    const size_t words = plan.kind == Kind::kSplit         ? topk::workspace_words(plan.slots)
+    const size_t words = plan.kind == Kind::kSplit         ? topk::workspace_words(std::max(plan.slots, plan.alt_slots))
                          : plan.kind == Kind::kSplitStream ? topk::split_stream_words(batch)
                                                            : topk::kHdrWords;
     if (noalloc) {
@@ -577,7 +600,21 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     e = topk::launch_stream_rows(plan.stream_variant, a, stream);
   else if (plan.kind == Kind::kSplitStream)
     e = topk::launch_split_stream(plan.ss_variant, a, stream);
-  else
+  else if (plan.alt_ept_idx >= 0) {
+    // the pair of cycled shapes (Plan): the E = 16 launch first, then this
+    // plan's; the device runs one of them
+    topk::KernelArgs b = a;
+    b.wgs_per_row = (int32_t)plan.alt_G;
+    b.slots = (int32_t)plan.alt_slots;
+    b.choice = 1;
+    b.choice_rows = (int32_t)plan.alt_slots;
+    b.choice_len = topk::kThreads * topk::kEptValues[plan.alt_ept_idx];
+    e = topk::launch_rows(plan.alt_ept_idx, true, b, stream);
+    a.choice = 2;
+    a.choice_rows = b.choice_rows;
+    a.choice_len = b.choice_len;
+    if (e == hipSuccess) e = topk::launch_rows(plan.ept_idx, true, a, stream);
+  } else
     e = topk::launch_rows(plan.ept_idx, plan.kind == Kind::kSplit, a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   int64_t sorted_slots = 0, sorted_g = 0;
@@ -612,13 +649,19 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   if (sorted)
     std::snprintf(sorted_note, sizeof(sorted_note), sorted_g > 0 ? " + sorted-finish rank G=%lld" : " + sorted-finish rows",
                   (long long)sorted_g);
-  char buf[240];
-  std::snprintf(buf, sizeof(buf), "%s%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s",
+  char pair_note[160] = "";
+  if (plan.alt_ept_idx >= 0)
+    std::snprintf(pair_note, sizeof(pair_note),
+                  " | ept=%d wgs_per_row=%lld slots=%lld when at most %lld rows exceed %d positions (device choice)",
+                  topk::kEptValues[plan.alt_ept_idx], (long long)plan.alt_G, (long long)plan.alt_slots,
+                  (long long)plan.alt_slots, topk::kThreads * topk::kEptValues[plan.alt_ept_idx]);
+  char buf[400];
+  std::snprintf(buf, sizeof(buf), "%s%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s%s",
                 kind_name(plan.kind), plan.ss_spread ? " length-aware" : "",
                 plan.kind == Kind::kStream || plan.kind == Kind::kSplitStream ? 0 : topk::kEptValues[plan.ept_idx],
                 (long long)plan.G, (long long)plan.slots, (long long)(plan.slots * plan.G),
                 plan.kind == Kind::kStream ? topk::stream_variant_threads(plan.stream_variant) : topk::kThreads, a.vec,
-                sorted_note, noalloc ? " (static scratch)" : "");
+                pair_note, sorted_note, noalloc ? " (static scratch)" : "");
   t_last_launch = buf;
   return TOPK_SUCCESS;
 }

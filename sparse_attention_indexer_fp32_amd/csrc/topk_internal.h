@@ -133,6 +133,13 @@ struct KernelArgs {
   uint32_t* fault_host;       // split rows: host-visible copy of the workspace's fault count, or nullptr
   int32_t spread;             // split streaming: 0 = wgs_per_row parts per row; else per-row parts from
                               // the lengths, at most wgs_per_row, the positions spread over this many shares
+  // Cycled split rows launched as a pair of shapes, one of which runs (the
+  // other's workgroups exit at once): 0 = run unconditionally; 1 = run if at
+  // most choice_rows rows are longer than choice_len positions; 2 = run if
+  // more are.  Both launches count the same lengths, so exactly one runs.
+  int32_t choice;
+  int32_t choice_rows;
+  int32_t choice_len;
 };
 
 // Polls of a split-row barrier wait before it gives up (with s_sleep 1 between

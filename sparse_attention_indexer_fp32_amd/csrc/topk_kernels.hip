@@ -628,6 +628,23 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
   __shared__ int32_t sh_cpos[COOP ? kCandCap : 1];
   __shared__ int32_t sh_cout[COOP && kOverlap ? kCandCap : 1];   // the candidates' output values
 
+  if (SHORT && a.choice != 0) {
+    // one launch of a pair of cycled shapes: every workgroup counts the rows
+    // longer than choice_len (the same count in both launches), and this
+    // launch runs only on its side of choice_rows; otherwise it exits before
+    // touching the workspace and the pair's other launch takes the batch
+    __shared__ uint32_t sh_long;
+    const int t0 = opaque_tid();
+    if (t0 == 0) sh_long = 0u;
+    __syncthreads();
+    uint32_t c = 0;
+    for (int r = t0; r < a.batch; r += kThreads)
+      c += (a.width > (int64_t)a.choice_len && a.seq_lens[r] > a.choice_len) ? 1u : 0u;   // min(len, W) > choice_len
+    if (c != 0u) atomicAdd(&sh_long, c);
+    __syncthreads();
+    const bool few = uniform(sh_long) <= (uint32_t)a.choice_rows;
+    if ((a.choice == 1) != few) return;
+  }
   const int G = COOP ? a.wgs_per_row : 1;
   const int slot = (int)blockIdx.x / G;
   const int g = (int)blockIdx.x - slot * G;

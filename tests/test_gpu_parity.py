@@ -253,6 +253,58 @@ def test_split_rows_cycled_repeated_and_graph(lib):
     lib.topk_check_faults()   # raises if a split-row wait gave up
 
 
+def test_split_rows_cycled_device_choice(lib):
+    """A batch of more long rows than fit resident is cycled over split slots
+    in one of two shapes, and the device picks it from the lengths: E = 16
+    (four times the workgroups per row, a round of its slots) when at most
+    that many rows exceed one E = 16 workgroup, else E = 64.  Both sides,
+    eagerly and inside one captured graph whose replays see the lengths
+    change (so the choice flips between replays)."""
+    import dataclasses
+    import re
+    import torch
+    W, B = 1 << 20, 32
+    probe = workloads.custom(950, B, W, 2048, 64, seq_lens=[W] * 4 + [16384] * (B - 4), kind="normal", table="perm")
+    tens = upload(probe)
+    run(lib, probe, raw=False, tensors=tens)
+    launch = lib.topk_last_launch()
+    note(f"device choice: {launch}")
+    m = re.search(r"\| ept=16 wgs_per_row=(\d+) slots=(\d+) when at most (\d+) rows exceed 16384", launch)
+    assert launch.startswith("split-row ept=64") and m, launch
+    fit = int(m.group(2))
+    seq_few = [W - 5 * i for i in range(fit)] + [16384, 3000, 0, 2048] * 8
+    seq_few = seq_few[:B]
+    seq_many = [W - 5 * i for i in range(fit + 1)] + [16384, 3000, 0, 2048] * 8
+    seq_many = seq_many[:B]
+    variants = {"few": np.array(seq_few, np.int32), "many": np.array(seq_many, np.int32)}
+    # scores and table valid up to either pattern's length (both are poisoned past the lengths given)
+    seq_max = np.maximum(variants["few"], variants["many"]).tolist()
+    w = workloads.custom(951, B, W, 2048, 64, seq_lens=seq_max, kind="normal", table="perm")
+    s, sl, pt = upload(w)
+    for name, seq in variants.items():
+        note(f"device choice eager: {name} long rows")
+        sl.copy_(torch.from_numpy(seq))
+        out, raw = run(lib, w, raw=True, tensors=(s, sl, pt))
+        check(dataclasses.replace(w, seq_lens=seq), out, raw)
+    out = torch.empty((B, w.k), dtype=torch.int32, device=s.device)
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)   # the side stream's workspace
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            lib.topk_transform(s, sl, pt, w.k, w.page_size, out=out)
+    for rep, name in enumerate(["few", "many", "few", "many"]):
+        note(f"device choice graph replay {rep}: {name} long rows")
+        sl.copy_(torch.from_numpy(variants[name]))
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(dataclasses.replace(w, seq_lens=variants[name]), out.cpu().numpy(), None)
+    lib.topk_check_faults()   # raises if a split-row wait gave up
+
+
 def test_graph_replay(lib):
     """Calls captured in a HIP graph and replayed give the eager result every time."""
     import torch
