@@ -433,7 +433,10 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
       // at E 64; 32 x 1M: 147 against 72.8 us).  Only the device knows the
       // lengths, so both shapes are launched and each counts the rows that
       // need more than one E = 16 workgroup: the E = 16 launch runs if they
-      // fit its slots at once, else the E = 64 one.
+      // fit two rounds of its slots, else the E = 64 one (32 x 1M batches
+      // with n such rows, the rest at most 16K, E 16 against E 64: n = 4
+      // 29.6 against 47.3 us; 6: 44.1 against 48.8; 8: 44.9 against 49.7;
+      // 12: 61.0 against 54.4).
       const int a16 = 2;   // kEptValues[2] = 16
       const int64_t G16 = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[a16]);
       const int64_t slots16 = (int64_t)dev.occ[1][a16] * dev.cus / G16;
@@ -607,7 +610,7 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     b.wgs_per_row = (int32_t)plan.alt_G;
     b.slots = (int32_t)plan.alt_slots;
     b.choice = 1;
-    b.choice_rows = (int32_t)plan.alt_slots;
+    b.choice_rows = (int32_t)(2 * plan.alt_slots);
     b.choice_len = topk::kThreads * topk::kEptValues[plan.alt_ept_idx];
     e = topk::launch_rows(plan.alt_ept_idx, true, b, stream);
     a.choice = 2;
@@ -654,7 +657,7 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
     std::snprintf(pair_note, sizeof(pair_note),
                   " | ept=%d wgs_per_row=%lld slots=%lld when at most %lld rows exceed %d positions (device choice)",
                   topk::kEptValues[plan.alt_ept_idx], (long long)plan.alt_G, (long long)plan.alt_slots,
-                  (long long)plan.alt_slots, topk::kThreads * topk::kEptValues[plan.alt_ept_idx]);
+                  (long long)(2 * plan.alt_slots), topk::kThreads * topk::kEptValues[plan.alt_ept_idx]);
   char buf[400];
   std::snprintf(buf, sizeof(buf), "%s%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s%s",
                 kind_name(plan.kind), plan.ss_spread ? " length-aware" : "",

@@ -256,8 +256,8 @@ def test_split_rows_cycled_repeated_and_graph(lib):
 def test_split_rows_cycled_device_choice(lib):
     """A batch of more long rows than fit resident is cycled over split slots
     in one of two shapes, and the device picks it from the lengths: E = 16
-    (four times the workgroups per row, a round of its slots) when at most
-    that many rows exceed one E = 16 workgroup, else E = 64.  Both sides,
+    (four times the workgroups per row) when at most two rounds of its slots'
+    worth of rows exceed one E = 16 workgroup, else E = 64.  Both sides,
     eagerly and inside one captured graph whose replays see the lengths
     change (so the choice flips between replays)."""
     import dataclasses
@@ -271,7 +271,7 @@ def test_split_rows_cycled_device_choice(lib):
     note(f"device choice: {launch}")
     m = re.search(r"\| ept=16 wgs_per_row=(\d+) slots=(\d+) when at most (\d+) rows exceed 16384", launch)
     assert launch.startswith("split-row ept=64") and m, launch
-    fit = int(m.group(2))
+    fit = int(m.group(3))   # the most long rows the E = 16 shape takes
     seq_few = [W - 5 * i for i in range(fit)] + [16384, 3000, 0, 2048] * 8
     seq_few = seq_few[:B]
     seq_many = [W - 5 * i for i in range(fit + 1)] + [16384, 3000, 0, 2048] * 8
