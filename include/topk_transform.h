@@ -112,9 +112,11 @@ typedef enum topk_status_t {
  * cooperative launch).  When a batch's rows cannot all be resident at once
  * they are cycled over the resident slots, and two shapes are queued (more
  * workgroups per row, or more rows at once); the device runs the one the
- * row lengths favour and the other exits.  The override below forces one.  If that fails, a bounded wait gives up and the call's
- * outputs are invalid; this is reported as TOPK_ERROR_DEVICE_FAULT, never
- * silently.
+ * row lengths favour (the first while the rows longer than one of its
+ * workgroups fit two rounds of its slots) and the other exits.  The
+ * dispatch override forces one.  If the workgroups of a row are not all
+ * resident after all, a bounded wait gives up and the call's outputs are
+ * invalid; this is reported as TOPK_ERROR_DEVICE_FAULT, never silently.
  *
  * Completion is asynchronous: outputs are valid once `stream` reaches the call.
  * Returns TOPK_SUCCESS, or an error status; on error nothing was queued.
