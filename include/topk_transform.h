@@ -110,10 +110,10 @@ typedef enum topk_status_t {
  * Split rows rely on every workgroup of a row being resident at once: the
  * grid is sized to the device's resident capacity and launched normally (no
  * cooperative launch).  When a batch's rows cannot all be resident at once
- * they are cycled over the resident slots, and two shapes are queued (more
- * workgroups per row, or more rows at once); the device runs the one the
- * row lengths favour (the first while the rows longer than one of its
- * workgroups fit two rounds of its slots) and the other exits.  The
+ * they are cycled over the resident slots in one of two shapes (more
+ * workgroups per row, or more rows at once), both held by one launch; the
+ * device takes the one the row lengths favour (the first while the rows
+ * longer than one of its workgroups fit two rounds of its slots).  The
  * dispatch override forces one.  If the workgroups of a row are not all
  * resident after all, a bounded wait gives up and the call's outputs are
  * invalid; this is reported as TOPK_ERROR_DEVICE_FAULT, never silently.

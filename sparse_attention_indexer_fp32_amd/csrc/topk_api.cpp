@@ -48,6 +48,7 @@ struct DeviceInfo {
   int sorted_occ_small = 0;         // sorted finish: resident workgroups per CU, k <= kSortSmallK
   int sorted_occ = 0;               //                                            larger k
   int ss_occ[topk::kNumSplitStreamVariants] = {};   // split streaming shapes: resident workgroups per CU
+  int pair_occ = 0;                 // the cycled pair's kernel (E = 16 or 64): resident workgroups per CU
   uint32_t* fault_page = nullptr;   // pinned, device-mapped host memory (kFaultWords words), or null
   uint32_t* fault_page_dev = nullptr;   // its device address
   int fault_next = 1;               // next unassigned word of the page
@@ -122,6 +123,8 @@ topk_status_t device_info(int dev, DeviceInfo** out) {
       e = topk::split_stream_occupancy(v, &info.ss_occ[v]);
       if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     }
+    e = topk::rows_pair_occupancy(&info.pair_occ);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     // set-up of the static scratch: its address on this (the current) device
     e = topk::scratch_address(&info.scratch);
     if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
@@ -431,16 +434,18 @@ topk_status_t plan_launch(const DeviceInfo& dev, int32_t batch, int64_t width, i
       // short rows run on one workgroup each meanwhile (measured on MI355X:
       // 4 x 1M + 28 x 16K, k 2048: 30.1-30.5 us at E 16 against 45.9-46.5 us
       // at E 64; 32 x 1M: 147 against 72.8 us).  Only the device knows the
-      // lengths, so both shapes are launched and each counts the rows that
-      // need more than one E = 16 workgroup: the E = 16 launch runs if they
-      // fit two rounds of its slots, else the E = 64 one (32 x 1M batches
-      // with n such rows, the rest at most 16K, E 16 against E 64: n = 4
-      // 29.6 against 47.3 us; 6: 44.1 against 48.8; 8: 44.9 against 49.7;
-      // 12: 61.0 against 54.4).
+      // lengths, so one launch holds both shapes, and its workgroups count
+      // the rows that need more than one E = 16 workgroup: E = 16 runs if
+      // they fit two rounds of its slots, else E = 64 (32 x 1M batches with
+      // n such rows, the rest at most 16K, E 16 against E 64: n = 4 29.6
+      // against 47.3 us; 6: 44.1 against 48.8; 8: 44.9 against 49.7; 12:
+      // 61.0 against 54.4).  Both shapes' grids must fit the pair kernel's
+      // residency.
       const int a16 = 2;   // kEptValues[2] = 16
       const int64_t G16 = ceil_div(Wc, (int64_t)topk::kThreads * topk::kEptValues[a16]);
-      const int64_t slots16 = (int64_t)dev.occ[1][a16] * dev.cus / G16;
-      if (chosen == i && slots16 >= 1 && slots16 < B && G16 <= (int64_t)topk::kBarGroup * topk::kBarMaxGroups) {
+      const int64_t slots16 = (int64_t)dev.pair_occ * dev.cus / G16;
+      if (chosen == i && dev.pair_occ >= dev.occ[1][i] && slots16 >= 1 && slots16 < B &&
+          G16 <= (int64_t)topk::kBarGroup * topk::kBarMaxGroups) {
         plan->alt_ept_idx = a16;
         plan->alt_G = G16;
         plan->alt_slots = slots16;
@@ -604,19 +609,15 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   else if (plan.kind == Kind::kSplitStream)
     e = topk::launch_split_stream(plan.ss_variant, a, stream);
   else if (plan.alt_ept_idx >= 0) {
-    // the pair of cycled shapes (Plan): the E = 16 launch first, then this
-    // plan's; the device runs one of them
+    // the pair of cycled shapes (Plan): E = 16 with the alternative's
+    // workgroups per row and slots, E = 64 with this plan's; one launch, the
+    // device takes one of them
     topk::KernelArgs b = a;
     b.wgs_per_row = (int32_t)plan.alt_G;
     b.slots = (int32_t)plan.alt_slots;
-    b.choice = 1;
     b.choice_rows = (int32_t)(2 * plan.alt_slots);
     b.choice_len = topk::kThreads * topk::kEptValues[plan.alt_ept_idx];
-    e = topk::launch_rows(plan.alt_ept_idx, true, b, stream);
-    a.choice = 2;
-    a.choice_rows = b.choice_rows;
-    a.choice_len = b.choice_len;
-    if (e == hipSuccess) e = topk::launch_rows(plan.ept_idx, true, a, stream);
+    e = topk::launch_rows_pair(b, a, stream);
   } else
     e = topk::launch_rows(plan.ept_idx, plan.kind == Kind::kSplit, a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
@@ -655,9 +656,11 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   char pair_note[160] = "";
   if (plan.alt_ept_idx >= 0)
     std::snprintf(pair_note, sizeof(pair_note),
-                  " | ept=%d wgs_per_row=%lld slots=%lld when at most %lld rows exceed %d positions (device choice)",
+                  " | ept=%d wgs_per_row=%lld slots=%lld when at most %lld rows exceed %d positions (device "
+                  "choice in one launch, grid=%lld)",
                   topk::kEptValues[plan.alt_ept_idx], (long long)plan.alt_G, (long long)plan.alt_slots,
-                  (long long)(2 * plan.alt_slots), topk::kThreads * topk::kEptValues[plan.alt_ept_idx]);
+                  (long long)(2 * plan.alt_slots), topk::kThreads * topk::kEptValues[plan.alt_ept_idx],
+                  (long long)std::max(plan.alt_slots * plan.alt_G, plan.slots * plan.G));
   char buf[400];
   std::snprintf(buf, sizeof(buf), "%s%s ept=%d wgs_per_row=%lld slots=%lld grid=%lld block=%d vec=%d%s%s%s",
                 kind_name(plan.kind), plan.ss_spread ? " length-aware" : "",

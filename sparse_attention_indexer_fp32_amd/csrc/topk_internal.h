@@ -133,11 +133,9 @@ struct KernelArgs {
   uint32_t* fault_host;       // split rows: host-visible copy of the workspace's fault count, or nullptr
   int32_t spread;             // split streaming: 0 = wgs_per_row parts per row; else per-row parts from
                               // the lengths, at most wgs_per_row, the positions spread over this many shares
-  // Cycled split rows launched as a pair of shapes, one of which runs (the
-  // other's workgroups exit at once): 0 = run unconditionally; 1 = run if at
-  // most choice_rows rows are longer than choice_len positions; 2 = run if
-  // more are.  Both launches count the same lengths, so exactly one runs.
-  int32_t choice;
+  // The cycled pair's kernel (read from its E = 16 arguments): it takes the
+  // E = 16 shape if at most choice_rows rows are longer than choice_len
+  // positions, else the E = 64 shape.
   int32_t choice_rows;
   int32_t choice_len;
 };
@@ -150,6 +148,11 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 21;
 // kernel (cooperative launch, grid = slots * wgs_per_row).
 hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStream_t stream);
 hipError_t rows_occupancy(int ept_index, bool coop, int* blocks_per_cu);
+// Cycled split rows in one launch that takes E = 16 (a16) or E = 64 (a64)
+// from the row lengths (a16.choice_rows, a16.choice_len); grid = the larger
+// of the two shapes' slots * wgs_per_row, all resident at once.
+hipError_t launch_rows_pair(const KernelArgs& a16, const KernelArgs& a64, hipStream_t stream);
+hipError_t rows_pair_occupancy(int* blocks_per_cu);
 
 // Streaming kernel, one workgroup per row, persistent over rows (grid =
 // slots).  `variant` selects one of kNumStreamVariants compiled shapes

@@ -618,7 +618,7 @@ __device__ __forceinline__ void load_keys(uint32_t (&key)[4 * V], const float* r
 // workgroup run in one workgroup of the slot (below).  A separate
 // instantiation, so the one-pass split kernel keeps its split-only code.
 template <int E, bool COOP, bool SHORT>
-__global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
+__device__ __forceinline__ void rows_body(KernelArgs a) {
   constexpr bool kOverlap = !SHORT;   // see the compaction below
   __shared__ uint32_t sh_hist[kBinsWide];
   __shared__ int32_t sh_raw[kMaxK + 64];   // + one trash word per lane
@@ -628,23 +628,6 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
   __shared__ int32_t sh_cpos[COOP ? kCandCap : 1];
   __shared__ int32_t sh_cout[COOP && kOverlap ? kCandCap : 1];   // the candidates' output values
 
-  if (SHORT && a.choice != 0) {
-    // one launch of a pair of cycled shapes: every workgroup counts the rows
-    // longer than choice_len (the same count in both launches), and this
-    // launch runs only on its side of choice_rows; otherwise it exits before
-    // touching the workspace and the pair's other launch takes the batch
-    __shared__ uint32_t sh_long;
-    const int t0 = opaque_tid();
-    if (t0 == 0) sh_long = 0u;
-    __syncthreads();
-    uint32_t c = 0;
-    for (int r = t0; r < a.batch; r += kThreads)
-      c += (a.width > (int64_t)a.choice_len && a.seq_lens[r] > a.choice_len) ? 1u : 0u;   // min(len, W) > choice_len
-    if (c != 0u) atomicAdd(&sh_long, c);
-    __syncthreads();
-    const bool few = uniform(sh_long) <= (uint32_t)a.choice_rows;
-    if ((a.choice == 1) != few) return;
-  }
   const int G = COOP ? a.wgs_per_row : 1;
   const int slot = (int)blockIdx.x / G;
   const int g = (int)blockIdx.x - slot * G;
@@ -1038,6 +1021,39 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
     __syncthreads();
   }
   if (COOP) launch_exit(a, gave_up, &sh_var[15], opaque_tid());
+}
+
+template <int E, bool COOP, bool SHORT>
+__global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
+  rows_body<E, COOP, SHORT>(a);
+}
+
+// Cycled split rows in one of two shapes, E = 16 (a16) or E = 64 (a64), both
+// in one launch whose grid holds the larger of their grids.  Every workgroup
+// counts the rows longer than a16.choice_len (the same count everywhere), and
+// the launch takes the E = 16 shape if there are at most a16.choice_rows of
+// them.  Workgroups past the taken shape's grid only check in at the launch's
+// exit count.
+__global__ void __launch_bounds__(kThreads) rows_pair_kernel(KernelArgs a16, KernelArgs a64) {
+  __shared__ uint32_t sh_long;
+  const int t0 = opaque_tid();
+  if (t0 == 0) sh_long = 0u;
+  __syncthreads();
+  uint32_t c = 0;
+  for (int r = t0; r < a16.batch; r += kThreads)   // min(len, W) > choice_len
+    c += (a16.width > (int64_t)a16.choice_len && a16.seq_lens[r] > a16.choice_len) ? 1u : 0u;
+  if (c != 0u) atomicAdd(&sh_long, c);
+  __syncthreads();
+  const bool few = uniform(sh_long) <= (uint32_t)a16.choice_rows;
+  const KernelArgs& t = few ? a16 : a64;
+  if ((int64_t)blockIdx.x >= (int64_t)t.slots * t.wgs_per_row) {
+    launch_exit(t, 0u, &sh_long, opaque_tid());
+    return;
+  }
+  if (few)
+    rows_body<16, true, true>(a16);
+  else
+    rows_body<64, true, true>(a64);
 }
 
 // ---------------------------------------------------------------------------
@@ -2660,6 +2676,17 @@ hipError_t scratch_address(uint32_t** ptr) {
 hipError_t clear_words(uint32_t* p, size_t words, hipStream_t stream) {
   hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, stream, p, words);
   return hipGetLastError();
+}
+
+hipError_t launch_rows_pair(const KernelArgs& a16, const KernelArgs& a64, hipStream_t stream) {
+  const int64_t g16 = (int64_t)a16.slots * a16.wgs_per_row, g64 = (int64_t)a64.slots * a64.wgs_per_row;
+  hipLaunchKernelGGL(rows_pair_kernel, dim3((unsigned)(g16 > g64 ? g16 : g64)), dim3(kThreads), 0, stream, a16, a64);
+  return hipGetLastError();
+}
+
+hipError_t rows_pair_occupancy(int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(&rows_pair_kernel),
+                                                      kThreads, 0);
 }
 
 hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStream_t stream) {
