@@ -609,15 +609,12 @@ topk_status_t run_transform_locked(const float* scores, const int32_t* seq_lens,
   else if (plan.kind == Kind::kSplitStream)
     e = topk::launch_split_stream(plan.ss_variant, a, stream);
   else if (plan.alt_ept_idx >= 0) {
-    // the pair of cycled shapes (Plan): E = 16 with the alternative's
-    // workgroups per row and slots, E = 64 with this plan's; one launch, the
+    // the pair of cycled shapes (Plan): E = 64 with this plan's workgroups
+    // per row and slots, E = 16 with the alternative's; one launch, the
     // device takes one of them
-    topk::KernelArgs b = a;
-    b.wgs_per_row = (int32_t)plan.alt_G;
-    b.slots = (int32_t)plan.alt_slots;
-    b.choice_rows = (int32_t)(2 * plan.alt_slots);
-    b.choice_len = topk::kThreads * topk::kEptValues[plan.alt_ept_idx];
-    e = topk::launch_rows_pair(b, a, stream);
+    a.choice_rows = (int32_t)(2 * plan.alt_slots);
+    a.choice_len = topk::kThreads * topk::kEptValues[plan.alt_ept_idx];
+    e = topk::launch_rows_pair(a, (int32_t)plan.alt_G, (int32_t)plan.alt_slots, stream);
   } else
     e = topk::launch_rows(plan.ept_idx, plan.kind == Kind::kSplit, a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

@@ -133,9 +133,9 @@ struct KernelArgs {
   uint32_t* fault_host;       // split rows: host-visible copy of the workspace's fault count, or nullptr
   int32_t spread;             // split streaming: 0 = wgs_per_row parts per row; else per-row parts from
                               // the lengths, at most wgs_per_row, the positions spread over this many shares
-  // The cycled pair's kernel (read from its E = 16 arguments): it takes the
-  // E = 16 shape if at most choice_rows rows are longer than choice_len
-  // positions, else the E = 64 shape.
+  // The cycled pair's kernel: it takes the E = 16 shape if at most
+  // choice_rows rows are longer than choice_len positions, else the E = 64
+  // shape.
   int32_t choice_rows;
   int32_t choice_len;
 };
@@ -148,10 +148,11 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 21;
 // kernel (cooperative launch, grid = slots * wgs_per_row).
 hipError_t launch_rows(int ept_index, bool coop, const KernelArgs& args, hipStream_t stream);
 hipError_t rows_occupancy(int ept_index, bool coop, int* blocks_per_cu);
-// Cycled split rows in one launch that takes E = 16 (a16) or E = 64 (a64)
-// from the row lengths (a16.choice_rows, a16.choice_len); grid = the larger
-// of the two shapes' slots * wgs_per_row, all resident at once.
-hipError_t launch_rows_pair(const KernelArgs& a16, const KernelArgs& a64, hipStream_t stream);
+// Cycled split rows in one launch that takes E = 64 (a.wgs_per_row, a.slots)
+// or E = 16 (g16, slots16) from the row lengths (a.choice_rows,
+// a.choice_len); grid = the larger of the two shapes' slots * wgs_per_row, all
+// resident at once.
+hipError_t launch_rows_pair(const KernelArgs& a, int32_t g16, int32_t slots16, hipStream_t stream);
 hipError_t rows_pair_occupancy(int* blocks_per_cu);
 
 // Streaming kernel, one workgroup per row, persistent over rows (grid =

@@ -1028,32 +1028,36 @@ __global__ void __launch_bounds__(kThreads) rows_kernel(KernelArgs a) {
   rows_body<E, COOP, SHORT>(a);
 }
 
-// Cycled split rows in one of two shapes, E = 16 (a16) or E = 64 (a64), both
-// in one launch whose grid holds the larger of their grids.  Every workgroup
-// counts the rows longer than a16.choice_len (the same count everywhere), and
-// the launch takes the E = 16 shape if there are at most a16.choice_rows of
-// them.  Workgroups past the taken shape's grid only check in at the launch's
-// exit count.
-__global__ void __launch_bounds__(kThreads) rows_pair_kernel(KernelArgs a16, KernelArgs a64) {
+// Cycled split rows in one of two shapes, E = 64 (a's wgs_per_row and slots)
+// or E = 16 (g16 and slots16), both in one launch whose grid holds the larger
+// of their grids.  Every workgroup counts the rows longer than a.choice_len
+// (the same count everywhere), and the launch takes the E = 16 shape if there
+// are at most a.choice_rows of them.  Workgroups past the taken shape's grid
+// only check in at the launch's exit count.
+__global__ void __launch_bounds__(kThreads) rows_pair_kernel(KernelArgs a, int32_t g16, int32_t slots16) {
   __shared__ uint32_t sh_long;
   const int t0 = opaque_tid();
   if (t0 == 0) sh_long = 0u;
   __syncthreads();
   uint32_t c = 0;
-  for (int r = t0; r < a16.batch; r += kThreads)   // min(len, W) > choice_len
-    c += (a16.width > (int64_t)a16.choice_len && a16.seq_lens[r] > a16.choice_len) ? 1u : 0u;
+  for (int r = t0; r < a.batch; r += kThreads)   // min(len, W) > choice_len
+    c += (a.width > (int64_t)a.choice_len && a.seq_lens[r] > a.choice_len) ? 1u : 0u;
   if (c != 0u) atomicAdd(&sh_long, c);
   __syncthreads();
-  const bool few = uniform(sh_long) <= (uint32_t)a16.choice_rows;
-  const KernelArgs& t = few ? a16 : a64;
-  if ((int64_t)blockIdx.x >= (int64_t)t.slots * t.wgs_per_row) {
-    launch_exit(t, 0u, &sh_long, opaque_tid());
+  const bool few = uniform(sh_long) <= (uint32_t)a.choice_rows;
+  const int64_t grid = few ? (int64_t)slots16 * g16 : (int64_t)a.slots * a.wgs_per_row;
+  if ((int64_t)blockIdx.x >= grid) {
+    launch_exit(a, 0u, &sh_long, opaque_tid());
     return;
   }
-  if (few)
-    rows_body<16, true, true>(a16);
-  else
-    rows_body<64, true, true>(a64);
+  if (few) {
+    KernelArgs b = a;
+    b.wgs_per_row = g16;
+    b.slots = slots16;
+    rows_body<16, true, true>(b);
+  } else {
+    rows_body<64, true, true>(a);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2678,9 +2682,10 @@ hipError_t clear_words(uint32_t* p, size_t words, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_rows_pair(const KernelArgs& a16, const KernelArgs& a64, hipStream_t stream) {
-  const int64_t g16 = (int64_t)a16.slots * a16.wgs_per_row, g64 = (int64_t)a64.slots * a64.wgs_per_row;
-  hipLaunchKernelGGL(rows_pair_kernel, dim3((unsigned)(g16 > g64 ? g16 : g64)), dim3(kThreads), 0, stream, a16, a64);
+hipError_t launch_rows_pair(const KernelArgs& a, int32_t g16, int32_t slots16, hipStream_t stream) {
+  const int64_t n16 = (int64_t)slots16 * g16, n64 = (int64_t)a.slots * a.wgs_per_row;
+  hipLaunchKernelGGL(rows_pair_kernel, dim3((unsigned)(n16 > n64 ? n16 : n64)), dim3(kThreads), 0, stream, a, g16,
+                     slots16);
   return hipGetLastError();
 }
 
