@@ -253,17 +253,20 @@ def test_split_rows_cycled_repeated_and_graph(lib):
     lib.topk_check_faults()   # raises if a split-row wait gave up
 
 
-def test_split_rows_cycled_device_choice(lib):
+@pytest.mark.parametrize("W", [1 << 20, 3 << 19])
+def test_split_rows_cycled_device_choice(lib, W):
     """A batch of more long rows than fit resident is cycled over split slots
     in one of two shapes, and the device picks it from the lengths: E = 16
     (four times the workgroups per row) when at most two rounds of its slots'
     worth of rows exceed one E = 16 workgroup, else E = 64.  Both sides,
     eagerly and inside one captured graph whose replays see the lengths
-    change (so the choice flips between replays)."""
+    change (so the choice flips between replays).  At width 1.5M the two
+    shapes' grids differ (96 x 2 against 24 x 10 workgroups on 256 CUs), so
+    the launch's spare workgroups take the exit path."""
     import dataclasses
     import re
     import torch
-    W, B = 1 << 20, 32
+    B = 32
     probe = workloads.custom(950, B, W, 2048, 64, seq_lens=[W] * 4 + [16384] * (B - 4), kind="normal", table="perm")
     tens = upload(probe)
     run(lib, probe, raw=False, tensors=tens)
